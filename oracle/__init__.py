@@ -1,0 +1,136 @@
+"""fp64 CPU oracle for linear attention with phi(x) = elu(x) + 1.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the smoke check
+and the benchmark's CPU-baseline leg may import this package.  It shares no
+code with the HIP library: the arithmetic lives in ``linattn_oracle.c`` (plain
+C, double precision, OpenMP over heads), which this module builds with gcc and
+calls through ctypes.
+
+Every function takes NumPy/torch CPU arrays laid out [BH, N, d] (or [BH, d]
+for the decode step), converts them to contiguous float32 (exact for bf16 and
+fp32 inputs) and returns float64 results.  Citations of the defining passages
+are in the C source, next to each function.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "linattn_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+# The mutation tests point this at deliberately broken builds of the oracle.
+_LIB = os.environ.get("LINATTN_ORACLE_LIB_OVERRIDE", _LIB)
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile linattn_oracle.c into liboracle.so with gcc (-O2, OpenMP)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+               "-Wall", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        fp = ctypes.POINTER(ctypes.c_float)
+        L, D = ctypes.c_long, ctypes.c_double
+        lib.oracle_causal.argtypes = [L, L, L, D, fp, fp, fp, dp, dp, dp, dp, dp]
+        lib.oracle_causal.restype = None
+        lib.oracle_decode_step.argtypes = [L, L, D, fp, fp, fp, dp, dp, dp]
+        lib.oracle_decode_step.restype = None
+        lib.oracle_noncausal.argtypes = [L, L, L, D, fp, fp, fp, dp, dp, dp]
+        lib.oracle_noncausal.restype = None
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f32(x) -> np.ndarray:
+    if hasattr(x, "detach"):  # torch tensor (CPU); bf16 -> float32 is exact
+        x = x.detach().float().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+
+def _f64(x) -> np.ndarray:
+    if hasattr(x, "detach"):
+        x = x.detach().double().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _fptr(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+def _dptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def causal(q, k, v, eps: float, z_in=None, s_in=None, want_out: bool = True):
+    """Causal linear attention, recurrent form.
+
+    q, k, v: [..., N, d] (leading dims flattened to heads).
+    z_in: [..., d, d] or None; s_in: [..., d] or None.
+    Returns (out [..., N, d] or None, z_out [..., d, d], s_out [..., d]) in float64.
+    """
+    qa, ka, va = _f32(q), _f32(k), _f32(v)
+    lead, (N, d) = qa.shape[:-2], qa.shape[-2:]
+    BH = int(np.prod(lead)) if lead else 1
+    zi = None if z_in is None else _f64(z_in).reshape(BH, d, d)
+    si = None if s_in is None else _f64(s_in).reshape(BH, d)
+    out = np.empty((BH, N, d), np.float64) if want_out else None
+    zo = np.empty((BH, d, d), np.float64)
+    so = np.empty((BH, d), np.float64)
+    _load().oracle_causal(BH, N, d, float(eps), _fptr(qa), _fptr(ka), _fptr(va),
+                          _dptr(zi), _dptr(si), _dptr(out), _dptr(zo), _dptr(so))
+    return (None if out is None else out.reshape(*lead, N, d),
+            zo.reshape(*lead, d, d), so.reshape(*lead, d))
+
+
+def decode_step(q, k, v, z, s, eps: float):
+    """One recurrent step per head.  q, k, v: [..., d]; z: [..., d, d]; s: [..., d].
+
+    Returns (out [..., d], z_new, s_new) in float64; the inputs are not modified.
+    """
+    qa, ka, va = _f32(q), _f32(k), _f32(v)
+    lead, d = qa.shape[:-1], qa.shape[-1]
+    BH = int(np.prod(lead)) if lead else 1
+    zz = _f64(z).reshape(BH, d, d).copy()
+    ss = _f64(s).reshape(BH, d).copy()
+    out = np.empty((BH, d), np.float64)
+    _load().oracle_decode_step(BH, d, float(eps), _fptr(qa), _fptr(ka), _fptr(va),
+                               _dptr(zz), _dptr(ss), _dptr(out))
+    return out.reshape(*lead, d), zz.reshape(*lead, d, d), ss.reshape(*lead, d)
+
+
+def noncausal(q, k, v, eps: float, want_out: bool = True):
+    """Non-causal linear attention.  Returns (out or None, z, s) in float64."""
+    qa, ka, va = _f32(q), _f32(k), _f32(v)
+    lead, (N, d) = qa.shape[:-2], qa.shape[-2:]
+    BH = int(np.prod(lead)) if lead else 1
+    out = np.empty((BH, N, d), np.float64) if want_out else None
+    zo = np.empty((BH, d, d), np.float64)
+    so = np.empty((BH, d), np.float64)
+    _load().oracle_noncausal(BH, N, d, float(eps), _fptr(qa), _fptr(ka), _fptr(va),
+                             _dptr(out), _dptr(zo), _dptr(so))
+    return (None if out is None else out.reshape(*lead, N, d),
+            zo.reshape(*lead, d, d), so.reshape(*lead, d))

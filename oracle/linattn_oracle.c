@@ -1,0 +1,188 @@
+/*
+ * linattn_oracle.c -- plain fp64 CPU oracle for causal / decode / non-causal
+ * linear attention with the feature map phi(x) = elu(x) + 1.
+ *
+ * TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the smoke
+ * check and the benchmark's CPU-baseline leg may load this library.  It
+ * shares no source, header, table or helper with the HIP library: it is the
+ * slow, obviously-correct definition that the GPU path is compared against.
+ *
+ * Sources (web pages, cited by title and section):
+ *  - "Attention Kernel Mask" (allenlu2009.github.io, 2024-11-17), section
+ *    "Cumsum" (the plain-words cumulative-sum derivation): the running key sum
+ *    S_t = S_{t-1} + k_t, the running context Z_t = Z_{t-1} + k_t v_t^T, the
+ *    normaliser D_t = q_t^T S_t + eps and the output out_t = q_t^T Z_t / D_t;
+ *    causality means position t only sees positions <= t.
+ *  - The same page, "How to accelerate causal linear attention", mode 2 (pure
+ *    sequential / RNN mode): one token at a time with a fixed-size state, which
+ *    is the decode step below.
+ *  - The same page, "Non-causal Bi-Directional Attention Kernel" and its
+ *    remark that non-causal attention reads the inputs once: one global
+ *    Z = sum_t phi(k_t) v_t^T and S = sum_t phi(k_t) applied to every query.
+ *  - "Segment-Wise Attention" (GitHub issue on an Infini-attention
+ *    implementation): the compressive memory is an associative matrix whose
+ *    update and retrieval follow the linear-attention rule of "Transformers
+ *    are RNNs" (Katharopoulos et al. 2020), carried from segment to segment.
+ *    That paper's feature map is elu(x) + 1; the printed recurrence uses raw
+ *    q, k, and the reading taken here applies phi to both q and k.
+ *
+ * Conventions: every input tensor is contiguous [BH][N][d] float (bf16 and
+ * fp32 inputs are both exact in float); all arithmetic and all outputs are
+ * double.  The state Z of one head is [d][d] row-major with Z[j][c] = sum over
+ * tokens of phi(k)_j * v_c (key dimension first), S is [d].
+ *
+ * Parity pins: brute-force quadratic masked evaluation, an independent chunked
+ * evaluator, closed forms and invariants (see the oracle pin tests).
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* elu(x) + 1 with elu's alpha = 1: x + 1 above zero, exp(x) at or below it.
+ * Both branches give 1 at x = 0. */
+static double phi(double x) { return x > 0.0 ? x + 1.0 : exp(x); }
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Causal linear attention over N tokens of each of BH heads, recurrent form
+ * ("Attention Kernel Mask", section "Cumsum"), with phi applied to q and k:
+ *   f = phi(k_t);  Z += f v_t^T;  S += f;
+ *   g = phi(q_t);  out_t = (g^T Z) / (g . S + eps)
+ * The update comes before the readout, so token t attends to itself.
+ * z_in / s_in (may be NULL = zeros) give the state carried in from earlier
+ * segments ("Segment-Wise Attention"); z_out / s_out (may be NULL) receive the
+ * state after the last token.  out may be NULL (state only).
+ */
+void oracle_causal(long BH, long N, long d, double eps,
+                   const float *q, const float *k, const float *v,
+                   const double *z_in, const double *s_in,
+                   double *out, double *z_out, double *s_out)
+{
+    long h;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (h = 0; h < BH; ++h) {
+        double *Z = (double *)calloc((size_t)(d * d), sizeof(double));
+        double *S = (double *)calloc((size_t)d, sizeof(double));
+        double *f = (double *)malloc((size_t)d * sizeof(double));
+        double *g = (double *)malloc((size_t)d * sizeof(double));
+        long t, j, c;
+        if (z_in) memcpy(Z, z_in + h * d * d, (size_t)(d * d) * sizeof(double));
+        if (s_in) memcpy(S, s_in + h * d, (size_t)d * sizeof(double));
+        for (t = 0; t < N; ++t) {
+            const float *kt = k + (h * N + t) * d;
+            const float *vt = v + (h * N + t) * d;
+            const float *qt = q + (h * N + t) * d;
+            for (j = 0; j < d; ++j) f[j] = phi((double)kt[j]);
+            for (j = 0; j < d; ++j) {
+                for (c = 0; c < d; ++c) Z[j * d + c] += f[j] * (double)vt[c];
+                S[j] += f[j];
+            }
+            if (!out) continue;
+            for (j = 0; j < d; ++j) g[j] = phi((double)qt[j]);
+            {
+                double den = 0.0;
+                double *ot = out + (h * N + t) * d;
+                for (j = 0; j < d; ++j) den += g[j] * S[j];
+                den += eps;
+                for (c = 0; c < d; ++c) {
+                    double num = 0.0;
+                    for (j = 0; j < d; ++j) num += g[j] * Z[j * d + c];
+                    ot[c] = num / den;
+                }
+            }
+        }
+        if (z_out) memcpy(z_out + h * d * d, Z, (size_t)(d * d) * sizeof(double));
+        if (s_out) memcpy(s_out + h * d, S, (size_t)d * sizeof(double));
+        free(Z); free(S); free(f); free(g);
+    }
+}
+
+/*
+ * One generation step for each of BH heads ("Attention Kernel Mask", mode 2,
+ * pure sequential / RNN mode: fixed memory, no KV cache).  q, k, v are [BH][d];
+ * Z [BH][d][d] and S [BH][d] are updated in place, then read:
+ *   Z += phi(k) v^T;  S += phi(k);  out = phi(q)^T Z / (phi(q) . S + eps)
+ */
+void oracle_decode_step(long BH, long d, double eps,
+                        const float *q, const float *k, const float *v,
+                        double *Z, double *S, double *out)
+{
+    long h;
+#pragma omp parallel for schedule(static)
+    for (h = 0; h < BH; ++h) {
+        double *Zh = Z + h * d * d, *Sh = S + h * d;
+        const float *qh = q + h * d, *kh = k + h * d, *vh = v + h * d;
+        double den = 0.0;
+        long j, c;
+        for (j = 0; j < d; ++j) {
+            double fj = phi((double)kh[j]);
+            for (c = 0; c < d; ++c) Zh[j * d + c] += fj * (double)vh[c];
+            Sh[j] += fj;
+        }
+        for (j = 0; j < d; ++j) den += phi((double)qh[j]) * Sh[j];
+        den += eps;
+        for (c = 0; c < d; ++c) {
+            double num = 0.0;
+            for (j = 0; j < d; ++j) num += phi((double)qh[j]) * Zh[j * d + c];
+            out[h * d + c] = num / den;
+        }
+    }
+}
+
+/*
+ * Non-causal (bidirectional) linear attention ("Attention Kernel Mask",
+ * section "Non-causal Bi-Directional Attention Kernel"): every query sees all
+ * N keys of its head through one global state
+ *   Z = sum_t phi(k_t) v_t^T,  S = sum_t phi(k_t),
+ *   out_t = phi(q_t)^T Z / (phi(q_t) . S + eps).
+ * z_out / s_out (may be NULL) receive the global state; out may be NULL.
+ */
+void oracle_noncausal(long BH, long N, long d, double eps,
+                      const float *q, const float *k, const float *v,
+                      double *out, double *z_out, double *s_out)
+{
+    long h;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (h = 0; h < BH; ++h) {
+        double *Z = (double *)calloc((size_t)(d * d), sizeof(double));
+        double *S = (double *)calloc((size_t)d, sizeof(double));
+        double *g = (double *)malloc((size_t)d * sizeof(double));
+        long t, j, c;
+        for (t = 0; t < N; ++t) {
+            const float *kt = k + (h * N + t) * d;
+            const float *vt = v + (h * N + t) * d;
+            for (j = 0; j < d; ++j) {
+                double fj = phi((double)kt[j]);
+                for (c = 0; c < d; ++c) Z[j * d + c] += fj * (double)vt[c];
+                S[j] += fj;
+            }
+        }
+        for (t = 0; out && t < N; ++t) {
+            const float *qt = q + (h * N + t) * d;
+            double *ot = out + (h * N + t) * d;
+            double den = 0.0;
+            for (j = 0; j < d; ++j) g[j] = phi((double)qt[j]);
+            for (j = 0; j < d; ++j) den += g[j] * S[j];
+            den += eps;
+            for (c = 0; c < d; ++c) {
+                double num = 0.0;
+                for (j = 0; j < d; ++j) num += g[j] * Z[j * d + c];
+                ot[c] = num / den;
+            }
+        }
+        if (z_out) memcpy(z_out + h * d * d, Z, (size_t)(d * d) * sizeof(double));
+        if (s_out) memcpy(s_out + h * d, S, (size_t)d * sizeof(double));
+        free(Z); free(S); free(g);
+    }
+}

@@ -1,0 +1,68 @@
+"""The pins must catch plausible slips in the oracle.
+
+Each case plants one mistake in a copy of the oracle's C source (here, on the
+CPU), builds it, and runs the pin suite against it in a subprocess: at least
+one pin must fail.  The unmodified source must pass the same run.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "linattn_oracle.c")
+
+MUTANTS = {
+    "phi_drops_plus_one": ("x > 0.0 ? x + 1.0 : exp(x)", "x > 0.0 ? x : exp(x)"),
+    "phi_branch_flipped": ("x > 0.0 ? x + 1.0 : exp(x)", "x < 0.0 ? x + 1.0 : exp(x)"),
+    "state_update_transposed": ("for (c = 0; c < d; ++c) Z[j * d + c] += f[j] * (double)vt[c];",
+                                "for (c = 0; c < d; ++c) Z[c * d + j] += f[j] * (double)vt[c];"),
+    "key_sum_without_phi": ("                S[j] += f[j];\n            }\n            if (!out)",
+                            "                S[j] += (double)kt[j];\n            }\n            if (!out)"),
+    "eps_dropped": ("                den += eps;\n                for (c = 0; c < d; ++c) {\n                    double num = 0.0;\n                    for (j = 0; j < d; ++j) num += g[j] * Z[j * d + c];\n                    ot[c]",
+                    "                den += 0.0;\n                for (c = 0; c < d; ++c) {\n                    double num = 0.0;\n                    for (j = 0; j < d; ++j) num += g[j] * Z[j * d + c];\n                    ot[c]"),
+    "readout_transposed": ("for (j = 0; j < d; ++j) num += g[j] * Z[j * d + c];\n                    ot[c] = num / den;\n                }\n            }\n        }",
+                           "for (j = 0; j < d; ++j) num += g[j] * Z[c * d + j];\n                    ot[c] = num / den;\n                }\n            }\n        }"),
+    "query_uses_key": ("for (j = 0; j < d; ++j) g[j] = phi((double)qt[j]);\n            {",
+                       "for (j = 0; j < d; ++j) g[j] = phi((double)kt[j]);\n            {"),
+    "state_in_ignored": ("if (z_in) memcpy(Z,", "if (0) memcpy(Z,"),
+    "exclusive_causality": ("            const float *kt = k + (h * N + t) * d;\n            const float *vt = v + (h * N + t) * d;\n            const float *qt = q + (h * N + t) * d;",
+                            "            const float *kt = k + (h * N + t) * d;\n            const float *vt = v + (h * N + t) * d;\n            const float *qt = q + (h * N + (t + 1 < N ? t + 1 : t)) * d;"),
+    "decode_skips_key_sum": ("            Sh[j] += fj;", "            Sh[j] += 0.0 * fj;"),
+    "noncausal_sum_stops_early": ("        for (t = 0; t < N; ++t) {\n            const float *kt = k + (h * N + t) * d;\n            const float *vt = v + (h * N + t) * d;\n            for (j = 0; j < d; ++j) {\n                double fj",
+                                  "        for (t = 0; t + 1 < N; ++t) {\n            const float *kt = k + (h * N + t) * d;\n            const float *vt = v + (h * N + t) * d;\n            for (j = 0; j < d; ++j) {\n                double fj"),
+}
+
+
+def _build(tmp_path, name, src_text):
+    c = tmp_path / f"{name}.c"
+    so = tmp_path / f"lib{name}.so"
+    c.write_text(src_text)
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-o", str(so), str(c), "-lm"],
+                   check=True)
+    return str(so)
+
+
+def _run_pins(lib):
+    env = dict(os.environ, LINATTN_ORACLE_LIB_OVERRIDE=lib, OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    return r.returncode, r.stdout[-2000:]
+
+
+def test_unmodified_oracle_passes_pins(tmp_path):
+    lib = _build(tmp_path, "clean", open(SRC).read())
+    rc, out = _run_pins(lib)
+    assert rc == 0, out
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    src = open(SRC).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique/absent"
+    lib = _build(tmp_path, name, src.replace(old, new))
+    rc, out = _run_pins(lib)
+    assert rc != 0, f"mutant {name} passed every pin:\n{out}"
