@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Throughput of causal linear attention (phi = elu + 1) on one MI355X.
+
+One step = one la_causal_fwd call on the headline workload (B=4, H=8,
+N=4096, d=64, bf16 inputs, fp32 state and outputs, chunk 64, eps 1e-6), with
+inputs resident in HBM.  Eight input/output sets (about 670 MB, more than
+twice the 256 MB Infinity Cache) are rotated so every step reads HBM.
+
+Prints ONE JSON line: value = B*H*N head-tokens per second over the timed
+steps; `roofline` = algorithmic bytes of one call / its average duration
+(HIP events on the launch stream) against 8 TB/s; `cpu_baseline` = the fp64
+oracle on the host cores; `workloads` = the segment-carried, decode and
+non-causal workloads timed the same way.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal linear-attn fwd tokens/sec (B·H·N/s) at d=64/128 + % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def alg_bytes_causal(w, with_state_io=False):
+    """inputs once, fp32 outputs once (+ fp32 state in and out per head)."""
+    b = w.B * w.H * w.N * (3 * w.d * w.dtype.itemsize + 4 * w.d)
+    if with_state_io:
+        b += 2 * w.B * w.H * (w.d * w.d + w.d) * 4
+    return b
+
+
+def time_steps(fn, steps, warmup, n_rot):
+    """Run fn(i) warmup + steps times; return (total_ms, per-step event ms list)."""
+    import torch
+    for i in range(warmup):
+        fn(i % n_rot)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(steps):
+        evs[i][0].record()
+        fn((warmup + i) % n_rot)
+        evs[i][1].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    return t_start.elapsed_time(t_end), [a.elapsed_time(b) for a, b in evs]
+
+
+def roofline(bytes_per_call, ms_per_call, traffic=None):
+    achieved = bytes_per_call / (ms_per_call * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+
+def bench_headline(args, torch, la, inp):
+    w = inp.WORKLOADS[inp.HEADLINE]
+    dev = torch.device("cuda:0")
+    q, k, v = inp.workload_inputs(w)
+    n_rot = args.rotate
+    sets = []
+    for _ in range(n_rot):
+        sets.append((q.to(dev), k.to(dev), v.to(dev),
+                     torch.empty(w.B, w.H, w.N, w.d, dtype=torch.float32, device=dev)))
+    ws = torch.empty(max(1, la.la_causal_fwd_workspace(w.B, w.H, w.N, w.d, w.dtype, w.chunk)),
+                     dtype=torch.uint8, device=dev)
+
+    def step(i):
+        a = sets[i]
+        la.la_causal_fwd(a[0], a[1], a[2], a[3], chunk=w.chunk, eps=w.eps, workspace=ws)
+
+    total_ms, per = time_steps(step, args.steps, args.warmup, n_rot)
+    per_call = sum(per) / len(per)
+    return w, total_ms, per_call, (q, k, v)
+
+
+def bench_segmented(args, torch, la, inp):
+    w = inp.WORKLOADS[inp.SEGMENTED]
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in inp.workload_inputs(w))
+    B, H, N, d = q.shape
+    out = torch.empty(B, H, N, d, dtype=torch.float32, device=dev)
+    zs = [torch.zeros(B, H, d, d, device=dev) for _ in range(2)]
+    ss = [torch.zeros(B, H, d, device=dev) for _ in range(2)]
+    ws = torch.empty(max(1, la.la_causal_fwd_workspace(B, H, w.segment, d, w.dtype, 0)), dtype=torch.uint8,
+                     device=dev)
+    nseg = N // w.segment
+
+    def step(_):
+        for i in range(nseg):
+            sl = slice(i * w.segment, (i + 1) * w.segment)
+            la.la_causal_fwd(q[:, :, sl], k[:, :, sl], v[:, :, sl], out[:, :, sl], eps=w.eps,
+                             z_in=zs[i & 1] if i else None, s_in=ss[i & 1] if i else None,
+                             z_out=zs[(i + 1) & 1], s_out=ss[(i + 1) & 1], workspace=ws)
+
+    steps = max(3, args.steps // 4)
+    total_ms, per = time_steps(step, steps, max(1, args.warmup // 2), 1)
+    ms = total_ms / steps
+    seg_w = inp.Workload("segment", "causal", w.dtype, w.B, w.H, w.segment, w.d, 0, 1.0)
+    b_call = alg_bytes_causal(seg_w, with_state_io=True)
+    return {"workload": w.name, "value": round(w.head_tokens / (ms * 1e-3), 1), "unit": "head-tokens/s",
+            "ms_per_step": round(ms, 4), "calls_per_step": nseg,
+            "roofline": roofline(b_call, ms / nseg)}
+
+
+def bench_decode(args, torch, la, inp):
+    w = inp.WORKLOADS[inp.DECODE]
+    dev = torch.device("cuda:0")
+    (pq, pk, pv), (sq, sk, sv) = inp.workload_inputs(w)
+    B, H, d, T = w.B, w.H, w.d, w.N
+    sqd, skd, svd = sq.to(dev), sk.to(dev), sv.to(dev)
+    res = {}
+    for label, nstate in (("hot_state", 1), ("cold_state_x4", 4)):
+        zs, ss = [], []
+        for _ in range(nstate):
+            z = torch.empty(B, H, d, d, device=dev)
+            s = torch.empty(B, H, d, device=dev)
+            la.la_causal_fwd(pq.to(dev), pk.to(dev), pv.to(dev), None, eps=w.eps, z_out=z, s_out=s)
+            zs.append(z)
+            ss.append(s)
+        out = torch.empty(B, H, d, device=dev)
+
+        def step(i):
+            t = i % T
+            la.la_decode_step(sqd[t], skd[t], svd[t], zs[i % nstate], ss[i % nstate], out, eps=w.eps)
+
+        total_ms, per = time_steps(step, min(T, 256), 16, 10 ** 9)
+        ms = total_ms / min(T, 256)
+        per_call = sum(per) / len(per)
+        bpc = B * H * (2 * (d * d + d) * 4 + 3 * d * w.dtype.itemsize + d * 4)
+        res[label] = {"ms_per_step": round(ms, 5), "value": round(B * H / (ms * 1e-3), 1),
+                      "roofline": roofline(bpc, per_call)}
+    return {"workload": w.name, "unit": "head-tokens/s", **res}
+
+
+def bench_noncausal(args, torch, la, inp):
+    w = inp.WORKLOADS[inp.NONCAUSAL]
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in inp.workload_inputs(w))
+    out = torch.empty(w.B, w.H, w.N, w.d, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, la.la_noncausal_workspace(w.B, w.H, w.N, w.d, w.dtype)), dtype=torch.uint8, device=dev)
+
+    def step(_):
+        la.la_noncausal_fwd(q, k, v, out, eps=w.eps, workspace=ws)
+
+    steps = max(3, args.steps // 2)
+    total_ms, per = time_steps(step, steps, 2, 1)
+    per_call = sum(per) / len(per)
+    return {"workload": w.name, "value": round(w.head_tokens / (per_call * 1e-3), 1), "unit": "head-tokens/s",
+            "ms_per_step": round(per_call, 4), "roofline": roofline(alg_bytes_causal(w), per_call)}
+
+
+def cpu_baseline(w, qkv):
+    import oracle
+    q, k, v = qkv
+    t0 = time.perf_counter()
+    oracle.causal(q, k, v, w.eps)
+    dt = time.perf_counter() - t0
+    return {"value": round(w.head_tokens / dt, 1), "unit": "head-tokens/s", "cores": oracle.max_threads(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"one full step of {w.name}: all {w.B * w.H} heads x {w.N} tokens, fp64 recurrent form"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rotate", type=int, default=8, help="input/output sets rotated over the steps")
+    ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); run it with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import segment_wise_compressive_amd as la
+    from segment_wise_compressive_amd import inputs as inp
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    la.load_library()
+
+    log("headline workload ...")
+    w, total_ms, per_call, qkv = bench_headline(args, torch, la, inp)
+    ms_step = total_ms / args.steps
+    line = {
+        "metric": METRIC,
+        "value": round(w.head_tokens * args.steps / (total_ms * 1e-3), 1),
+        "unit": "head-tokens/s (B*H*N per second)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "chunk": w.chunk,
+                   "input_dtype": "bf16", "state_and_output_dtype": "fp32", "eps": w.eps, "seed": w.seed,
+                   "rotated_sets": args.rotate},
+        "roofline": roofline(alg_bytes_causal(w), per_call),
+    }
+    line["roofline"]["kernels"] = "k_group_state + k_chunk_fwd (one la_causal_fwd call)"
+    if not args.headline_only:
+        log("segmented workload ...")
+        line.setdefault("workloads", {})["segmented"] = bench_segmented(args, torch, la, inp)
+        log("decode workload ...")
+        line["workloads"]["decode"] = bench_decode(args, torch, la, inp)
+        log("non-causal workload ...")
+        line["workloads"]["noncausal"] = bench_noncausal(args, torch, la, inp)
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        line["cpu_baseline"] = cpu_baseline(w, qkv)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

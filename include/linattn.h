@@ -1,0 +1,148 @@
+/*
+ * linattn.h -- C ABI of liblinattn.so: causal (segment-carried), decode and
+ * non-causal linear attention with the feature map phi(x) = elu(x) + 1, on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (web pages, cited by title and section):
+ *  - "Attention Kernel Mask" (allenlu2009.github.io, 2024-11-17), section
+ *    "Cumsum": running key sum S_t = S_{t-1} + phi(k_t), running context
+ *    Z_t = Z_{t-1} + phi(k_t) v_t^T, normaliser D_t = phi(q_t) . S_t + eps and
+ *    output out_t = phi(q_t)^T Z_t / D_t; token t sees positions <= t.
+ *  - Same page, "How to accelerate causal linear attention": chunk-sequential
+ *    mode (inter-chunk term from the carried state plus an intra-chunk masked
+ *    quadratic term), the materialised mode (chunk states first, then the
+ *    chunks in parallel), and mode 2 (recurrent generation).
+ *  - Same page, "Non-causal Bi-Directional Attention Kernel".
+ *  - "Segment-Wise Attention" (GitHub issue on Infini-attention): the sequence
+ *    is cut into segments that are processed one after another with the
+ *    compressive memory -- here the (Z, S) state -- carried between them; the
+ *    memory update and retrieval follow the linear-attention rule of
+ *    "Transformers are RNNs", whose feature map is elu + 1.
+ *
+ * Common conventions
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
+ *    allocates no device memory and keeps no global state; it is reentrant.
+ *    Calls on different streams must not share output or workspace buffers.
+ *  - q, k, v are [B, H, N, d] with element strides (b, h, n) given in
+ *    la_strides and a unit stride along d.  dtype LA_BF16 or LA_F32.
+ *  - out is float32 [B, H, N, d] with its own strides (unit stride along d).
+ *  - State per head: Z float32 [d][d] row-major, Z[j][c] = sum phi(k)_j v_c
+ *    (key dimension first), and S float32 [d].  State tensors are contiguous
+ *    [B, H, d, d] and [B, H, d].
+ *  - d must be 32, 64 or 128.  eps must be finite and >= 0.
+ *  - Alignment: every tensor pointer 16-byte aligned; every stride times the
+ *    element size a multiple of 16 bytes.
+ *  - Errors: argument errors are detected synchronously before any device work
+ *    and nothing is written.  A failed kernel launch returns LA_ERR_LAUNCH.
+ *    Faults inside kernels surface at the caller's next synchronisation.
+ *  - Every call is asynchronous on `hip_stream` (a hipStream_t; NULL = the
+ *    null stream).
+ *  - Results are deterministic: the same inputs, sizes and chunk give bitwise
+ *    identical outputs (no floating-point atomics).
+ *  - Non-finite inputs propagate to every later output of their head and to
+ *    the carried state; in the causal kernels an infinite v may also turn the
+ *    outputs of earlier tokens of the same chunk into NaN.
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LA_OK = 0,
+    LA_ERR_NULL = 1,        /* a required pointer is NULL */
+    LA_ERR_SHAPE = 2,       /* a negative size, or sizes too large for 32-bit indexing */
+    LA_ERR_DTYPE = 3,       /* dtype is not LA_F32 or LA_BF16 */
+    LA_ERR_ALIGN = 4,       /* a pointer or a stride is not 16-byte aligned */
+    LA_ERR_UNSUPPORTED = 5, /* d not in {32,64,128}, or chunk not in {0,16,32,64,128} */
+    LA_ERR_VALUE = 6,       /* eps negative or not finite */
+    LA_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than the query returned */
+    LA_ERR_ALIAS = 8,       /* an output state overlaps an input state other than exactly */
+    LA_ERR_LAUNCH = 9       /* a HIP launch or copy failed */
+} la_status;
+
+typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+
+/* Element strides of a [B, H, N, d] tensor; the stride along d is 1. */
+typedef struct {
+    int64_t b, h, n;
+} la_strides;
+
+/* Workspace flag: the causal call will pass z_out == z_in and/or s_out == s_in. */
+#define LA_WS_INPLACE_STATE 1
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *la_status_str(la_status s);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int la_version(void);
+
+/*
+ * Causal linear attention forward ("Attention Kernel Mask", section "Cumsum",
+ * computed chunk by chunk as in the chunk-sequential mode, with the sequence
+ * split into groups whose starting states come from a scan of group states,
+ * as in the materialised mode).  For every head (b, h) and token t:
+ *   Z = Z_in + sum_{i<=t} phi(k_i) v_i^T,  S = S_in + sum_{i<=t} phi(k_i),
+ *   out_t = phi(q_t)^T Z / (phi(q_t) . S + eps).
+ * z_in / s_in: state carried in from earlier segments ("Segment-Wise
+ * Attention"); NULL means zeros (each independently).
+ * z_out / s_out: state after the last token; NULL means not written.  They may
+ * equal z_in / s_in exactly (in place) if the workspace was sized with
+ * LA_WS_INPLACE_STATE; any other overlap is LA_ERR_ALIAS.
+ * out: NULL computes only the state (prefill / state-only use); then z_out
+ * and s_out must not both be NULL.
+ * chunk: 0 = default; otherwise 16, 32, 64 or 128 tokens.  It is a tuning
+ * choice only: results agree for every chunk up to rounding.  A chunk too
+ * large for the on-chip memory of a (dtype, d) pair is reduced to the largest
+ * one that fits.
+ * N = 0 copies the input state (or zeros) to the output state.
+ * Workspace: at least la_causal_fwd_workspace(...) bytes of device memory,
+ * any contents; 256-byte alignment recommended.  NULL is allowed when the
+ * query returns 0.
+ */
+size_t la_causal_fwd_workspace(int B, int H, int N, int d, la_dtype dt, int chunk, int flags);
+la_status la_causal_fwd(const void *q, la_strides sq, const void *k, la_strides sk,
+                        const void *v, la_strides sv, la_dtype dt,
+                        float *out, la_strides so,
+                        int B, int H, int N, int d, int chunk, float eps,
+                        const float *z_in, const float *s_in,
+                        float *z_out, float *s_out,
+                        void *workspace, size_t ws_bytes, void *hip_stream);
+
+/*
+ * One generation step per head ("Attention Kernel Mask", mode 2: recurrent
+ * generation with a fixed-size state and no KV cache):
+ *   Z += phi(k) v^T;  S += phi(k);  out = phi(q)^T Z / (phi(q) . S + eps).
+ * The update precedes the readout, so the new token attends to itself.
+ * q, k, v: contiguous [B, H, d] of dtype dt.  z [B, H, d, d] and s [B, H, d]
+ * are float32, read and updated in place.  out: float32 [B, H, d].
+ */
+la_status la_decode_step(const void *q, const void *k, const void *v, la_dtype dt,
+                         float *z, float *s, float *out,
+                         int B, int H, int d, float eps, void *hip_stream);
+
+/*
+ * Non-causal (bidirectional) linear attention ("Attention Kernel Mask",
+ * section "Non-causal Bi-Directional Attention Kernel"): per head
+ *   Z = sum_t phi(k_t) v_t^T,  S = sum_t phi(k_t),
+ *   out_t = phi(q_t)^T Z / (phi(q_t) . S + eps)   for every t.
+ * The sums over t are split across workgroups and reduced in a fixed order.
+ * Workspace: at least la_noncausal_workspace(...) bytes, any contents.
+ */
+size_t la_noncausal_workspace(int B, int H, int N, int d, la_dtype dt);
+la_status la_noncausal_fwd(const void *q, la_strides sq, const void *k, la_strides sk,
+                           const void *v, la_strides sv, la_dtype dt,
+                           float *out, la_strides so,
+                           int B, int H, int N, int d, float eps,
+                           void *workspace, size_t ws_bytes, void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

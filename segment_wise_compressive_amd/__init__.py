@@ -1,1 +1,248 @@
-"""MI355X-native causal / decode / non-causal linear attention (phi = elu + 1)."""
+"""MI355X-native linear attention with phi(x) = elu(x) + 1.
+
+Thin Python binding over the C ABI of ``liblinattn.so`` (declared in
+``include/linattn.h``).  The functions named ``la_*`` mirror the C entry
+points one to one: they only check and marshal arguments (device pointers,
+strides, the current HIP stream) and raise ``LinAttnError`` on a non-OK status.
+Every step of the computation runs in the library's HIP kernels; there is no
+fallback of any kind, and a missing library is an error.
+
+PyTorch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "LinAttnError", "LA_F32", "LA_BF16", "LA_WS_INPLACE_STATE",
+    "library_path", "load_library",
+    "la_status_str", "la_version",
+    "la_causal_fwd_workspace", "la_causal_fwd",
+    "la_decode_step",
+    "la_noncausal_workspace", "la_noncausal_fwd",
+    "causal_fwd", "noncausal_fwd", "decode_step",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIBPATH = os.path.join(_HERE, "liblinattn.so")
+_lib = None
+
+LA_F32, LA_BF16 = 0, 1
+LA_WS_INPLACE_STATE = 1
+
+
+class LinAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {la_status_str(status)} (status {status})")
+        self.status = status
+
+
+class la_strides(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("n", ctypes.c_int64)]
+
+
+def library_path() -> str:
+    return _LIBPATH
+
+
+def load_library():
+    """Load liblinattn.so (built in-tree).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIBPATH):
+        raise RuntimeError(f"{_LIBPATH} is not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(_LIBPATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    S = la_strides
+    lib.la_status_str.argtypes = [i32]
+    lib.la_status_str.restype = ctypes.c_char_p
+    lib.la_version.argtypes = []
+    lib.la_version.restype = i32
+    lib.la_causal_fwd_workspace.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.la_causal_fwd_workspace.restype = sz
+    lib.la_causal_fwd.argtypes = [vp, S, vp, S, vp, S, i32, vp, S, i32, i32, i32, i32, i32, f32,
+                                  vp, vp, vp, vp, vp, sz, vp]
+    lib.la_causal_fwd.restype = i32
+    lib.la_decode_step.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, f32, vp]
+    lib.la_decode_step.restype = i32
+    lib.la_noncausal_workspace.argtypes = [i32, i32, i32, i32, i32]
+    lib.la_noncausal_workspace.restype = sz
+    lib.la_noncausal_fwd.argtypes = [vp, S, vp, S, vp, S, i32, vp, S, i32, i32, i32, i32, f32, vp, sz, vp]
+    lib.la_noncausal_fwd.restype = i32
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------- marshalling
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return LA_F32
+    if t.dtype == torch.bfloat16:
+        return LA_BF16
+    raise TypeError(f"q, k, v must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _strides(t: torch.Tensor) -> la_strides:
+    if t.dim() != 4 or (t.shape[-1] > 1 and t.stride(-1) != 1):
+        raise ValueError("expected a [B, H, N, d] tensor with unit stride along d")
+    return la_strides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _stream(stream, device) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise LinAttnError(status, where)
+
+
+def _state_check(t, shape, name):
+    if t is None:
+        return
+    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)}")
+
+
+# ---------------------------------------------------------------- C ABI mirrors
+def la_status_str(status: int) -> str:
+    return load_library().la_status_str(int(status)).decode()
+
+
+def la_version() -> int:
+    return int(load_library().la_version())
+
+
+def la_causal_fwd_workspace(B: int, H: int, N: int, d: int, dtype: torch.dtype,
+                            chunk: int = 0, inplace_state: bool = False) -> int:
+    code = LA_F32 if dtype == torch.float32 else LA_BF16
+    return int(load_library().la_causal_fwd_workspace(B, H, N, d, code, chunk,
+                                                       LA_WS_INPLACE_STATE if inplace_state else 0))
+
+
+def la_causal_fwd(q, k, v, out=None, *, chunk: int = 0, eps: float = 1e-6,
+                  z_in=None, s_in=None, z_out=None, s_out=None,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Causal linear attention forward (see la_causal_fwd in linattn.h).
+
+    q, k, v: [B, H, N, d] bf16 or fp32 CUDA tensors (any strides with unit d stride).
+    out: float32 [B, H, N, d] or None (state only).  States: float32 contiguous
+    [B, H, d, d] / [B, H, d]; z_out/s_out may be the z_in/s_in tensors themselves.
+    """
+    B, H, N, d = q.shape
+    if tuple(k.shape) != (B, H, N, d) or tuple(v.shape) != (B, H, N, d):
+        raise ValueError("q, k, v must have the same shape")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must have the same dtype")
+    if out is not None and (out.dtype != torch.float32 or tuple(out.shape) != (B, H, N, d)):
+        raise ValueError("out must be float32 [B, H, N, d]")
+    for t, shp, nm in ((z_in, (B, H, d, d), "z_in"), (z_out, (B, H, d, d), "z_out"),
+                       (s_in, (B, H, d), "s_in"), (s_out, (B, H, d), "s_out")):
+        _state_check(t, shp, nm)
+    inplace = (z_out is not None and z_in is not None and z_out.data_ptr() == z_in.data_ptr()) or \
+              (s_out is not None and s_in is not None and s_out.data_ptr() == s_in.data_ptr())
+    ws_bytes = la_causal_fwd_workspace(B, H, N, d, q.dtype, chunk, inplace)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    so = _strides(out) if out is not None else la_strides(0, 0, 0)
+    st = load_library().la_causal_fwd(
+        _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v), _dtype_code(q),
+        _ptr(out), so, B, H, N, d, int(chunk), float(eps),
+        _ptr(z_in), _ptr(s_in), _ptr(z_out), _ptr(s_out),
+        _ptr(workspace), have, _stream(stream, q.device))
+    _check(st, "la_causal_fwd")
+
+
+def la_decode_step(q, k, v, z, s, out, *, eps: float = 1e-6, stream=None) -> None:
+    """One recurrent step per head; z, s updated in place (see linattn.h).
+
+    q, k, v: contiguous [B, H, d]; z float32 [B, H, d, d]; s float32 [B, H, d];
+    out float32 [B, H, d].
+    """
+    B, H, d = q.shape
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        if tuple(t.shape) != (B, H, d) or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError(f"{nm} must be a contiguous [B, H, d] tensor of q's dtype")
+    _state_check(z, (B, H, d, d), "z")
+    _state_check(s, (B, H, d), "s")
+    _state_check(out, (B, H, d), "out")
+    st = load_library().la_decode_step(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q),
+                                       _ptr(z), _ptr(s), _ptr(out), B, H, d, float(eps),
+                                       _stream(stream, q.device))
+    _check(st, "la_decode_step")
+
+
+def la_noncausal_workspace(B: int, H: int, N: int, d: int, dtype: torch.dtype) -> int:
+    code = LA_F32 if dtype == torch.float32 else LA_BF16
+    return int(load_library().la_noncausal_workspace(B, H, N, d, code))
+
+
+def la_noncausal_fwd(q, k, v, out, *, eps: float = 1e-6,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Non-causal linear attention forward (see la_noncausal_fwd in linattn.h)."""
+    B, H, N, d = q.shape
+    if tuple(k.shape) != (B, H, N, d) or tuple(v.shape) != (B, H, N, d):
+        raise ValueError("q, k, v must have the same shape")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must have the same dtype")
+    if out.dtype != torch.float32 or tuple(out.shape) != (B, H, N, d):
+        raise ValueError("out must be float32 [B, H, N, d]")
+    ws_bytes = la_noncausal_workspace(B, H, N, d, q.dtype)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().la_noncausal_fwd(
+        _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v), _dtype_code(q),
+        _ptr(out), _strides(out), B, H, N, d, float(eps),
+        _ptr(workspace), have, _stream(stream, q.device))
+    _check(st, "la_noncausal_fwd")
+
+
+# ---------------------------------------------------------------- conveniences
+def causal_fwd(q, k, v, *, eps: float = 1e-6, chunk: int = 0,
+               state: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+               return_state: bool = False):
+    """out = causal linear attention of (q, k, v), optionally carrying (Z, S)."""
+    B, H, N, d = q.shape
+    out = torch.empty(B, H, N, d, dtype=torch.float32, device=q.device)
+    z_in, s_in = state if state is not None else (None, None)
+    z_out = s_out = None
+    if return_state:
+        z_out = torch.empty(B, H, d, d, dtype=torch.float32, device=q.device)
+        s_out = torch.empty(B, H, d, dtype=torch.float32, device=q.device)
+    la_causal_fwd(q, k, v, out, chunk=chunk, eps=eps, z_in=z_in, s_in=s_in, z_out=z_out, s_out=s_out)
+    return (out, (z_out, s_out)) if return_state else out
+
+
+def noncausal_fwd(q, k, v, *, eps: float = 1e-6):
+    B, H, N, d = q.shape
+    out = torch.empty(B, H, N, d, dtype=torch.float32, device=q.device)
+    la_noncausal_fwd(q, k, v, out, eps=eps)
+    return out
+
+
+def decode_step(q, k, v, z, s, *, eps: float = 1e-6):
+    """One generation step; z and s are updated in place.  Returns out [B, H, d]."""
+    out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    la_decode_step(q, k, v, z, s, out, eps=eps)
+    return out
+
+
+def declared_entry_points(header: Optional[str] = None):
+    """Names of the functions declared in include/linattn.h."""
+    header = header or os.path.join(os.path.dirname(_HERE), "include", "linattn.h")
+    text = open(header).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(la_\w+)\s*\(", text, re.M)))
