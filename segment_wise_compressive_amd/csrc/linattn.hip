@@ -168,299 +168,344 @@ struct Args {
     float eps;
     const float *z_in, *s_in;
     float *z_out, *s_out;
-    float *part;  // group partial states [BH][P][Gs][SLOT]
+    float *part;  // per (head, column block) state slots [BH][P][NS][SLOT]
     float *fin;   // reduced states [BH][P][SLOT]
     int P;        // column blocks per head
     int G;        // token groups per head (for this launch)
-    int Gs;       // partial slots per (head, column block)
+    int NS;       // slots per (head, column block)
     int L;        // tokens per group
+    int slot0;    // slot written by group 0 of a group-state launch
 };
 
-// A slot holds one (head, column block) state: Z^T as [DV][D] (value column
-// major, so a lane's 4 key rows are contiguous) followed by S [D].
+// A slot holds one (head, column block) state in the layout of the state
+// tensors: Z[:, block columns] as [D][DV] (key row major) followed by S [D].
 template <int D, int DV> struct Slot { static constexpr int Z = DV * D, SIZE = DV * D + D; };
 
-// LDS bytes of one workgroup: two stages of
-//   phi(Q) [C][D+pad], phi(K) [C][D+pad]            (16-bit or fp32, row major)
-//   phi(K)^T [D][C+pad]  x (2 for bf16: hi and lo)   (token contiguous)
-//   V^T [DV][C+pad]
-// plus the running key sum S (fp32, two copies).
+// ------------------------------------------------------------------ tile geometry
+constexpr int NWAVE = 4;                 // waves per workgroup
+constexpr int NTHR = NWAVE * WAVE;       // threads per workgroup
+
+__host__ __device__ constexpr int pad_of(bool f32) { return f32 ? 4 : 8; }  // 16 bytes of row padding
+
+// LDS bytes of one workgroup (one chunk stage, row major as loaded):
+//   phi(K) [C][D+pad]   (x2 for bf16: hi and lo parts)
+//   V      [C][DV+pad]  (the input values)
+//   Z^T    [DV][D+pad]  (x2 for bf16: hi and lo parts; the shared state)
+//   S      [D]          (fp32)
 __host__ __device__ constexpr int lds_bytes(bool f32, int d, int dv, int c)
 {
-    return 2 * ((2 * c * (d + (f32 ? 4 : 8)) + (f32 ? 1 : 2) * d * (c + (f32 ? 4 : 8)) + dv * (c + (f32 ? 4 : 8)))
-                * (f32 ? 4 : 2)) + 2 * d * 4;
+    return ((f32 ? 1 : 2) * c * (d + pad_of(f32)) + c * (dv + pad_of(f32)) + (f32 ? 1 : 2) * dv * (d + pad_of(f32))) *
+               (f32 ? 4 : 2) + d * 4;
 }
 constexpr int LDS_LIMIT = 160 * 1024;  // per workgroup on gfx950
 
-// ------------------------------------------------------------------ tile geometry
 template <bool F32, int D, int DV, int C>
 struct Geo {
-    typedef typename pick<F32, float, bf16>::type E;        // LDS element
-    typedef typename pick<F32, f32x4, bf16x4>::type Frag;   // K-tile fragment
+    typedef typename pick<F32, float, bf16>::type E;      // LDS element
     static constexpr int JT = D / 16;      // key-dimension tiles
-    static constexpr int TB = C / 16;      // token tiles per chunk
-    static constexpr int NW = DV / 16;     // waves = value-column tiles
-    static constexpr int NT = NW * WAVE;   // threads
-    static constexpr int JS = JT / NW;     // key-sum tiles owned by each wave
-    static constexpr int VEC = Vec<F32>::N;
-    static constexpr int PAD = 16 / (int)sizeof(E);   // 16-byte row padding
-    static constexpr int RQ = D + PAD;     // row stride of phi(Q), phi(K) [token][dim]
-    static constexpr int RT = C + PAD;     // row stride of phi(K)^T [dim][token], V^T [col][token]
-    static constexpr int NKT = F32 ? 1 : 2;               // phi(K)^T arrays: fp32, or bf16 hi + lo
-    static constexpr int OQ = 0, OK = C * RQ, OKT = 2 * C * RQ, OKL = OKT + D * RT;
-    static constexpr int OVT = OKT + NKT * D * RT;
-    static constexpr int STAGE = OVT + DV * RT;           // elements per stage
+    static constexpr int CT = DV / 16;     // value-column tiles
+    static constexpr int TBN = C / 16;     // token tiles per chunk
+    static constexpr int BPW = TBN / NWAVE;  // query tiles per wave (1 or 2)
+    static constexpr int ZT = JT * CT / NWAVE;  // state tiles owned by each wave
+    static constexpr int SMAX = (JT + NWAVE - 1) / NWAVE;  // key-sum tiles per wave (at most)
+    static constexpr int VEC = Vec<F32>::N;  // values per 16-byte vector
+    static constexpr int PAD = pad_of(F32);
+    static constexpr int RK = D + PAD;     // row stride of phi(K) [token][dim] and Z^T [col][dim]
+    static constexpr int RV = DV + PAD;    // row stride of V [token][col]
+    static constexpr int NP = F32 ? 1 : 2; // copies of phi(K) and Z^T (hi, lo)
+    static constexpr int OK = 0, OKL = C * RK, OV = NP * C * RK;
+    static constexpr int OZ = OV + C * RV, OZL = OZ + DV * RK;
+    static constexpr int NE = OZ + NP * DV * RK;           // E elements before S
     static constexpr int LDS_BYTES = lds_bytes(F32, D, DV, C);
-    static_assert(JT % NW == 0, "key-sum tiles must split evenly over the waves");
-    static_assert(2 * STAGE * (int)sizeof(E) + 2 * D * 4 == LDS_BYTES, "LDS layout");
-    // 16-byte load items per chunk
-    static constexpr int IQ = C * (D / VEC);            // q rows
-    static constexpr int IK = (C / 2) * (D / VEC);      // k row pairs
-    static constexpr int IV = (C / 2) * (DV / VEC);     // v row pairs
-    static constexpr int NQ = (IQ + NT - 1) / NT;
-    static constexpr int NK = (IK + NT - 1) / NT;
-    static constexpr int NV = (IV + NT - 1) / NT;
+    static_assert(NE * (int)sizeof(E) + D * 4 == LDS_BYTES, "LDS layout");
+    static_assert(TBN % NWAVE == 0 && (BPW == 1 || BPW == 2), "chunk must be 64 or 128 tokens");
+    static_assert((JT * CT) % NWAVE == 0, "state tiles must split evenly over the waves");
+    // 16-byte load items per chunk (rows x vectors)
+    static constexpr int IK = C * (D / VEC);
+    static constexpr int IV = C * (DV / VEC);
+    static constexpr int NK = (IK + NTHR - 1) / NTHR;
+    static constexpr int NV = (IV + NTHR - 1) / NTHR;
+    // per-lane 16-byte vectors of one query row (dims: bf16 32u+8g..+7, fp32 16u+4g..+3)
+    static constexpr int NQV = F32 ? JT : JT / 2;
 };
 
-template <bool F32, class Frag>
-__device__ __forceinline__ Frag lds_frag(const void *p)
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// ---- MFMA operand fragments.
+// Contraction over the head dimension (scores, inter-chunk term): A and B are
+// read "naturally" -- bf16: 8 consecutive dims 32u + 8g .. +7 per lane; fp32:
+// 4 dims 16u + 4g .. +3.  Contraction over tokens (P V, state update): the
+// operand must hold 4 consecutive tokens of one column, which is how a 16x16
+// accumulator holds its rows; it is read from the row-major [token][col]
+// arrays with the gfx950 LDS transpose read (bf16) or four scalar reads (fp32).
+
+// bf16: 8 natural values at `p` (16-byte aligned).
+__device__ __forceinline__ bf16x8 nat8(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+__device__ __forceinline__ f32x4 nat4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+
+// bf16 transposed fragment: lane (n = lane % 16, g = lane / 16) receives rows
+// s0 + 4g .. s0 + 4g + 3 of column col0 + n of a row-major array (stride ld).
+// Each lane addresses row s0 + 4g + n/4, columns col0 + 4(n%4) .. +3; the
+// transpose read redistributes those 4-element pieces within every 16 lanes.
+__device__ __forceinline__ bf16x4 tr4(const bf16 *base, int ld, int s0, int col0, int n, int g)
 {
-    return *reinterpret_cast<const Frag *>(p);
+    const bf16 *p = base + (s0 + 4 * g + (n >> 2)) * ld + col0 + 4 * (n & 3);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(bf16 *)p);
+}
+// two tiles (s0 and s0 + 16) concatenated: the 8 values of one bf16 MFMA
+__device__ __forceinline__ bf16x8 tr8(const bf16 *base, int ld, int s0, int col0, int n, int g)
+{
+    const bf16x4 a = tr4(base, ld, s0, col0, n, g), b = tr4(base, ld, s0 + 16, col0, n, g);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// fp32 transposed fragment: rows s0 + 4g + i of column col0 + n.
+__device__ __forceinline__ f32x4 trf(const float *base, int ld, int s0, int col0, int n, int g)
+{
+    f32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = base[(s0 + 4 * g + i) * ld + col0 + n];
+    return v;
+}
+
+__device__ __forceinline__ f32x4 mma8(f32x4 c, bf16x8 a, bf16x8 b)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
-// Load the raw q (rows), k (row pairs) and v (row pairs) of one chunk into
-// registers.  Tokens at or beyond `nval` are not read.
-template <bool F32, int D, int DV, int C, bool WANT_Q, bool WANT_K, bool WANT_V>
-struct ChunkRegs {
-    typedef Geo<F32, D, DV, C> G_;
-    u32x4 q[WANT_Q ? G_::NQ : 1];
-    u32x4 k[WANT_K ? 2 * G_::NK : 1];
-    u32x4 v[WANT_V ? 2 * G_::NV : 1];
+// Query rows of one wave tile: lane (r, g) holds query token r of the tile and
+// the dims it supplies as an MFMA operand, so phi(q) never goes through LDS.
+template <bool F32, int D>
+struct QRegs {
+    static constexpr int NQV = F32 ? D / 16 : D / 32;
+    u32x4 raw[NQV];
 
-    __device__ __forceinline__ void load(int tid, const char *qh, const char *kh, const char *vh,
-                                         int64_t sqn, int64_t skn, int64_t svn, int t0, int nval, int col0)
+    __device__ __forceinline__ static int dim0(int u, int g) { return F32 ? 16 * u + 4 * g : 32 * u + 8 * g; }
+
+    __device__ __forceinline__ void load(const char *qh, int64_t sqn, int t, bool valid, int g)
+    {
+        constexpr int ES = F32 ? 4 : 2;
+#pragma unroll
+        for (int u = 0; u < NQV; ++u)
+            raw[u] = valid ? ld16(qh + ((int64_t)t * sqn + dim0(u, g)) * ES) : (u32x4){0u, 0u, 0u, 0u};
+    }
+};
+
+// Cooperative load of the k and v rows of one chunk into registers
+// (16-byte vectors, consecutive threads along a row), then phi and the LDS
+// stage.  Tokens at or beyond `nval` are not read and become exact zeros.
+template <bool F32, int D, int DV, int C>
+struct KVRegs {
+    typedef Geo<F32, D, DV, C> G_;
+    u32x4 k[G_::NK];
+    u32x4 v[G_::NV];
+
+    __device__ __forceinline__ void load(int tid, const char *kh, const char *vh, int64_t skn, int64_t svn,
+                                         int t0, int nval, int col0)
     {
         constexpr int ES = F32 ? 4 : 2;
         const u32x4 z = {0u, 0u, 0u, 0u};
-        if (WANT_Q) {
 #pragma unroll
-            for (int it = 0; it < G_::NQ; ++it) {
-                const int idx = tid + it * G_::NT;
-                const int row = idx / (D / G_::VEC), vg = idx % (D / G_::VEC);
-                q[it] = (idx < G_::IQ && row < nval)
-                            ? ld16(qh + ((int64_t)(t0 + row) * sqn + vg * G_::VEC) * ES) : z;
-            }
+        for (int it = 0; it < G_::NK; ++it) {
+            const int idx = tid + it * NTHR;
+            const int row = idx / (D / G_::VEC), vg = idx % (D / G_::VEC);
+            k[it] = (idx < G_::IK && row < nval) ? ld16(kh + ((int64_t)(t0 + row) * skn + vg * G_::VEC) * ES) : z;
         }
-        if (WANT_K) {
 #pragma unroll
-            for (int it = 0; it < G_::NK; ++it) {
-                const int idx = tid + it * G_::NT;
-                const int tp = idx / (D / G_::VEC), vg = idx % (D / G_::VEC);
-                const bool ok = idx < G_::IK;
-                k[2 * it] = (ok && 2 * tp < nval)
-                                ? ld16(kh + ((int64_t)(t0 + 2 * tp) * skn + vg * G_::VEC) * ES) : z;
-                k[2 * it + 1] = (ok && 2 * tp + 1 < nval)
-                                    ? ld16(kh + ((int64_t)(t0 + 2 * tp + 1) * skn + vg * G_::VEC) * ES) : z;
-            }
-        }
-        if (WANT_V) {
-#pragma unroll
-            for (int it = 0; it < G_::NV; ++it) {
-                const int idx = tid + it * G_::NT;
-                const int tp = idx / (DV / G_::VEC), vg = idx % (DV / G_::VEC);
-                const bool ok = idx < G_::IV;
-                v[2 * it] = (ok && 2 * tp < nval)
-                                ? ld16(vh + ((int64_t)(t0 + 2 * tp) * svn + col0 + vg * G_::VEC) * ES) : z;
-                v[2 * it + 1] = (ok && 2 * tp + 1 < nval)
-                                    ? ld16(vh + ((int64_t)(t0 + 2 * tp + 1) * svn + col0 + vg * G_::VEC) * ES) : z;
-            }
+        for (int it = 0; it < G_::NV; ++it) {
+            const int idx = tid + it * NTHR;
+            const int row = idx / (DV / G_::VEC), vg = idx % (DV / G_::VEC);
+            v[it] = (idx < G_::IV && row < nval) ? ld16(vh + ((int64_t)(t0 + row) * svn + col0 + vg * G_::VEC) * ES) : z;
         }
     }
 
-    // Apply phi and write one LDS stage.  Invalid tokens become exact zeros in
-    // phi(q), phi(k) and v, so they add nothing to any product.
-    //  - phi(Q), phi(K) row major: one rounding to the operand type (scores).
-    //  - phi(K)^T: for bf16 as hi + lo, so the state update sees phi(k) to
-    //    about 16 bits; for fp32 as is.
-    //  - V^T: the input values unchanged.
-    __device__ __forceinline__ void fill(int tid, typename G_::E *st, int nval, bool k_rowmajor) const
+    // phi(K): bf16 hi + lo (the state update sees phi(k) to ~16 bits; the
+    // scores use hi), or fp32.  V: the input values unchanged.
+    __device__ __forceinline__ void fill(int tid, typename G_::E *st, int nval) const
     {
         typedef typename G_::E E;
         constexpr int VEC = G_::VEC;
-        if (WANT_Q) {
 #pragma unroll
-            for (int it = 0; it < G_::NQ; ++it) {
-                const int idx = tid + it * G_::NT;
-                if (idx >= G_::IQ) continue;
-                const int row = idx / (D / VEC), vg = idx % (D / VEC);
-                float f[VEC];
-                Vec<F32>::to_float(q[it], f);
-                const bool ok = row < nval;
-                E *dst = st + G_::OQ + row * G_::RQ + vg * VEC;
-                if (F32) {
-                    f32x4 o;
+        for (int it = 0; it < G_::NK; ++it) {
+            const int idx = tid + it * NTHR;
+            if (idx >= G_::IK) continue;
+            const int row = idx / (D / VEC), vg = idx % (D / VEC);
+            float f[VEC];
+            Vec<F32>::to_float(k[it], f);
+            const bool ok = row < nval;
+            E *dst = st + G_::OK + row * G_::RK + vg * VEC;
+            if (F32) {
+                f32x4 o;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) o[e] = ok ? phi<F32>(f[e]) : 0.f;
-                    *reinterpret_cast<f32x4 *>(dst) = o;
-                } else {
-                    u32x4 o;
+                for (int e = 0; e < 4; ++e) o[e] = ok ? phi<F32>(f[e]) : 0.f;
+                *reinterpret_cast<f32x4 *>(dst) = o;
+            } else {
+                bf16x8 hi, lo;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        o[e] = ok ? pack_bf16(phi<F32>(f[2 * e]), phi<F32>(f[2 * e + 1])) : 0u;
-                    *reinterpret_cast<u32x4 *>(dst) = o;
+                for (int e = 0; e < 8; ++e) {
+                    const float x = ok ? phi<F32>(f[e]) : 0.f;
+                    hi[e] = (bf16)x;
+                    lo[e] = (bf16)(x - (float)hi[e]);
                 }
+                *reinterpret_cast<bf16x8 *>(dst) = hi;
+                *reinterpret_cast<bf16x8 *>(dst + (G_::OKL - G_::OK)) = lo;
             }
         }
-        if (WANT_K) {
 #pragma unroll
-            for (int it = 0; it < G_::NK; ++it) {
-                const int idx = tid + it * G_::NT;
-                if (idx >= G_::IK) continue;
-                const int tp = idx / (D / VEC), vg = idx % (D / VEC);
-                float a[VEC], b[VEC];
-                Vec<F32>::to_float(k[2 * it], a);
-                Vec<F32>::to_float(k[2 * it + 1], b);
-                const bool oka = 2 * tp < nval, okb = 2 * tp + 1 < nval;
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    a[e] = oka ? phi<F32>(a[e]) : 0.f;
-                    b[e] = okb ? phi<F32>(b[e]) : 0.f;
-                }
-                E *kt = st + G_::OKT + (vg * VEC) * G_::RT + 2 * tp;
-                if (F32) {
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) {
-                        f32x2 pr = {a[e], b[e]};
-                        *reinterpret_cast<f32x2 *>(kt + e * G_::RT) = pr;
-                    }
-                    if (k_rowmajor) {
-                        E *k0 = st + G_::OK + (2 * tp) * G_::RQ + vg * VEC;
-                        f32x4 ra = {a[0], a[1], a[2], a[3]}, rb = {b[0], b[1], b[2], b[3]};
-                        *reinterpret_cast<f32x4 *>(k0) = ra;
-                        *reinterpret_cast<f32x4 *>(k0 + G_::RQ) = rb;
-                    }
-                } else {
-                    bf16 ha[VEC], hb[VEC];
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) {
-                        ha[e] = (bf16)a[e];
-                        hb[e] = (bf16)b[e];
-                        bf16x2 hi = {ha[e], hb[e]};
-                        bf16x2 lo = {(bf16)(a[e] - (float)ha[e]), (bf16)(b[e] - (float)hb[e])};
-                        *reinterpret_cast<bf16x2 *>(kt + e * G_::RT) = hi;
-                        *reinterpret_cast<bf16x2 *>(kt + (G_::OKL - G_::OKT) + e * G_::RT) = lo;
-                    }
-                    if (k_rowmajor) {
-                        E *k0 = st + G_::OK + (2 * tp) * G_::RQ + vg * VEC;
-                        bf16x8 va = {ha[0], ha[1], ha[2], ha[3], ha[4], ha[5], ha[6], ha[7]};
-                        bf16x8 vb = {hb[0], hb[1], hb[2], hb[3], hb[4], hb[5], hb[6], hb[7]};
-                        *reinterpret_cast<bf16x8 *>(k0) = va;
-                        *reinterpret_cast<bf16x8 *>(k0 + G_::RQ) = vb;
-                    }
-                }
-            }
-        }
-        if (WANT_V) {
-#pragma unroll
-            for (int it = 0; it < G_::NV; ++it) {
-                const int idx = tid + it * G_::NT;
-                if (idx >= G_::IV) continue;
-                const int tp = idx / (DV / VEC), vg = idx % (DV / VEC);
-                E *vt = st + G_::OVT + (vg * VEC) * G_::RT + 2 * tp;
-                // rows beyond nval were loaded as zeros already
-                if (F32) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        f32x2 pr = {__uint_as_float(v[2 * it][e]), __uint_as_float(v[2 * it + 1][e])};
-                        *reinterpret_cast<f32x2 *>(vt + e * G_::RT) = pr;
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t wa = v[2 * it][e], wb = v[2 * it + 1][e];
-                        // element 2e: low halves; element 2e+1: high halves
-                        *reinterpret_cast<uint32_t *>(vt + (2 * e) * G_::RT) = (wa & 0xffffu) | (wb << 16);
-                        *reinterpret_cast<uint32_t *>(vt + (2 * e + 1) * G_::RT) = (wa >> 16) | (wb & 0xffff0000u);
-                    }
-                }
-            }
+        for (int it = 0; it < G_::NV; ++it) {
+            const int idx = tid + it * NTHR;
+            if (idx >= G_::IV) continue;
+            const int row = idx / (DV / VEC), vg = idx % (DV / VEC);
+            *reinterpret_cast<u32x4 *>(st + G_::OV + row * G_::RV + vg * VEC) = v[it];
         }
     }
 };
 
-// Z += phi(K_c)^T V_c for the wave's column tile (all key tiles), and
-// S += phi(K_c)^T 1 for the wave's own key-sum tiles (the all-ones B operand
-// leaves S_j in exactly the lanes that hold row j of a state tile).
+// Owned state tiles: wave w owns key-sum tiles jt = w + NWAVE*m and the state
+// tiles (jt, ct) of one value-column tile ct = w % CT, key tiles
+// jt = m * (NWAVE / CT) + w / CT (so a wave reuses one V fragment).
+template <int JT, int CT>
+__device__ __forceinline__ int own_ct(int w) { return w % CT; }
+template <int JT, int CT>
+__device__ __forceinline__ int own_jt(int w, int m) { return m * (NWAVE / CT) + w / CT; }
+
+// Z += phi(K_c)^T V_c on the owned tiles, S += phi(K_c)^T 1 on the owned
+// key-sum tiles (the all-ones operand leaves S_j in the lanes of row j).
 template <bool F32, int D, int DV, int C>
 __device__ __forceinline__ void state_update(const typename Geo<F32, D, DV, C>::E *st, int w, int r, int g,
-                                             f32x4 *Zacc, f32x4 *Sown)
+                                             f32x4 *Zown, f32x4 *Sown)
 {
     typedef Geo<F32, D, DV, C> G_;
-    typedef typename G_::E E;
-    const E *kt = st + G_::OKT;
-    const E *vt = st + G_::OVT + (16 * w + r) * G_::RT + 4 * g;
+    constexpr int JT = G_::JT, CT = G_::CT;
+    const int ct = own_ct<JT, CT>(w);
     if (F32) {
+        const float *k = reinterpret_cast<const float *>(st) + G_::OK;
+        const float *v = reinterpret_cast<const float *>(st) + G_::OV;
         const f32x4 ones = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-        for (int sa = 0; sa < G_::TB; ++sa) {
-            const f32x4 vb = lds_frag<F32, f32x4>(vt + 16 * sa);
+        for (int sa = 0; sa < G_::TBN; ++sa) {
+            const f32x4 vb = trf(v, G_::RV, 16 * sa, 16 * ct, r, g);
 #pragma unroll
-            for (int jt = 0; jt < G_::JT; ++jt) {
-                const f32x4 ka = lds_frag<F32, f32x4>(kt + (16 * jt + r) * G_::RT + 16 * sa + 4 * g);
-                Zacc[jt] = mma1(Zacc[jt], ka, vb);
-            }
+            for (int m = 0; m < G_::ZT; ++m)
+                Zown[m] = mma1(Zown[m], trf(k, G_::RK, 16 * sa, 16 * own_jt<JT, CT>(w, m), r, g), vb);
 #pragma unroll
-            for (int js = 0; js < G_::JS; ++js) {
-                const int jt = w * G_::JS + js;
-                const f32x4 ka = lds_frag<F32, f32x4>(kt + (16 * jt + r) * G_::RT + 16 * sa + 4 * g);
-                Sown[js] = mma1(Sown[js], ka, ones);
+            for (int m = 0; m < G_::SMAX; ++m) {
+                const int jt = w + NWAVE * m;
+                if (jt < JT) Sown[m] = mma1(Sown[m], trf(k, G_::RK, 16 * sa, 16 * jt, r, g), ones);
             }
         }
     } else {
-        const bf16 one = (bf16)1.f, zr = (bf16)0.f;
-        const bf16x4 ones = {one, one, one, one};
-        const bf16x4 zero = {zr, zr, zr, zr};
-        const E *kl = st + G_::OKL;
+        const bf16 *kh = reinterpret_cast<const bf16 *>(st) + G_::OK;
+        const bf16 *kl = reinterpret_cast<const bf16 *>(st) + G_::OKL;
+        const bf16 *v = reinterpret_cast<const bf16 *>(st) + G_::OV;
+        const bf16 one = (bf16)1.f;
+        const bf16x8 ones = {one, one, one, one, one, one, one, one};
 #pragma unroll
-        for (int sa = 0; sa < G_::TB; sa += 2) {
-            const bool two = sa + 1 < G_::TB;
-            const bf16x4 vb0 = lds_frag<F32, bf16x4>(vt + 16 * sa);
-            const bf16x4 vb1 = two ? lds_frag<F32, bf16x4>(vt + 16 * (sa + 1)) : zero;
+        for (int sa = 0; sa < G_::TBN; sa += 2) {
+            const bf16x8 vb = tr8(v, G_::RV, 16 * sa, 16 * ct, r, g);
 #pragma unroll
-            for (int jt = 0; jt < G_::JT; ++jt) {
-                const int o = (16 * jt + r) * G_::RT + 16 * sa + 4 * g;
-                const bf16x4 h0 = lds_frag<F32, bf16x4>(kt + o), l0 = lds_frag<F32, bf16x4>(kl + o);
-                const bf16x4 h1 = two ? lds_frag<F32, bf16x4>(kt + o + 16) : zero;
-                const bf16x4 l1 = two ? lds_frag<F32, bf16x4>(kl + o + 16) : zero;
-                Zacc[jt] = mma2(Zacc[jt], h0, h1, vb0, vb1);
-                Zacc[jt] = mma2(Zacc[jt], l0, l1, vb0, vb1);
+            for (int m = 0; m < G_::ZT; ++m) {
+                const int jt = own_jt<JT, CT>(w, m);
+                Zown[m] = mma8(Zown[m], tr8(kh, G_::RK, 16 * sa, 16 * jt, r, g), vb);
+                Zown[m] = mma8(Zown[m], tr8(kl, G_::RK, 16 * sa, 16 * jt, r, g), vb);
             }
 #pragma unroll
-            for (int js = 0; js < G_::JS; ++js) {
-                const int o = (16 * (w * G_::JS + js) + r) * G_::RT + 16 * sa + 4 * g;
-                const bf16x4 h0 = lds_frag<F32, bf16x4>(kt + o), l0 = lds_frag<F32, bf16x4>(kl + o);
-                const bf16x4 h1 = two ? lds_frag<F32, bf16x4>(kt + o + 16) : zero;
-                const bf16x4 l1 = two ? lds_frag<F32, bf16x4>(kl + o + 16) : zero;
-                Sown[js] = mma2(Sown[js], h0, h1, ones, ones);
-                Sown[js] = mma2(Sown[js], l0, l1, ones, ones);
+            for (int m = 0; m < G_::SMAX; ++m) {
+                const int jt = w + NWAVE * m;
+                if (jt < JT) {
+                    Sown[m] = mma8(Sown[m], tr8(kh, G_::RK, 16 * sa, 16 * jt, r, g), ones);
+                    Sown[m] = mma8(Sown[m], tr8(kl, G_::RK, 16 * sa, 16 * jt, r, g), ones);
+                }
             }
+        }
+    }
+}
+
+// Load / store the owned tiles of a state in the [D][width] layout (row
+// stride `ld`); S from / to `s` (lanes of row 0 of each lane group).
+template <int JT, int CT, int ZT, int SMAX>
+__device__ __forceinline__ void load_owned(const float *z, int64_t ld, const float *s, int w, int r, int g,
+                                           f32x4 *Zown, f32x4 *Sown)
+{
+    const int ct = own_ct<JT, CT>(w);
+#pragma unroll
+    for (int m = 0; m < ZT; ++m) {
+        const int jt = own_jt<JT, CT>(w, m);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            Zown[m][i] = z ? z[(int64_t)(16 * jt + 4 * g + i) * ld + 16 * ct + r] : 0.f;
+    }
+#pragma unroll
+    for (int m = 0; m < SMAX; ++m) {
+        const int jt = w + NWAVE * m;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Sown[m][i] = (s && jt < JT) ? s[16 * jt + 4 * g + i] : 0.f;
+    }
+}
+
+template <int JT, int CT, int ZT, int SMAX>
+__device__ __forceinline__ void store_owned(float *z, int64_t ld, float *s, int w, int r, int g,
+                                            const f32x4 *Zown, const f32x4 *Sown)
+{
+    const int ct = own_ct<JT, CT>(w);
+    if (z) {
+#pragma unroll
+        for (int m = 0; m < ZT; ++m) {
+            const int jt = own_jt<JT, CT>(w, m);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) z[(int64_t)(16 * jt + 4 * g + i) * ld + 16 * ct + r] = Zown[m][i];
+        }
+    }
+    if (s && r == 0) {
+#pragma unroll
+        for (int m = 0; m < SMAX; ++m) {
+            const int jt = w + NWAVE * m;
+            if (jt < JT) *reinterpret_cast<f32x4 *>(s + 16 * jt + 4 * g) = Sown[m];
+        }
+    }
+}
+
+// Publish the owned tiles to LDS: Z^T [col][dim] as MFMA A operands (hi + lo
+// for bf16) and S as fp32.
+template <bool F32, int D, int DV, int C>
+__device__ __forceinline__ void publish_state(typename Geo<F32, D, DV, C>::E *sm, float *sS, int w, int r, int g,
+                                              const f32x4 *Zown, const f32x4 *Sown)
+{
+    typedef Geo<F32, D, DV, C> G_;
+    constexpr int JT = G_::JT, CT = G_::CT;
+    const int ct = own_ct<JT, CT>(w);
+#pragma unroll
+    for (int m = 0; m < G_::ZT; ++m) {
+        const int o = (16 * ct + r) * G_::RK + 16 * own_jt<JT, CT>(w, m) + 4 * g;
+        if (F32) {
+            *reinterpret_cast<f32x4 *>(sm + G_::OZ + o) = Zown[m];
+        } else {
+            bf16x4 hi, lo;
+            split_hi_lo(Zown[m], hi, lo);
+            *reinterpret_cast<bf16x4 *>(sm + G_::OZ + o) = hi;
+            *reinterpret_cast<bf16x4 *>(sm + G_::OZL + o) = lo;
+        }
+    }
+    if (r == 0) {
+#pragma unroll
+        for (int m = 0; m < G_::SMAX; ++m) {
+            const int jt = w + NWAVE * m;
+            if (jt < JT) *reinterpret_cast<f32x4 *>(sS + 16 * jt + 4 * g) = Sown[m];
         }
     }
 }
 
 // ------------------------------------------------------------------ kernels
-// Partial state of one token group: Z_g = phi(K_g)^T V_g (the wave's column
-// tile), S_g = sum phi(k) (the wave's key-sum tiles).  Written to the group's
-// slot.
+// Partial state of one token group: A_g = phi(K_g)^T V_g (column block p),
+// S_g = sum phi(k).  Written to slot `slot0 + g`.
 template <bool F32, int D, int DV, int C>
-__global__ void __launch_bounds__(DV / 16 * WAVE) k_group_state(const Args a)
+__global__ void __launch_bounds__(NTHR) k_group_state(const Args a)
 {
     typedef Geo<F32, D, DV, C> G_;
     typedef typename G_::E E;
     __shared__ __attribute__((aligned(16))) char smem_raw[G_::LDS_BYTES];
-    E *smem = reinterpret_cast<E *>(smem_raw);
+    E *st = reinterpret_cast<E *>(smem_raw);
     const int tid = threadIdx.x, w = tid / WAVE, lane = tid % WAVE, r = lane % 16, g = lane / 16;
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
     const int p = wg % a.P, rest = wg / a.P, grp = rest % a.G, bh = rest / a.G;
@@ -470,250 +515,257 @@ __global__ void __launch_bounds__(DV / 16 * WAVE) k_group_state(const Args a)
     const char *kh = (const char *)a.k + (b * a.skb + h * a.skh) * ES;
     const char *vh = (const char *)a.v + (b * a.svb + h * a.svh) * ES;
 
-    f32x4 Zacc[G_::JT], Sown[G_::JS];
+    f32x4 Zown[G_::ZT], Sown[G_::SMAX];
 #pragma unroll
-    for (int jt = 0; jt < G_::JT; ++jt) Zacc[jt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < G_::ZT; ++m) Zown[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int js = 0; js < G_::JS; ++js) Sown[js] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < G_::SMAX; ++m) Sown[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    ChunkRegs<F32, D, DV, C, false, true, true> R;
+    KVRegs<F32, D, DV, C> R;
     const int nch = (t_end - t_begin + C - 1) / C;
-    R.load(tid, nullptr, kh, vh, 0, a.skn, a.svn, t_begin, min(C, t_end - t_begin), p * DV);
-    R.fill(tid, smem, min(C, t_end - t_begin), false);
+    R.load(tid, kh, vh, a.skn, a.svn, t_begin, min(C, t_end - t_begin), p * DV);
     for (int ch = 0; ch < nch; ++ch) {
-        __syncthreads();
         const int t0 = t_begin + ch * C;
-        const bool more = ch + 1 < nch;
-        const int nnext = more ? min(C, t_end - t0 - C) : 0;
-        if (more) R.load(tid, nullptr, kh, vh, 0, a.skn, a.svn, t0 + C, nnext, p * DV);
-        const E *st = smem + (ch & 1) * G_::STAGE;
-        state_update<F32, D, DV, C>(st, w, r, g, Zacc, Sown);
-        if (more) R.fill(tid, smem + ((ch + 1) & 1) * G_::STAGE, nnext, false);
+        R.fill(tid, st, min(C, t_end - t0));
+        __syncthreads();
+        if (ch + 1 < nch) R.load(tid, kh, vh, a.skn, a.svn, t0 + C, min(C, t_end - t0 - C), p * DV);
+        state_update<F32, D, DV, C>(st, w, r, g, Zown, Sown);
+        __syncthreads();
     }
-
     constexpr int SL = Slot<D, DV>::SIZE;
-    float *slot = a.part + ((int64_t)(bh * a.P + p) * a.Gs + grp) * SL;
-#pragma unroll
-    for (int jt = 0; jt < G_::JT; ++jt)
-        *reinterpret_cast<f32x4 *>(slot + (16 * w + r) * D + 16 * jt + 4 * g) = Zacc[jt];
-    if (r == 0) {
-#pragma unroll
-        for (int js = 0; js < G_::JS; ++js)
-            *reinterpret_cast<f32x4 *>(slot + Slot<D, DV>::Z + 16 * (w * G_::JS + js) + 4 * g) = Sown[js];
-    }
+    float *slot = a.part + ((int64_t)(bh * a.P + p) * a.NS + a.slot0 + grp) * SL;
+    store_owned<G_::JT, G_::CT, G_::ZT, G_::SMAX>(slot, DV, slot + Slot<D, DV>::Z, w, r, g, Zown, Sown);
 }
 
-// Sum of the group partials in group order (plus the carried-in state):
-//  * to_state = true : state-only causal call -> z_out, s_out ([j][c] layout).
-//  * to_state = false: non-causal call -> reduced slots `fin`.
-// Every element is read and written by the same thread, so z_out may be z_in.
+// Element-wise pass over the slots of each (head, column block), all in the
+// [D][DV] + [D] layout (coalesced), summing in slot order:
+//  mode 0 (scan):  slot 0 <- carried-in state (or 0); slot i <- slot i-1 + slot i
+//                  for i < nslots: the starting states of the token groups.
+//  mode 1 (total): z_out/s_out <- carried-in state + sum of the nslots slots.
+//  mode 2 (fin):   fin <- sum of the nslots slots.
+// Each element is read and written by one thread, so z_out may be z_in.
 template <int D, int DV>
-__global__ void __launch_bounds__(256) k_reduce(const Args a, int ngroups, bool to_state)
+__global__ void __launch_bounds__(256) k_slots(const Args a, int nslots, int mode)
 {
     constexpr int SL = Slot<D, DV>::SIZE, SZ = Slot<D, DV>::Z;
-    const int bh = blockIdx.x;
-    const int total = a.P * SL;
-    for (int e = threadIdx.x; e < total; e += blockDim.x) {
-        const int p = e / SL, kk = e % SL;
-        const bool is_s = kk >= SZ;
-        if (to_state && is_s && p != 0) continue;  // S is identical in every column block
-        int64_t sidx;
-        float acc;
-        if (!is_s) {
-            const int c = kk / D, j = kk % D;
-            sidx = (int64_t)bh * D * D + (int64_t)j * D + p * DV + c;
-            acc = (to_state && a.z_in) ? a.z_in[sidx] : 0.f;
-        } else {
-            sidx = (int64_t)bh * D + (kk - SZ);
-            acc = (to_state && a.s_in) ? a.s_in[sidx] : 0.f;
+    const int hp = blockIdx.y;  // head * P + p
+    const int bh = hp / a.P, p = hp % a.P;
+    const int kk = blockIdx.x * 256 + threadIdx.x;
+    if (kk >= SL) return;
+    const bool is_s = kk >= SZ;
+    if (is_s && p != 0 && mode == 1) return;  // S is identical in every column block
+    int64_t gidx;
+    if (!is_s) {
+        const int j = kk / DV, c = kk % DV;
+        gidx = (int64_t)bh * D * D + (int64_t)j * D + p * DV + c;
+    } else {
+        gidx = (int64_t)bh * D + (kk - SZ);
+    }
+    float *src = a.part + (int64_t)hp * a.NS * SL + kk;
+    float acc = 0.f;
+    if (mode != 2) {
+        const float *init = is_s ? a.s_in : a.z_in;
+        acc = init ? init[gidx] : 0.f;
+    }
+    if (mode == 0) {
+        // loads are batched ahead of the stores (which may alias them)
+        src[0] = acc;
+        for (int i0 = 1; i0 < nslots; i0 += 8) {
+            const int n = min(8, nslots - i0);
+            float vals[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) vals[u] = u < n ? src[(int64_t)(i0 + u) * SL] : 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (u < n) {
+                    acc += vals[u];
+                    src[(int64_t)(i0 + u) * SL] = acc;
+                }
+            }
         }
-        const float *src = a.part + (int64_t)(bh * a.P + p) * a.Gs * SL + kk;
-        for (int gi = 0; gi < ngroups; ++gi) acc += src[(int64_t)gi * SL];
-        if (to_state) {
-            if (!is_s) { if (a.z_out) a.z_out[sidx] = acc; }
-            else if (a.s_out) a.s_out[sidx] = acc;
-        } else {
-            a.fin[(int64_t)(bh * a.P + p) * SL + kk] = acc;
-        }
+        return;
+    }
+    float vals[8];
+    int i = 0;
+    for (; i + 8 <= nslots; i += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) vals[u] = src[(int64_t)(i + u) * SL];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += vals[u];
+    }
+    for (; i < nslots; ++i) acc += src[(int64_t)i * SL];
+    if (mode == 1) {
+        float *dst = is_s ? a.s_out : a.z_out;
+        if (dst) dst[gidx] = acc;
+    } else {
+        a.fin[(int64_t)hp * SL + kk] = acc;
     }
 }
 
 // Chunk-sequential forward of one token group (mode 3 inside the group).
+// Wave w owns query tile w (and 2*NWAVE-1-w for 128-token chunks):
 // CAUSAL: out_t = [phi(q_t) Z_prev + sum_{s<=t in chunk} P_ts v_s] /
 //                 [phi(q_t) . S_prev + sum_{s<=t in chunk} P_ts + eps],
-//         P = phi(Q_c) phi(K_c)^T, then Z += phi(K_c)^T V_c, S += phi(K_c)^T 1.
-//         The group starts from z_in/s_in plus the partials of all earlier
-//         groups (mode 4); the last group writes z_out/s_out.
+//         P = phi(Q_c) phi(K_c)^T; then Z += phi(K_c)^T V_c, S += phi(K_c)^T 1
+//         on the owned state tiles, published to LDS for the next chunk.  The
+//         group starts from its slot (or z_in/s_in when there is one group);
+//         the last group writes z_out/s_out.
 // !CAUSAL (non-causal apply): out_t = phi(q_t) Z / (phi(q_t) . S + eps) with
 //         the reduced global state.
 template <bool F32, int D, int DV, int C, bool CAUSAL>
-__global__ void __launch_bounds__(DV / 16 * WAVE) k_chunk_fwd(const Args a)
+__global__ void __launch_bounds__(NTHR) k_chunk_fwd(const Args a)
 {
     typedef Geo<F32, D, DV, C> G_;
     typedef typename G_::E E;
-    typedef typename G_::Frag Frag;
-    constexpr int JT = G_::JT, TB = G_::TB, JS = G_::JS;
+    constexpr int JT = G_::JT, CT = G_::CT, TBN = G_::TBN, BPW = G_::BPW, NQV = G_::NQV;
     constexpr int ES = F32 ? 4 : 2;
     constexpr int SL = Slot<D, DV>::SIZE;
     __shared__ __attribute__((aligned(16))) char smem_raw[G_::LDS_BYTES];
-    E *smem = reinterpret_cast<E *>(smem_raw);
-    float *sS = reinterpret_cast<float *>(smem_raw + 2 * G_::STAGE * sizeof(E));  // [2][D]
+    E *sm = reinterpret_cast<E *>(smem_raw);
+    float *sS = reinterpret_cast<float *>(smem_raw + G_::NE * sizeof(E));
 
     const int tid = threadIdx.x, w = tid / WAVE, lane = tid % WAVE, r = lane % 16, g = lane / 16;
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
     const int p = wg % a.P, rest = wg / a.P, grp = rest % a.G, bh = rest / a.G;
     const int b = bh / a.H, h = bh % a.H;
     const int t_begin = grp * a.L, t_end = min(t_begin + a.L, a.N);
-    const int col = p * DV + 16 * w + r;  // this lane's value column (state layout)
     const char *qh = (const char *)a.q + (b * a.sqb + h * a.sqh) * ES;
     const char *kh = (const char *)a.k + (b * a.skb + h * a.skh) * ES;
     const char *vh = (const char *)a.v + (b * a.svb + h * a.svh) * ES;
-    float *oh = a.out + b * a.sob + h * a.soh;
+    float *oh = a.out + b * a.sob + h * a.soh + p * DV;
+    int tbs[BPW];
+    tbs[0] = w;
+    if (BPW == 2) tbs[BPW - 1] = TBN - 1 - w;
 
-    // ---- starting state of this group: Z tile of this wave's columns, and
-    // this wave's share of S (published to LDS for every wave)
-    f32x4 Zacc[JT], Sown[JS];
+    // ---- starting state: owned tiles, published to LDS
+    f32x4 Zown[G_::ZT], Sown[G_::SMAX];
     if (CAUSAL) {
-#pragma unroll
-        for (int jt = 0; jt < JT; ++jt) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j = 16 * jt + 4 * g + i;
-                Zacc[jt][i] = a.z_in ? a.z_in[(int64_t)bh * D * D + (int64_t)j * D + col] : 0.f;
-            }
-        }
-#pragma unroll
-        for (int js = 0; js < JS; ++js) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j = 16 * (w * JS + js) + 4 * g + i;
-                Sown[js][i] = a.s_in ? a.s_in[(int64_t)bh * D + j] : 0.f;
-            }
-        }
-        const float *slots = a.part + (int64_t)(bh * a.P + p) * a.Gs * SL;
-        for (int gp = 0; gp < grp; ++gp) {
-            const float *sl = slots + (int64_t)gp * SL;
-#pragma unroll
-            for (int jt = 0; jt < JT; ++jt)
-                Zacc[jt] += *reinterpret_cast<const f32x4 *>(sl + (16 * w + r) * D + 16 * jt + 4 * g);
-#pragma unroll
-            for (int js = 0; js < JS; ++js)
-                Sown[js] += *reinterpret_cast<const f32x4 *>(sl + Slot<D, DV>::Z + 16 * (w * JS + js) + 4 * g);
+        if (a.NS > 0) {
+            const float *sl = a.part + ((int64_t)(bh * a.P + p) * a.NS + grp) * SL;
+            load_owned<JT, CT, G_::ZT, G_::SMAX>(sl, DV, sl + Slot<D, DV>::Z, w, r, g, Zown, Sown);
+        } else {
+            load_owned<JT, CT, G_::ZT, G_::SMAX>(a.z_in ? a.z_in + (int64_t)bh * D * D + p * DV : nullptr, D,
+                                                 a.s_in ? a.s_in + (int64_t)bh * D : nullptr, w, r, g, Zown, Sown);
         }
     } else {
         const float *sl = a.fin + (int64_t)(bh * a.P + p) * SL;
-#pragma unroll
-        for (int jt = 0; jt < JT; ++jt)
-            Zacc[jt] = *reinterpret_cast<const f32x4 *>(sl + (16 * w + r) * D + 16 * jt + 4 * g);
-#pragma unroll
-        for (int js = 0; js < JS; ++js)
-            Sown[js] = *reinterpret_cast<const f32x4 *>(sl + Slot<D, DV>::Z + 16 * (w * JS + js) + 4 * g);
+        load_owned<JT, CT, G_::ZT, G_::SMAX>(sl, DV, sl + Slot<D, DV>::Z, w, r, g, Zown, Sown);
     }
-    if (r == 0) {
-#pragma unroll
-        for (int js = 0; js < JS; ++js)
-            *reinterpret_cast<f32x4 *>(sS + 16 * (w * JS + js) + 4 * g) = Sown[js];
-    }
+    publish_state<F32, D, DV, C>(sm, sS, w, r, g, Zown, Sown);
 
-    ChunkRegs<F32, D, DV, C, true, CAUSAL, CAUSAL> R;
+    QRegs<F32, D> Q[BPW];
+    KVRegs<F32, D, DV, C> R;
     const int nch = (t_end - t_begin + C - 1) / C;
-    R.load(tid, qh, kh, vh, a.sqn, a.skn, a.svn, t_begin, min(C, t_end - t_begin), p * DV);
-    R.fill(tid, smem, min(C, t_end - t_begin), true);
+#pragma unroll
+    for (int bi = 0; bi < BPW; ++bi) {
+        const int tq = 16 * tbs[bi] + r;
+        Q[bi].load(qh, a.sqn, t_begin + tq, tq < t_end - t_begin, g);
+    }
+    if (CAUSAL) R.load(tid, kh, vh, a.skn, a.svn, t_begin, min(C, t_end - t_begin), p * DV);
+    else __syncthreads();
 
     for (int ch = 0; ch < nch; ++ch) {
-        __syncthreads();
         const int t0 = t_begin + ch * C;
         const int nval = min(C, t_end - t0);
         const bool more = ch + 1 < nch;
-        const int nnext = more ? min(C, t_end - t0 - C) : 0;
-        if (more) R.load(tid, qh, kh, vh, a.sqn, a.skn, a.svn, t0 + C, nnext, p * DV);
-        const E *st = smem + (ch & 1) * G_::STAGE;
-
-        // running key sum before this chunk, for the lane's key rows
-        f32x4 Sv[JT];
-#pragma unroll
-        for (int jt = 0; jt < JT; ++jt)
-            Sv[jt] = *reinterpret_cast<const f32x4 *>(sS + (ch & 1) * D + 16 * jt + 4 * g);
-
-        // state as the A operand of phi(Q) Z: hi (+ lo for bf16)
-        Frag zh[JT], zl[JT];
-#pragma unroll
-        for (int jt = 0; jt < JT; ++jt) {
-            if (F32) {
-                zh[jt] = *reinterpret_cast<const Frag *>(&Zacc[jt]);
-            } else {
-                bf16x4 hi, lo;
-                split_hi_lo(Zacc[jt], hi, lo);
-                zh[jt] = *reinterpret_cast<const Frag *>(&hi);
-                zl[jt] = *reinterpret_cast<const Frag *>(&lo);
-            }
+        if (CAUSAL) {
+            R.fill(tid, sm, nval);
+            __syncthreads();   // stage, Z and S of this chunk visible
+            if (more) R.load(tid, kh, vh, a.skn, a.svn, t0 + C, min(C, t_end - t0 - C), p * DV);
         }
 
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
-            // phi(q) fragments of query token 16*tb + r, dims 16*jt + 4g..+3
-            Frag qf[JT];
+        for (int bi = 0; bi < BPW; ++bi) {
+            const int tb = tbs[bi];
+            const int tq = 16 * tb + r;
+            const bool valid = tq < nval;
+            // phi(q) in fp32 (normaliser against S), then the MFMA operands
+            float fq[NQV][Vec<F32>::N];
             float dp = 0.f;
 #pragma unroll
-            for (int jt = 0; jt < JT; ++jt) {
-                qf[jt] = lds_frag<F32, Frag>(st + G_::OQ + (16 * tb + r) * G_::RQ + 16 * jt + 4 * g);
-                f32x4 qv;
-                if (F32) qv = *reinterpret_cast<const f32x4 *>(&qf[jt]);
-                else qv = to_f32x4(*reinterpret_cast<const bf16x4 *>(&qf[jt]));
+            for (int u = 0; u < NQV; ++u) {
+                Vec<F32>::to_float(Q[bi].raw[u], fq[u]);
+                const int d0 = QRegs<F32, D>::dim0(u, g);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dp += qv[i] * Sv[jt][i];
-            }
-            f32x4 o = {0.f, 0.f, 0.f, 0.f};
-            // inter-chunk term: O^T += Z^T phi(Q)^T
-            if (F32) {
-#pragma unroll
-                for (int jt = 0; jt < JT; ++jt)
-                    o = mma1(o, *reinterpret_cast<const f32x4 *>(&zh[jt]), *reinterpret_cast<const f32x4 *>(&qf[jt]));
-            } else {
-#pragma unroll
-                for (int jt = 0; jt < JT; jt += 2) {
-                    const bf16x4 *zh4 = reinterpret_cast<const bf16x4 *>(zh);
-                    const bf16x4 *zl4 = reinterpret_cast<const bf16x4 *>(zl);
-                    const bf16x4 *q4 = reinterpret_cast<const bf16x4 *>(qf);
-                    o = mma2(o, zh4[jt], zh4[jt + 1], q4[jt], q4[jt + 1]);
-                    o = mma2(o, zl4[jt], zl4[jt + 1], q4[jt], q4[jt + 1]);
+                for (int e = 0; e < Vec<F32>::N; ++e) {
+                    fq[u][e] = valid ? phi<F32>(fq[u][e]) : 0.f;
+                    dp += fq[u][e] * sS[d0 + e];
                 }
             }
-            float rs = 0.f;
-            if (CAUSAL) {
-                // intra-chunk term over key tiles sa <= tb
-                const E *vrow = st + G_::OVT + (16 * w + r) * G_::RT + 4 * g;
-                if (F32) {
+            if (more) {
+                const int tn = t0 + C + tq;
+                Q[bi].load(qh, a.sqn, tn, tn < t_end, g);
+            }
+            f32x4 o[CT];
 #pragma unroll
+            for (int ct = 0; ct < CT; ++ct) o[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            float rs = 0.f;
+            if (F32) {
+                const float *kf = reinterpret_cast<const float *>(sm) + G_::OK;
+                const float *vf = reinterpret_cast<const float *>(sm) + G_::OV;
+                const float *zf = reinterpret_cast<const float *>(sm) + G_::OZ;
+                f32x4 qf[NQV];
+#pragma unroll
+                for (int u = 0; u < NQV; ++u) qf[u] = (f32x4){fq[u][0], fq[u][1], fq[u][2], fq[u][3]};
+                // inter-chunk term: O^T += Z^T phi(Q)^T
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int u = 0; u < NQV; ++u)
+                        o[ct] = mma1(o[ct], nat4(zf + (16 * ct + r) * G_::RK + 16 * u + 4 * g), qf[u]);
+                if (CAUSAL) {
                     for (int sa = 0; sa <= tb; ++sa) {
                         f32x4 pt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int jt = 0; jt < JT; ++jt) {
-                            const f32x4 kf = lds_frag<F32, f32x4>(st + G_::OK + (16 * sa + r) * G_::RQ + 16 * jt + 4 * g);
-                            pt = mma1(pt, kf, *reinterpret_cast<const f32x4 *>(&qf[jt]));
-                        }
+                        for (int u = 0; u < NQV; ++u)
+                            pt = mma1(pt, nat4(kf + (16 * sa + r) * G_::RK + 16 * u + 4 * g), qf[u]);
                         if (sa == tb) {
 #pragma unroll
                             for (int i = 0; i < 4; ++i) if (4 * g + i > r) pt[i] = 0.f;
                         }
                         rs += (pt[0] + pt[1]) + (pt[2] + pt[3]);
-                        o = mma1(o, lds_frag<F32, f32x4>(vrow + 16 * sa), pt);
-                    }
-                } else {
-                    const bf16x4 zero = {(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
-                    const bf16x4 *q4 = reinterpret_cast<const bf16x4 *>(qf);
 #pragma unroll
+                        for (int ct = 0; ct < CT; ++ct)
+                            o[ct] = mma1(o[ct], trf(vf, G_::RV, 16 * sa, 16 * ct, r, g), pt);
+                    }
+                }
+            } else {
+                const bf16 *kb = reinterpret_cast<const bf16 *>(sm) + G_::OK;
+                const bf16 *vb = reinterpret_cast<const bf16 *>(sm) + G_::OV;
+                const bf16 *zh = reinterpret_cast<const bf16 *>(sm) + G_::OZ;
+                const bf16 *zl = reinterpret_cast<const bf16 *>(sm) + G_::OZL;
+                bf16x8 qh8[NQV], ql8[NQV];
+#pragma unroll
+                for (int u = 0; u < NQV; ++u) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        qh8[u][e] = (bf16)fq[u][e];
+                        ql8[u][e] = (bf16)(fq[u][e] - (float)qh8[u][e]);
+                    }
+                }
+                // inter-chunk term: O^T += Z^T phi(Q)^T with Z and phi(q) as hi + lo
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const int zo = (16 * ct + r) * G_::RK + 8 * g;
+#pragma unroll
+                    for (int u = 0; u < NQV; ++u) {
+                        const bf16x8 a_hi = nat8(zh + zo + 32 * u), a_lo = nat8(zl + zo + 32 * u);
+                        o[ct] = mma8(o[ct], a_hi, qh8[u]);
+                        o[ct] = mma8(o[ct], a_lo, qh8[u]);
+                        o[ct] = mma8(o[ct], a_hi, ql8[u]);
+                    }
+                }
+                if (CAUSAL) {
+                    // intra-chunk term over key tiles sa <= tb: scores P^T (rows =
+                    // keys, columns = queries) feed P V as the B operand directly
+                    const bf16 zr = (bf16)0.f;
                     for (int sa = 0; sa <= tb; sa += 2) {
                         const bool two = sa + 1 <= tb;
                         f32x4 pt0 = {0.f, 0.f, 0.f, 0.f}, pt1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int jt = 0; jt < JT; jt += 2) {
-                            const E *k0 = st + G_::OK + (16 * sa + r) * G_::RQ + 16 * jt + 4 * g;
-                            pt0 = mma2(pt0, lds_frag<F32, bf16x4>(k0), lds_frag<F32, bf16x4>(k0 + 16), q4[jt], q4[jt + 1]);
-                            if (two) {
-                                const E *k1 = k0 + 16 * G_::RQ;
-                                pt1 = mma2(pt1, lds_frag<F32, bf16x4>(k1), lds_frag<F32, bf16x4>(k1 + 16), q4[jt], q4[jt + 1]);
-                            }
+                        for (int u = 0; u < NQV; ++u) {
+                            pt0 = mma8(pt0, nat8(kb + (16 * sa + r) * G_::RK + 32 * u + 8 * g), qh8[u]);
+                            if (two) pt1 = mma8(pt1, nat8(kb + (16 * sa + 16 + r) * G_::RK + 32 * u + 8 * g), qh8[u]);
                         }
                         // causal mask inside the diagonal tile: key 4g+i > query r
                         if (sa == tb) {
@@ -726,54 +778,43 @@ __global__ void __launch_bounds__(DV / 16 * WAVE) k_chunk_fwd(const Args a)
                         }
                         rs += (pt0[0] + pt0[1]) + (pt0[2] + pt0[3]);
                         if (two) rs += (pt1[0] + pt1[1]) + (pt1[2] + pt1[3]);
-                        bf16x4 ph0, pl0, ph1 = zero, pl1 = zero;
+                        bf16x4 ph0, pl0, ph1 = {zr, zr, zr, zr}, pl1 = {zr, zr, zr, zr};
                         split_hi_lo(pt0, ph0, pl0);
                         if (two) split_hi_lo(pt1, ph1, pl1);
-                        const bf16x4 va0 = lds_frag<F32, bf16x4>(vrow + 16 * sa);
-                        const bf16x4 va1 = two ? lds_frag<F32, bf16x4>(vrow + 16 * (sa + 1)) : zero;
-                        o = mma2(o, va0, va1, ph0, ph1);
-                        o = mma2(o, va0, va1, pl0, pl1);
+                        const bf16x8 bh8 = __builtin_shufflevector(ph0, ph1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        const bf16x8 bl8 = __builtin_shufflevector(pl0, pl1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                        for (int ct = 0; ct < CT; ++ct) {
+                            bf16x4 va0 = tr4(vb, G_::RV, 16 * sa, 16 * ct, r, g);
+                            bf16x4 va1 = {zr, zr, zr, zr};
+                            if (two) va1 = tr4(vb, G_::RV, 16 * sa + 16, 16 * ct, r, g);
+                            const bf16x8 a8 = __builtin_shufflevector(va0, va1, 0, 1, 2, 3, 4, 5, 6, 7);
+                            o[ct] = mma8(o[ct], a8, bh8);
+                            o[ct] = mma8(o[ct], a8, bl8);
+                        }
                     }
                 }
             }
             const float den = reduce_lane_groups(dp + rs) + a.eps;
-            const int tq = 16 * tb + r;
-            if (tq < nval) {
+            if (valid) {
                 const float inv = 1.f / den;
-                f32x4 res = o * inv;
-                *reinterpret_cast<f32x4 *>(oh + (int64_t)(t0 + tq) * a.son + p * DV + 16 * w + 4 * g) = res;
+                float *orow = oh + (int64_t)(t0 + tq) * a.son + 4 * g;
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) *reinterpret_cast<f32x4 *>(orow + 16 * ct) = o[ct] * inv;
             }
         }
 
         if (CAUSAL) {
-            state_update<F32, D, DV, C>(st, w, r, g, Zacc, Sown);
-            if (r == 0) {
-#pragma unroll
-                for (int js = 0; js < JS; ++js)
-                    *reinterpret_cast<f32x4 *>(sS + ((ch + 1) & 1) * D + 16 * (w * JS + js) + 4 * g) = Sown[js];
-            }
-        } else if (r == 0) {
-#pragma unroll
-            for (int js = 0; js < JS; ++js)
-                *reinterpret_cast<f32x4 *>(sS + ((ch + 1) & 1) * D + 16 * (w * JS + js) + 4 * g) = Sown[js];
+            state_update<F32, D, DV, C>(sm, w, r, g, Zown, Sown);
+            __syncthreads();   // every wave is done with this chunk's stage, Z and S
+            publish_state<F32, D, DV, C>(sm, sS, w, r, g, Zown, Sown);
         }
-        if (more) R.fill(tid, smem + ((ch + 1) & 1) * G_::STAGE, nnext, true);
     }
 
-    if (CAUSAL && grp == a.G - 1) {
-        if (a.z_out) {
-#pragma unroll
-            for (int jt = 0; jt < JT; ++jt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    a.z_out[(int64_t)bh * D * D + (int64_t)(16 * jt + 4 * g + i) * D + col] = Zacc[jt][i];
-        }
-        if (a.s_out && p == 0 && r == 0) {
-#pragma unroll
-            for (int js = 0; js < JS; ++js)
-                *reinterpret_cast<f32x4 *>(a.s_out + (int64_t)bh * D + 16 * (w * JS + js) + 4 * g) = Sown[js];
-        }
-    }
+    if (CAUSAL && grp == a.G - 1)
+        store_owned<JT, CT, G_::ZT, G_::SMAX>(a.z_out ? a.z_out + (int64_t)bh * D * D + p * DV : nullptr, D,
+                                              (a.s_out && p == 0) ? a.s_out + (int64_t)bh * D : nullptr,
+                                              w, r, g, Zown, Sown);
 }
 
 // One recurrent step for every head: Z += phi(k) v^T, S += phi(k),
@@ -860,32 +901,37 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb)
     return pa < pb + nb && pb < pa + na;
 }
 
-// Columns per workgroup: one 16-wide tile per wave, at most 4 waves.
+// Columns per workgroup: at most 64 (two column blocks per head at d = 128).
 inline int cols_per_wg(int d) { return d < 64 ? d : 64; }
 
 template <bool F32, int D, int DV, int C>
 constexpr bool fits() { return lds_bytes(F32, D, DV, C) <= LDS_LIMIT; }
 
-// Largest supported chunk <= requested whose LDS fits one workgroup.
+// Chunk of 64 or 128 tokens (requests below 64 run as 64; fp32 inputs use 64),
+// the largest <= the request whose LDS fits one workgroup.
 int pick_chunk(bool f32, int d, int chunk)
 {
-    if (chunk == 0) chunk = f32 ? 32 : 64;
-    const int cands[4] = {128, 64, 32, 16};
-    for (int c : cands)
-        if (c <= chunk && lds_bytes(f32, d, cols_per_wg(d), c) <= LDS_LIMIT) return c;
-    return 16;
+    if (chunk == 0 || chunk < 64 || f32) chunk = 64;   // fp32: 64 (register budget)
+    if (chunk >= 128 && lds_bytes(f32, d, cols_per_wg(d), 128) <= LDS_LIMIT) return 128;
+    return 64;
 }
 
 struct Plan {
-    int C, DV, P, G, L, Gs;
+    int C, DV, P, G, L, NS;
     size_t slot_floats;
-    size_t part_off, part_bytes, fin_off, fin_bytes, copy_off, copy_bytes, total;
+    size_t part_bytes, fin_off, fin_bytes, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Token groups: enough workgroups to cover the chip (about one per CU), each
-// group a whole number of chunks, at most 32 groups per head.
+// Token groups: enough workgroups to cover the chip, each group a whole
+// number of chunks, at most LA_MAX_GROUPS groups per head.
+#ifndef LA_MAX_GROUPS
+#define LA_MAX_GROUPS 32
+#endif
+#ifndef LA_CAUSAL_TARGET_WGS
+#define LA_CAUSAL_TARGET_WGS 512
+#endif
 int pick_groups(int64_t units, int N, int C, int target)
 {
     if (N <= 0) return 1;
@@ -893,99 +939,76 @@ int pick_groups(int64_t units, int N, int C, int target)
     int64_t g = (target + units - 1) / units;
     if (g < 1) g = 1;
     if (g > maxg) g = maxg;
-    if (g > 32) g = 32;
+    if (g > LA_MAX_GROUPS) g = LA_MAX_GROUPS;
     return (int)g;
 }
 
-Plan plan_causal(int B, int H, int N, int d, la_dtype dt, int chunk, int flags, bool want_out)
+void set_groups(Plan &pl, int N)
 {
-    Plan pl;
-    const bool f32 = dt == LA_F32;
-    pl.C = pick_chunk(f32, d, chunk);
-    pl.DV = cols_per_wg(d);
-    pl.P = d / pl.DV;
-    const int64_t BH = (int64_t)B * H;
-    pl.G = pick_groups(BH * pl.P, N, pl.C, want_out ? 256 : 512);
     int64_t per = (N + pl.G - 1) / pl.G;
     pl.L = (int)(((per + pl.C - 1) / pl.C) * pl.C);
     if (pl.L < pl.C) pl.L = pl.C;
     pl.G = N > 0 ? (int)((N + pl.L - 1) / pl.L) : 1;
-    pl.Gs = want_out ? pl.G - 1 : pl.G;
+}
+
+// want_out: the output is computed (else state only).  inplace: z_out/s_out
+// equal z_in/s_in.
+Plan plan_causal(int B, int H, int N, int d, la_dtype dt, int chunk, bool inplace, bool want_out)
+{
+    Plan pl;
+    pl.C = pick_chunk(dt == LA_F32, d, chunk);
+    pl.DV = cols_per_wg(d);
+    pl.P = d / pl.DV;
+    const int64_t BH = (int64_t)B * H;
+    pl.G = pick_groups(BH * pl.P, N, pl.C, want_out ? LA_CAUSAL_TARGET_WGS : 2 * LA_CAUSAL_TARGET_WGS);
+    set_groups(pl, N);
+    if (N == 0) pl.NS = 0;
+    else if (!want_out) pl.NS = pl.G;
+    else pl.NS = (pl.G > 1 || (inplace && pl.P > 1)) ? pl.G : 0;
     pl.slot_floats = (size_t)pl.DV * d + d;
-    pl.part_off = 0;
-    pl.part_bytes = align256((size_t)BH * pl.P * pl.Gs * pl.slot_floats * 4);
-    pl.fin_off = pl.part_off + pl.part_bytes;
+    pl.part_bytes = align256((size_t)BH * pl.P * pl.NS * pl.slot_floats * 4);
+    pl.fin_off = pl.part_bytes;
     pl.fin_bytes = 0;
-    pl.copy_off = pl.fin_off;
-    pl.copy_bytes = (want_out && (flags & LA_WS_INPLACE_STATE)) ? align256((size_t)BH * ((size_t)d * d + d) * 4) : 0;
-    pl.total = pl.copy_off + pl.copy_bytes;
-    if (N == 0) pl.total = pl.copy_bytes, pl.part_bytes = 0, pl.copy_off = 0, pl.Gs = 0;
+    pl.total = pl.part_bytes;
     return pl;
 }
 
 Plan plan_noncausal(int B, int H, int N, int d, la_dtype dt)
 {
     Plan pl;
-    const bool f32 = dt == LA_F32;
-    pl.C = pick_chunk(f32, d, 0);
+    pl.C = pick_chunk(dt == LA_F32, d, 0);
     pl.DV = cols_per_wg(d);
     pl.P = d / pl.DV;
     const int64_t BH = (int64_t)B * H;
-    pl.G = pick_groups(BH * pl.P, N, pl.C, 512);
-    int64_t per = (N + pl.G - 1) / pl.G;
-    pl.L = (int)(((per + pl.C - 1) / pl.C) * pl.C);
-    if (pl.L < pl.C) pl.L = pl.C;
-    pl.G = N > 0 ? (int)((N + pl.L - 1) / pl.L) : 1;
-    pl.Gs = pl.G;
+    pl.G = pick_groups(BH * pl.P, N, pl.C, 1024);
+    set_groups(pl, N);
+    pl.NS = pl.G;
     pl.slot_floats = (size_t)pl.DV * d + d;
-    pl.part_off = 0;
-    pl.part_bytes = align256((size_t)BH * pl.P * pl.Gs * pl.slot_floats * 4);
+    pl.part_bytes = align256((size_t)BH * pl.P * pl.NS * pl.slot_floats * 4);
     pl.fin_off = pl.part_bytes;
     pl.fin_bytes = align256((size_t)BH * pl.P * pl.slot_floats * 4);
-    pl.copy_off = pl.fin_off + pl.fin_bytes;
-    pl.copy_bytes = 0;
-    pl.total = pl.copy_off;
-    if (N == 0) pl.total = 0;
+    pl.total = N > 0 ? pl.fin_off + pl.fin_bytes : 0;
     return pl;
 }
 
 // ---- kernel dispatch tables (dtype x d x chunk)
-typedef void (*KFn)(Args);
-
 template <bool F32, int D, int C>
-void launch_group_state(const Args &a, int nwg, hipStream_t st)
+void launch_dc(int what, const Args &a, int nwg, hipStream_t st)
 {
     constexpr int DV = D < 64 ? D : 64;
-    if constexpr (fits<F32, D, DV, C>())
-        hipLaunchKernelGGL((k_group_state<F32, D, DV, C>), dim3(nwg), dim3(Geo<F32, D, DV, C>::NT), 0, st, a);
-}
-
-template <bool F32, int D, int C, bool CAUSAL>
-void launch_chunk(const Args &a, int nwg, hipStream_t st)
-{
-    constexpr int DV = D < 64 ? D : 64;
-    if constexpr (fits<F32, D, DV, C>())
-        hipLaunchKernelGGL((k_chunk_fwd<F32, D, DV, C, CAUSAL>), dim3(nwg), dim3(Geo<F32, D, DV, C>::NT), 0, st, a);
+    if constexpr (fits<F32, D, DV, C>()) {
+        if (what == 0) hipLaunchKernelGGL((k_group_state<F32, D, DV, C>), dim3(nwg), dim3(NTHR), 0, st, a);
+        else if (what == 1) hipLaunchKernelGGL((k_chunk_fwd<F32, D, DV, C, true>), dim3(nwg), dim3(NTHR), 0, st, a);
+        else hipLaunchKernelGGL((k_chunk_fwd<F32, D, DV, C, false>), dim3(nwg), dim3(NTHR), 0, st, a);
+    }
 }
 
 template <bool F32, int D>
 void dispatch_c(int C, int what, const Args &a, int nwg, hipStream_t st)
 {
     // what: 0 = group state, 1 = causal chunk, 2 = non-causal apply
-#define LA_CASE(CC)                                                          \
-    case CC:                                                                 \
-        if (what == 0) launch_group_state<F32, D, CC>(a, nwg, st);           \
-        else if (what == 1) launch_chunk<F32, D, CC, true>(a, nwg, st);      \
-        else launch_chunk<F32, D, CC, false>(a, nwg, st);                    \
-        break;
-    switch (C) {
-        LA_CASE(16)
-        LA_CASE(32)
-        LA_CASE(64)
-        LA_CASE(128)
-    default: break;
-    }
-#undef LA_CASE
+    if (C == 128) launch_dc<F32, D, 128>(what, a, nwg, st);
+    else launch_dc<F32, D, 64>(what, a, nwg, st);
 }
 
 void dispatch(bool f32, int d, int C, int what, const Args &a, int nwg, hipStream_t st)
@@ -1001,11 +1024,15 @@ void dispatch(bool f32, int d, int C, int what, const Args &a, int nwg, hipStrea
     }
 }
 
-void launch_reduce(int d, const Args &a, int BH, int ngroups, bool to_state, hipStream_t st)
+// mode: 0 = scan into group starting states, 1 = total into z_out/s_out,
+// 2 = total into fin.
+void launch_slots(int d, const Args &a, int64_t BH, int P, int nslots, int mode, hipStream_t st)
 {
-    if (d == 32) hipLaunchKernelGGL((k_reduce<32, 32>), dim3(BH), dim3(256), 0, st, a, ngroups, to_state);
-    else if (d == 64) hipLaunchKernelGGL((k_reduce<64, 64>), dim3(BH), dim3(256), 0, st, a, ngroups, to_state);
-    else hipLaunchKernelGGL((k_reduce<128, 64>), dim3(BH), dim3(256), 0, st, a, ngroups, to_state);
+    const int sl = cols_per_wg(d) * d + d;
+    dim3 grid((sl + 255) / 256, (unsigned)(BH * P));
+    if (d == 32) hipLaunchKernelGGL((k_slots<32, 32>), grid, dim3(256), 0, st, a, nslots, mode);
+    else if (d == 64) hipLaunchKernelGGL((k_slots<64, 64>), grid, dim3(256), 0, st, a, nslots, mode);
+    else hipLaunchKernelGGL((k_slots<128, 64>), grid, dim3(256), 0, st, a, nslots, mode);
 }
 
 la_status check_common(int B, int H, int N, int d, la_dtype dt, float eps)
@@ -1071,8 +1098,9 @@ size_t la_causal_fwd_workspace(int B, int H, int N, int d, la_dtype dt, int chun
     if (check_common(B, H, N, d, dt, 0.f) != LA_OK) return 0;
     if (chunk != 0 && chunk != 16 && chunk != 32 && chunk != 64 && chunk != 128) return 0;
     // the larger of the with-output and state-only plans
-    Plan a = plan_causal(B, H, N, d, dt, chunk, flags, true);
-    Plan b = plan_causal(B, H, N, d, dt, chunk, flags, false);
+    const bool inplace = (flags & LA_WS_INPLACE_STATE) != 0;
+    Plan a = plan_causal(B, H, N, d, dt, chunk, inplace, true);
+    Plan b = plan_causal(B, H, N, d, dt, chunk, inplace, false);
     return a.total > b.total ? a.total : b.total;
 }
 
@@ -1105,49 +1133,37 @@ la_status la_causal_fwd(const void *q, la_strides sq, const void *k, la_strides 
     if (s_out && s_in && s_out != (float *)s_in && overlaps(s_out, sb, s_in, sb)) return LA_ERR_ALIAS;
     if (overlaps(z_out, zb, s_in, sb) || overlaps(s_out, sb, z_in, zb) || overlaps(z_out, zb, s_out, sb))
         return LA_ERR_ALIAS;
-    const bool z_inplace = z_out && z_out == z_in, s_inplace = s_out && s_out == s_in;
-    const int flags = (z_inplace || s_inplace) ? LA_WS_INPLACE_STATE : 0;
-    Plan pl = plan_causal(B, H, N, d, dt, chunk, flags, want_out);
+    const bool inplace = (z_out && z_out == z_in) || (s_out && s_out == s_in);
+    Plan pl = plan_causal(B, H, N, d, dt, chunk, inplace, want_out);
     if (ws_bytes < pl.total || (pl.total > 0 && !workspace)) return LA_ERR_WORKSPACE;
     if (BH == 0) return LA_OK;
 
     hipStream_t stream = (hipStream_t)hip_stream;
     (void)hipGetLastError();
-    char *ws = (char *)workspace;
     Args a = make_args(q, sq, k, sk, v, sv, out, so, B, H, N, eps);
     a.z_in = z_in; a.s_in = s_in; a.z_out = z_out; a.s_out = s_out;
-    a.P = pl.P; a.L = pl.L; a.Gs = pl.Gs;
-    a.part = (float *)(ws + pl.part_off);
+    a.P = pl.P; a.L = pl.L; a.NS = pl.NS;
+    a.part = (float *)workspace;
     const bool f32 = dt == LA_F32;
 
     if (N == 0 || !want_out) {
-        // state only: group partials over all groups, then the ordered sum
-        // with the carried-in state (same thread reads and writes each element)
+        // state only: group partials, then carried-in state + their sum
         if (N > 0) {
-            a.G = pl.G;
+            a.G = pl.G; a.slot0 = 0;
             dispatch(f32, d, pl.C, 0, a, (int)(BH * pl.P * pl.G), stream);
         }
-        launch_reduce(d, a, (int)BH, N > 0 ? pl.G : 0, true, stream);
+        launch_slots(d, a, BH, pl.P, N > 0 ? pl.G : 0, 1, stream);
         return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
     }
-
-    // in-place state with more than one reader of the input state: read it
-    // from a copy in the workspace
-    if ((z_inplace || s_inplace) && (pl.G > 1 || pl.P > 1)) {
-        float *cz = (float *)(ws + pl.copy_off);
-        float *cs = cz + (size_t)BH * d * d;
-        if (z_inplace) {
-            if (hipMemcpyAsync(cz, z_in, zb, hipMemcpyDeviceToDevice, stream) != hipSuccess) return LA_ERR_LAUNCH;
-            a.z_in = cz;
+    if (pl.NS > 0) {
+        // group partials (groups 0..G-2 into slots 1..G-1), then the scan that
+        // turns the slots into the starting state of every group; the chunk
+        // kernel never reads z_in/s_in, so in-place state is safe
+        if (pl.G > 1) {
+            a.G = pl.G - 1; a.slot0 = 1;
+            dispatch(f32, d, pl.C, 0, a, (int)(BH * pl.P * (pl.G - 1)), stream);
         }
-        if (s_inplace) {
-            if (hipMemcpyAsync(cs, s_in, sb, hipMemcpyDeviceToDevice, stream) != hipSuccess) return LA_ERR_LAUNCH;
-            a.s_in = cs;
-        }
-    }
-    if (pl.G > 1) {
-        a.G = pl.G - 1;  // partials of groups 0 .. G-2
-        dispatch(f32, d, pl.C, 0, a, (int)(BH * pl.P * (pl.G - 1)), stream);
+        launch_slots(d, a, BH, pl.P, pl.NS, 0, stream);
     }
     a.G = pl.G;
     dispatch(f32, d, pl.C, 1, a, (int)(BH * pl.P * pl.G), stream);
@@ -1206,15 +1222,15 @@ la_status la_noncausal_fwd(const void *q, la_strides sq, const void *k, la_strid
     (void)hipGetLastError();
     char *ws = (char *)workspace;
     Args a = make_args(q, sq, k, sk, v, sv, out, so, B, H, N, eps);
-    a.P = pl.P; a.Gs = pl.Gs;
-    a.part = (float *)(ws + pl.part_off);
+    a.P = pl.P; a.NS = pl.NS;
+    a.part = (float *)ws;
     a.fin = (float *)(ws + pl.fin_off);
     const bool f32 = dt == LA_F32;
-    // 1) partial states of the token groups, 2) ordered reduction per head,
-    // 3) every query against the global state (token groups of L_apply)
-    a.G = pl.G; a.L = pl.L;
+    // 1) partial states of the token groups, 2) their sum per head in group
+    // order, 3) every query against the global state
+    a.G = pl.G; a.L = pl.L; a.slot0 = 0;
     dispatch(f32, d, pl.C, 0, a, (int)(BH * pl.P * pl.G), stream);
-    launch_reduce(d, a, (int)BH, pl.G, false, stream);
+    launch_slots(d, a, BH, pl.P, pl.G, 2, stream);
     const int la = pl.C * 4;
     a.L = la;
     a.G = (N + la - 1) / la;
