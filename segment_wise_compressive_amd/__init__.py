@@ -12,6 +12,7 @@ PyTorch is used for device memory and streams only.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 import re
 from typing import Optional, Tuple
@@ -26,6 +27,7 @@ __all__ = [
     "la_decode_step",
     "la_noncausal_workspace", "la_noncausal_fwd",
     "causal_fwd", "noncausal_fwd", "decode_step",
+    "Prepared", "prepare_causal_fwd", "prepare_noncausal_fwd", "prepare_decode_step",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -125,11 +127,20 @@ def la_version() -> int:
     return int(load_library().la_version())
 
 
+@functools.lru_cache(maxsize=4096)
+def _causal_ws(B, H, N, d, code, chunk, flags) -> int:
+    return int(load_library().la_causal_fwd_workspace(B, H, N, d, code, chunk, flags))
+
+
+@functools.lru_cache(maxsize=4096)
+def _noncausal_ws(B, H, N, d, code) -> int:
+    return int(load_library().la_noncausal_workspace(B, H, N, d, code))
+
+
 def la_causal_fwd_workspace(B: int, H: int, N: int, d: int, dtype: torch.dtype,
                             chunk: int = 0, inplace_state: bool = False) -> int:
     code = LA_F32 if dtype == torch.float32 else LA_BF16
-    return int(load_library().la_causal_fwd_workspace(B, H, N, d, code, chunk,
-                                                       LA_WS_INPLACE_STATE if inplace_state else 0))
+    return _causal_ws(B, H, N, d, code, chunk, LA_WS_INPLACE_STATE if inplace_state else 0)
 
 
 def la_causal_fwd(q, k, v, out=None, *, chunk: int = 0, eps: float = 1e-6,
@@ -187,7 +198,7 @@ def la_decode_step(q, k, v, z, s, out, *, eps: float = 1e-6, stream=None) -> Non
 
 def la_noncausal_workspace(B: int, H: int, N: int, d: int, dtype: torch.dtype) -> int:
     code = LA_F32 if dtype == torch.float32 else LA_BF16
-    return int(load_library().la_noncausal_workspace(B, H, N, d, code))
+    return _noncausal_ws(B, H, N, d, code)
 
 
 def la_noncausal_fwd(q, k, v, out, *, eps: float = 1e-6,
@@ -209,6 +220,79 @@ def la_noncausal_fwd(q, k, v, out, *, eps: float = 1e-6,
         _ptr(out), _strides(out), B, H, N, d, float(eps),
         _ptr(workspace), have, _stream(stream, q.device))
     _check(st, "la_noncausal_fwd")
+
+
+# ---------------------------------------------------------------- prepared calls
+class Prepared:
+    """A C-ABI call with every argument marshalled once.
+
+    For loops that call the library repeatedly on the same buffers (serving
+    loops, benchmarks): calling the object re-issues the C call with the
+    arguments fixed at construction, on the stream current at call time unless
+    one was given.  The tensors must stay alive and keep their storage.
+    """
+
+    def __init__(self, fn, args, stream_index, device, where):
+        self._fn, self._args, self._si, self._dev, self._where = fn, list(args), stream_index, device, where
+        self._fixed_stream = args[stream_index] is not None
+
+    def __call__(self):
+        if not self._fixed_stream:
+            self._args[self._si] = ctypes.c_void_p(torch.cuda.current_stream(self._dev).cuda_stream)
+        st = self._fn(*self._args)
+        if st != 0:
+            raise LinAttnError(st, self._where)
+
+
+def prepare_causal_fwd(q, k, v, out=None, *, chunk: int = 0, eps: float = 1e-6,
+                       z_in=None, s_in=None, z_out=None, s_out=None,
+                       workspace: Optional[torch.Tensor] = None, stream=None) -> Prepared:
+    """Validate and marshal a la_causal_fwd call once; returns a callable."""
+    B, H, N, d = q.shape
+    la_causal_fwd(q, k, v, out, chunk=chunk, eps=eps, z_in=z_in, s_in=s_in, z_out=z_out, s_out=s_out,
+                  workspace=workspace, stream=stream)   # validates (and runs once)
+    inplace = (z_out is not None and z_in is not None and z_out.data_ptr() == z_in.data_ptr()) or \
+              (s_out is not None and s_in is not None and s_out.data_ptr() == s_in.data_ptr())
+    ws_bytes = la_causal_fwd_workspace(B, H, N, d, q.dtype, chunk, inplace)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    so = _strides(out) if out is not None else la_strides(0, 0, 0)
+    args = [_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v), _dtype_code(q),
+            _ptr(out), so, B, H, N, d, int(chunk), ctypes.c_float(eps),
+            _ptr(z_in), _ptr(s_in), _ptr(z_out), _ptr(s_out), _ptr(workspace), ctypes.c_size_t(have),
+            None if stream is None else _stream(stream, q.device)]
+    p = Prepared(load_library().la_causal_fwd, args, len(args) - 1, q.device, "la_causal_fwd")
+    p._keep = (q, k, v, out, z_in, s_in, z_out, s_out, workspace)
+    return p
+
+
+def prepare_noncausal_fwd(q, k, v, out, *, eps: float = 1e-6,
+                          workspace: Optional[torch.Tensor] = None, stream=None) -> Prepared:
+    """Validate and marshal a la_noncausal_fwd call once; returns a callable."""
+    B, H, N, d = q.shape
+    la_noncausal_fwd(q, k, v, out, eps=eps, workspace=workspace, stream=stream)
+    ws_bytes = la_noncausal_workspace(B, H, N, d, q.dtype)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = [_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v), _dtype_code(q),
+            _ptr(out), _strides(out), B, H, N, d, ctypes.c_float(eps), _ptr(workspace), ctypes.c_size_t(have),
+            None if stream is None else _stream(stream, q.device)]
+    p = Prepared(load_library().la_noncausal_fwd, args, len(args) - 1, q.device, "la_noncausal_fwd")
+    p._keep = (q, k, v, out, workspace)
+    return p
+
+
+def prepare_decode_step(q, k, v, z, s, out, *, eps: float = 1e-6, stream=None) -> Prepared:
+    """Validate and marshal a la_decode_step call once; returns a callable."""
+    B, H, d = q.shape
+    la_decode_step(q, k, v, z, s, out, eps=eps, stream=stream)
+    args = [_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(z), _ptr(s), _ptr(out), B, H, d,
+            ctypes.c_float(eps), None if stream is None else _stream(stream, q.device)]
+    p = Prepared(load_library().la_decode_step, args, len(args) - 1, q.device, "la_decode_step")
+    p._keep = (q, k, v, z, s, out)
+    return p
 
 
 # ---------------------------------------------------------------- conveniences

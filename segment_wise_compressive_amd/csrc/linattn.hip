@@ -188,16 +188,18 @@ constexpr int NTHR = NWAVE * WAVE;       // threads per workgroup
 __host__ __device__ constexpr int pad_of(bool f32) { return f32 ? 4 : 8; }  // 16 bytes of row padding
 
 // LDS bytes of one workgroup (one chunk stage, row major as loaded):
-//   phi(K) [C][D+pad]   (x2 for bf16: hi and lo parts)
-//   V      [C][DV+pad]  (the input values)
-//   Z^T    [DV][D+pad]  (x2 for bf16: hi and lo parts; the shared state)
-//   S      [D]          (fp32)
+//   phi(K) [C][D+pad]        (x2 for bf16: hi and lo parts)
+//   V      [C][DV+pad]       (the input values)
+//   Z^T    [DV+1][D+pad]     (x2 for bf16: hi and lo parts): the shared state
+//                            and S as row DV
 __host__ __device__ constexpr int lds_bytes(bool f32, int d, int dv, int c)
 {
-    return ((f32 ? 1 : 2) * c * (d + pad_of(f32)) + c * (dv + pad_of(f32)) + (f32 ? 1 : 2) * dv * (d + pad_of(f32))) *
-               (f32 ? 4 : 2) + d * 4;
+    return ((f32 ? 1 : 2) * c * (d + pad_of(f32)) + c * (dv + pad_of(f32)) +
+            (f32 ? 1 : 2) * (dv + 1) * (d + pad_of(f32))) * (f32 ? 4 : 2);
 }
 constexpr int LDS_LIMIT = 160 * 1024;  // per workgroup on gfx950
+// workgroups per CU the causal kernel's register budget is sized for
+__host__ __device__ constexpr int minwg_of(int d, int c) { return (d <= 64 && c == 64) ? 3 : 1; }
 
 template <bool F32, int D, int DV, int C>
 struct Geo {
@@ -214,10 +216,17 @@ struct Geo {
     static constexpr int RV = DV + PAD;    // row stride of V [token][col]
     static constexpr int NP = F32 ? 1 : 2; // copies of phi(K) and Z^T (hi, lo)
     static constexpr int OK = 0, OKL = C * RK, OV = NP * C * RK;
-    static constexpr int OZ = OV + C * RV, OZL = OZ + DV * RK;
-    static constexpr int NE = OZ + NP * DV * RK;           // E elements before S
+    static constexpr int ZR = DV + 1;                      // rows of Z^T: state, then S
+    static constexpr int OZ = OV + C * RV, OZL = OZ + ZR * RK;
+    static constexpr int NE = OZ + NP * ZR * RK;           // E elements in all
     static constexpr int LDS_BYTES = lds_bytes(F32, D, DV, C);
-    static_assert(NE * (int)sizeof(E) + D * 4 == LDS_BYTES, "LDS layout");
+    static_assert(NE * (int)sizeof(E) == LDS_BYTES, "LDS layout");
+    // register pipeline depth: chunk c+DEPTH is loaded while chunk c is
+    // computed.  With output stores in the same loop, the gfx9 memory counter
+    // cannot separate older loads from newer ones, so a deeper register
+    // pipeline would only add registers; latency is hidden by occupancy.
+    static constexpr int DEPTH = 1;
+
     static_assert(TBN % NWAVE == 0 && (BPW == 1 || BPW == 2), "chunk must be 64 or 128 tokens");
     static_assert((JT * CT) % NWAVE == 0, "state tiles must split evenly over the waves");
     // 16-byte load items per chunk (rows x vectors)
@@ -272,7 +281,52 @@ __device__ __forceinline__ f32x4 mma8(f32x4 c, bf16x8 a, bf16x8 b)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+// ---- buffer access.  Every q/k/v/out access goes through a buffer resource
+// whose base is advanced per chunk with scalar arithmetic; lanes add a fixed
+// 32-bit offset.  Reads past the end of the resource return zero.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int RSRC_FLAGS = 0x00020000;   // raw (untyped) buffer, dword access
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes)
+{
+    const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : (int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, RSRC_FLAGS);
+}
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0); }
+__device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, f32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+}
+
+// A head's rows [t0, end of tensor): a view that buffer accesses index by
+// (row - t0) * stride + column bytes.
+struct RowView {
+    const char *head;   // element (row 0, col 0) of the head
+    int64_t rs;         // row stride in bytes
+    int64_t span;       // bytes from `head` to the end of the head's last row
+    __device__ __forceinline__ rsrc_t at(int t0) const { return make_rsrc(head + t0 * rs, span - t0 * rs); }
+    // rows from t0 if `live`, else an empty resource (reads return zero
+    // without touching memory, writes are dropped)
+    __device__ __forceinline__ rsrc_t at(int t0, bool live) const
+    {
+        return make_rsrc(head + t0 * rs, live ? span - t0 * rs : 0);
+    }
+};
+// a lane offset that is out of range for every resource (the access is dropped)
+constexpr uint32_t OFF_NONE = 0xfffffff0u;
+
+// bf16 pair <-> packed word; hi/lo split of two floats into two packed words
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b)
+{
+    bf16x2 v = {(bf16)a, (bf16)b};  // round to nearest even
+    return __builtin_bit_cast(uint32_t, v);
+}
+// returns {hi word, lo word}
+__device__ __forceinline__ uint2 split_pk(float a, float b)
+{
+    const uint32_t hi = pk_bf16(a, b);
+    return make_uint2(hi, pk_bf16(a - bf_lo(hi), b - bf_hi(hi)));
+}
 
 // Query rows of one wave tile: lane (r, g) holds query token r of the tile and
 // the dims it supplies as an MFMA operand, so phi(q) never goes through LDS.
@@ -282,42 +336,49 @@ struct QRegs {
     u32x4 raw[NQV];
 
     __device__ __forceinline__ static int dim0(int u, int g) { return F32 ? 16 * u + 4 * g : 32 * u + 8 * g; }
-
-    __device__ __forceinline__ void load(const char *qh, int64_t sqn, int t, bool valid, int g)
+    // byte offsets of the lane's vectors within a chunk view
+    __device__ __forceinline__ static void offsets(uint32_t *off, int row, int64_t rs, int g)
     {
         constexpr int ES = F32 ? 4 : 2;
 #pragma unroll
-        for (int u = 0; u < NQV; ++u)
-            raw[u] = valid ? ld16(qh + ((int64_t)t * sqn + dim0(u, g)) * ES) : (u32x4){0u, 0u, 0u, 0u};
+        for (int u = 0; u < NQV; ++u) off[u] = (uint32_t)(row * rs + dim0(u, g) * ES);
+    }
+    __device__ __forceinline__ void load(rsrc_t r, const uint32_t *off)
+    {
+#pragma unroll
+        for (int u = 0; u < NQV; ++u) raw[u] = bload16(r, off[u]);
     }
 };
 
 // Cooperative load of the k and v rows of one chunk into registers
 // (16-byte vectors, consecutive threads along a row), then phi and the LDS
-// stage.  Tokens at or beyond `nval` are not read and become exact zeros.
+// stage.  Rows at or beyond `nval` are zeroed in fill().
 template <bool F32, int D, int DV, int C>
 struct KVRegs {
     typedef Geo<F32, D, DV, C> G_;
+    static_assert(G_::IK % NTHR == 0 && G_::IV % NTHR == 0, "whole load items per thread");
     u32x4 k[G_::NK];
     u32x4 v[G_::NV];
 
-    __device__ __forceinline__ void load(int tid, const char *kh, const char *vh, int64_t skn, int64_t svn,
-                                         int t0, int nval, int col0)
+    __device__ __forceinline__ static void offsets(uint32_t *ko, uint32_t *vo, int tid, int64_t krs, int64_t vrs)
     {
-        constexpr int ES = F32 ? 4 : 2;
-        const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int it = 0; it < G_::NK; ++it) {
             const int idx = tid + it * NTHR;
-            const int row = idx / (D / G_::VEC), vg = idx % (D / G_::VEC);
-            k[it] = (idx < G_::IK && row < nval) ? ld16(kh + ((int64_t)(t0 + row) * skn + vg * G_::VEC) * ES) : z;
+            ko[it] = (uint32_t)((idx / (D / G_::VEC)) * krs + (idx % (D / G_::VEC)) * 16);
         }
 #pragma unroll
         for (int it = 0; it < G_::NV; ++it) {
             const int idx = tid + it * NTHR;
-            const int row = idx / (DV / G_::VEC), vg = idx % (DV / G_::VEC);
-            v[it] = (idx < G_::IV && row < nval) ? ld16(vh + ((int64_t)(t0 + row) * svn + col0 + vg * G_::VEC) * ES) : z;
+            vo[it] = (uint32_t)((idx / (DV / G_::VEC)) * vrs + (idx % (DV / G_::VEC)) * 16);
         }
+    }
+    __device__ __forceinline__ void load(rsrc_t kr, rsrc_t vr, const uint32_t *ko, const uint32_t *vo)
+    {
+#pragma unroll
+        for (int it = 0; it < G_::NK; ++it) k[it] = bload16(kr, ko[it]);
+#pragma unroll
+        for (int it = 0; it < G_::NV; ++it) v[it] = bload16(vr, vo[it]);
     }
 
     // phi(K): bf16 hi + lo (the state update sees phi(k) to ~16 bits; the
@@ -326,38 +387,32 @@ struct KVRegs {
     {
         typedef typename G_::E E;
         constexpr int VEC = G_::VEC;
+        const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int it = 0; it < G_::NK; ++it) {
             const int idx = tid + it * NTHR;
-            if (idx >= G_::IK) continue;
             const int row = idx / (D / VEC), vg = idx % (D / VEC);
             float f[VEC];
             Vec<F32>::to_float(k[it], f);
             const bool ok = row < nval;
             E *dst = st + G_::OK + row * G_::RK + vg * VEC;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) f[e] = ok ? phi<F32>(f[e]) : 0.f;
             if (F32) {
-                f32x4 o;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = ok ? phi<F32>(f[e]) : 0.f;
-                *reinterpret_cast<f32x4 *>(dst) = o;
+                *reinterpret_cast<f32x4 *>(dst) = (f32x4){f[0], f[1], f[2], f[3]};
             } else {
-                bf16x8 hi, lo;
+                u32x4 hi, lo;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float x = ok ? phi<F32>(f[e]) : 0.f;
-                    hi[e] = (bf16)x;
-                    lo[e] = (bf16)(x - (float)hi[e]);
-                }
-                *reinterpret_cast<bf16x8 *>(dst) = hi;
-                *reinterpret_cast<bf16x8 *>(dst + (G_::OKL - G_::OK)) = lo;
+                for (int e = 0; e < 4; ++e) { const uint2 sp_ = split_pk(f[2 * e], f[2 * e + 1]); hi[e] = sp_.x; lo[e] = sp_.y; }
+                *reinterpret_cast<u32x4 *>(dst) = hi;
+                *reinterpret_cast<u32x4 *>(dst + (G_::OKL - G_::OK)) = lo;
             }
         }
 #pragma unroll
         for (int it = 0; it < G_::NV; ++it) {
             const int idx = tid + it * NTHR;
-            if (idx >= G_::IV) continue;
             const int row = idx / (DV / VEC), vg = idx % (DV / VEC);
-            *reinterpret_cast<u32x4 *>(st + G_::OV + row * G_::RV + vg * VEC) = v[it];
+            *reinterpret_cast<u32x4 *>(st + G_::OV + row * G_::RV + vg * VEC) = row < nval ? v[it] : z;
         }
     }
 };
@@ -467,38 +522,43 @@ __device__ __forceinline__ void store_owned(float *z, int64_t ld, float *s, int 
 }
 
 // Publish the owned tiles to LDS: Z^T [col][dim] as MFMA A operands (hi + lo
-// for bf16) and S as fp32.
+// for bf16), and S as row DV of the same array, so that the inter-chunk
+// product also yields phi(q) . S (the normaliser) in its extra row tile.
 template <bool F32, int D, int DV, int C>
-__device__ __forceinline__ void publish_state(typename Geo<F32, D, DV, C>::E *sm, float *sS, int w, int r, int g,
+__device__ __forceinline__ void publish_state(typename Geo<F32, D, DV, C>::E *sm, int w, int r, int g,
                                               const f32x4 *Zown, const f32x4 *Sown)
 {
     typedef Geo<F32, D, DV, C> G_;
     constexpr int JT = G_::JT, CT = G_::CT;
     const int ct = own_ct<JT, CT>(w);
-#pragma unroll
-    for (int m = 0; m < G_::ZT; ++m) {
-        const int o = (16 * ct + r) * G_::RK + 16 * own_jt<JT, CT>(w, m) + 4 * g;
+    auto put = [&](int o, f32x4 x) {
         if (F32) {
-            *reinterpret_cast<f32x4 *>(sm + G_::OZ + o) = Zown[m];
+            *reinterpret_cast<f32x4 *>(sm + G_::OZ + o) = x;
         } else {
-            bf16x4 hi, lo;
-            split_hi_lo(Zown[m], hi, lo);
-            *reinterpret_cast<bf16x4 *>(sm + G_::OZ + o) = hi;
-            *reinterpret_cast<bf16x4 *>(sm + G_::OZL + o) = lo;
+            uint2 hi, lo;
+            { const uint2 sp_ = split_pk(x[0], x[1]); hi.x = sp_.x; lo.x = sp_.y; }
+            { const uint2 sp_ = split_pk(x[2], x[3]); hi.y = sp_.x; lo.y = sp_.y; }
+            *reinterpret_cast<uint2 *>(sm + G_::OZ + o) = hi;
+            *reinterpret_cast<uint2 *>(sm + G_::OZL + o) = lo;
         }
-    }
+    };
+#pragma unroll
+    for (int m = 0; m < G_::ZT; ++m) put((16 * ct + r) * G_::RK + 16 * own_jt<JT, CT>(w, m) + 4 * g, Zown[m]);
     if (r == 0) {
 #pragma unroll
         for (int m = 0; m < G_::SMAX; ++m) {
             const int jt = w + NWAVE * m;
-            if (jt < JT) *reinterpret_cast<f32x4 *>(sS + 16 * jt + 4 * g) = Sown[m];
+            if (jt < JT) put(DV * G_::RK + 16 * jt + 4 * g, Sown[m]);
         }
     }
 }
 
+template <int I> struct IC { static constexpr int value = I; };
+
 // ------------------------------------------------------------------ kernels
 // Partial state of one token group: A_g = phi(K_g)^T V_g (column block p),
-// S_g = sum phi(k).  Written to slot `slot0 + g`.
+// S_g = sum phi(k).  Written to slot `slot0 + g`.  Chunk c+2 is loaded while
+// chunk c is processed.
 template <bool F32, int D, int DV, int C>
 __global__ void __launch_bounds__(NTHR) k_group_state(const Args a)
 {
@@ -512,8 +572,11 @@ __global__ void __launch_bounds__(NTHR) k_group_state(const Args a)
     const int b = bh / a.H, h = bh % a.H;
     const int t_begin = grp * a.L, t_end = min(t_begin + a.L, a.N);
     constexpr int ES = F32 ? 4 : 2;
-    const char *kh = (const char *)a.k + (b * a.skb + h * a.skh) * ES;
-    const char *vh = (const char *)a.v + (b * a.svb + h * a.svh) * ES;
+    const RowView kv{(const char *)a.k + (b * a.skb + h * a.skh) * ES, a.skn * ES, (a.N - 1) * a.skn * ES + D * ES};
+    const RowView vv{(const char *)a.v + (b * a.svb + h * a.svh + p * DV) * ES, a.svn * ES,
+                     (a.N - 1) * a.svn * ES + DV * ES};
+    uint32_t ko[G_::NK], vo[G_::NV];
+    KVRegs<F32, D, DV, C>::offsets(ko, vo, tid, kv.rs, vv.rs);
 
     f32x4 Zown[G_::ZT], Sown[G_::SMAX];
 #pragma unroll
@@ -521,16 +584,29 @@ __global__ void __launch_bounds__(NTHR) k_group_state(const Args a)
 #pragma unroll
     for (int m = 0; m < G_::SMAX; ++m) Sown[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    KVRegs<F32, D, DV, C> R;
+    // Every memory access is issued unconditionally (chunks past the group
+    // read an empty resource), so the compiler can count outstanding accesses
+    // and wait only for the chunk it is about to use.
+    KVRegs<F32, D, DV, C> R[2];
     const int nch = (t_end - t_begin + C - 1) / C;
-    R.load(tid, kh, vh, a.skn, a.svn, t_begin, min(C, t_end - t_begin), p * DV);
-    for (int ch = 0; ch < nch; ++ch) {
+    auto issue = [&](int ch, auto slot) {
         const int t0 = t_begin + ch * C;
-        R.fill(tid, st, min(C, t_end - t0));
+        const bool live = ch < nch;
+        R[decltype(slot)::value].load(kv.at(t0, live), vv.at(t0, live), ko, vo);
+    };
+    auto step = [&](int ch, auto slot) {
+        const int t0 = t_begin + ch * C;
+        R[decltype(slot)::value].fill(tid, st, max(0, min(C, t_end - t0)));
         __syncthreads();
-        if (ch + 1 < nch) R.load(tid, kh, vh, a.skn, a.svn, t0 + C, min(C, t_end - t0 - C), p * DV);
+        issue(ch + 2, slot);
         state_update<F32, D, DV, C>(st, w, r, g, Zown, Sown);
         __syncthreads();
+    };
+    issue(0, IC<0>{});
+    issue(1, IC<1>{});
+    for (int ch = 0; ch < nch; ch += 2) {   // an odd count runs one empty step
+        step(ch, IC<0>{});
+        step(ch + 1, IC<1>{});
     }
     constexpr int SL = Slot<D, DV>::SIZE;
     float *slot = a.part + ((int64_t)(bh * a.P + p) * a.NS + a.slot0 + grp) * SL;
@@ -612,30 +688,45 @@ __global__ void __launch_bounds__(256) k_slots(const Args a, int nslots, int mod
 //         the last group writes z_out/s_out.
 // !CAUSAL (non-causal apply): out_t = phi(q_t) Z / (phi(q_t) . S + eps) with
 //         the reduced global state.
+// The normaliser comes out of the same MFMAs: S is an extra row of Z^T and an
+// all-ones row is an extra row of V^T, so an extra 16-row output tile (whose
+// other rows are zero operands) accumulates phi(q_t) . S_prev + sum_s P_ts in
+// its first row.
+// Loaded registers are consumed at one point per chunk (before the first
+// barrier); chunk c+DEPTH is requested right after it.
 template <bool F32, int D, int DV, int C, bool CAUSAL>
-__global__ void __launch_bounds__(NTHR) k_chunk_fwd(const Args a)
+__global__ void __launch_bounds__(NTHR, minwg_of(D, C)) k_chunk_fwd(const Args a)
 {
     typedef Geo<F32, D, DV, C> G_;
     typedef typename G_::E E;
     constexpr int JT = G_::JT, CT = G_::CT, TBN = G_::TBN, BPW = G_::BPW, NQV = G_::NQV;
+    constexpr int DEPTH = G_::DEPTH;
     constexpr int ES = F32 ? 4 : 2;
     constexpr int SL = Slot<D, DV>::SIZE;
+    typedef typename pick<F32, f32x4, bf16x8>::type QOp;   // one MFMA operand of phi(q)
     __shared__ __attribute__((aligned(16))) char smem_raw[G_::LDS_BYTES];
     E *sm = reinterpret_cast<E *>(smem_raw);
-    float *sS = reinterpret_cast<float *>(smem_raw + G_::NE * sizeof(E));
 
     const int tid = threadIdx.x, w = tid / WAVE, lane = tid % WAVE, r = lane % 16, g = lane / 16;
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
     const int p = wg % a.P, rest = wg / a.P, grp = rest % a.G, bh = rest / a.G;
     const int b = bh / a.H, h = bh % a.H;
     const int t_begin = grp * a.L, t_end = min(t_begin + a.L, a.N);
-    const char *qh = (const char *)a.q + (b * a.sqb + h * a.sqh) * ES;
-    const char *kh = (const char *)a.k + (b * a.skb + h * a.skh) * ES;
-    const char *vh = (const char *)a.v + (b * a.svb + h * a.svh) * ES;
-    float *oh = a.out + b * a.sob + h * a.soh + p * DV;
+    const RowView qv{(const char *)a.q + (b * a.sqb + h * a.sqh) * ES, a.sqn * ES, (a.N - 1) * a.sqn * ES + D * ES};
+    const RowView kv{(const char *)a.k + (b * a.skb + h * a.skh) * ES, a.skn * ES, (a.N - 1) * a.skn * ES + D * ES};
+    const RowView vv{(const char *)a.v + (b * a.svb + h * a.svh + p * DV) * ES, a.svn * ES,
+                     (a.N - 1) * a.svn * ES + DV * ES};
+    const RowView ov{(const char *)(a.out + b * a.sob + h * a.soh + p * DV), a.son * 4, (a.N - 1) * a.son * 4 + DV * 4};
     int tbs[BPW];
     tbs[0] = w;
     if (BPW == 2) tbs[BPW - 1] = TBN - 1 - w;
+    uint32_t ko[G_::NK], vo[G_::NV], qo[BPW][NQV], oo[BPW];
+    if (CAUSAL) KVRegs<F32, D, DV, C>::offsets(ko, vo, tid, kv.rs, vv.rs);
+#pragma unroll
+    for (int bi = 0; bi < BPW; ++bi) {
+        QRegs<F32, D>::offsets(qo[bi], 16 * tbs[bi] + r, qv.rs, g);
+        oo[bi] = (uint32_t)((16 * tbs[bi] + r) * ov.rs + 16 * g);
+    }
 
     // ---- starting state: owned tiles, published to LDS
     f32x4 Zown[G_::ZT], Sown[G_::SMAX];
@@ -651,82 +742,106 @@ __global__ void __launch_bounds__(NTHR) k_chunk_fwd(const Args a)
         const float *sl = a.fin + (int64_t)(bh * a.P + p) * SL;
         load_owned<JT, CT, G_::ZT, G_::SMAX>(sl, DV, sl + Slot<D, DV>::Z, w, r, g, Zown, Sown);
     }
-    publish_state<F32, D, DV, C>(sm, sS, w, r, g, Zown, Sown);
+    publish_state<F32, D, DV, C>(sm, w, r, g, Zown, Sown);
 
-    QRegs<F32, D> Q[BPW];
-    KVRegs<F32, D, DV, C> R;
+    KVRegs<F32, D, DV, C> R[DEPTH];
+    QRegs<F32, D> Q[DEPTH][BPW];
     const int nch = (t_end - t_begin + C - 1) / C;
-#pragma unroll
-    for (int bi = 0; bi < BPW; ++bi) {
-        const int tq = 16 * tbs[bi] + r;
-        Q[bi].load(qh, a.sqn, t_begin + tq, tq < t_end - t_begin, g);
-    }
-    if (CAUSAL) R.load(tid, kh, vh, a.skn, a.svn, t_begin, min(C, t_end - t_begin), p * DV);
-    else __syncthreads();
-
-    for (int ch = 0; ch < nch; ++ch) {
+    // Every memory access is issued unconditionally (chunks past the group
+    // read an empty resource; stores of rows outside the group use an
+    // out-of-range offset), so the compiler can count outstanding accesses
+    // and wait only for the chunk it is about to use.
+    auto issue = [&](int ch, auto slot) {
+        constexpr int S_ = decltype(slot)::value;
         const int t0 = t_begin + ch * C;
-        const int nval = min(C, t_end - t0);
-        const bool more = ch + 1 < nch;
-        if (CAUSAL) {
-            R.fill(tid, sm, nval);
-            __syncthreads();   // stage, Z and S of this chunk visible
-            if (more) R.load(tid, kh, vh, a.skn, a.svn, t0 + C, min(C, t_end - t0 - C), p * DV);
+        const bool live = ch < nch;
+        if (CAUSAL) R[S_].load(kv.at(t0, live), vv.at(t0, live), ko, vo);
+        const rsrc_t qr = qv.at(t0, live);
+#pragma unroll
+        for (int bi = 0; bi < BPW; ++bi) Q[S_][bi].load(qr, qo[bi]);
+    };
+
+    // all-ones row of V^T (lane row 0 of the extra tile), a constant operand
+    QOp ones_row;
+    {
+        const float one = r == 0 ? 1.f : 0.f;
+        if (F32) {
+            f32x4 o4 = {one, one, one, one};
+            ones_row = *reinterpret_cast<QOp *>(&o4);
+        } else {
+            const bf16 ob = (bf16)one;
+            bf16x8 o8 = {ob, ob, ob, ob, ob, ob, ob, ob};
+            ones_row = *reinterpret_cast<QOp *>(&o8);
         }
+    }
+
+    auto step = [&](int ch, auto slot) {
+        constexpr int S_ = decltype(slot)::value;
+        const int t0 = t_begin + ch * C;
+        const int nval = max(0, min(C, t_end - t0));
+        // ---- consume the registers of chunk ch: K, V into the stage, phi(q)
+        if (CAUSAL) R[S_].fill(tid, sm, nval);
+        QOp qhi[BPW][NQV], qlo[BPW][NQV];
+#pragma unroll
+        for (int bi = 0; bi < BPW; ++bi) {
+            const bool valid = 16 * tbs[bi] + r < nval;
+#pragma unroll
+            for (int u = 0; u < NQV; ++u) {
+                float f[Vec<F32>::N];
+                Vec<F32>::to_float(Q[S_][bi].raw[u], f);
+#pragma unroll
+                for (int e = 0; e < Vec<F32>::N; ++e) f[e] = valid ? phi<F32>(f[e]) : 0.f;
+                if (F32) {
+                    f32x4 x = {f[0], f[1], f[2], f[3]};
+                    qhi[bi][u] = *reinterpret_cast<QOp *>(&x);
+                } else {
+                    u32x4 hi, lo;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { const uint2 sp_ = split_pk(f[2 * e], f[2 * e + 1]); hi[e] = sp_.x; lo[e] = sp_.y; }
+                    qhi[bi][u] = __builtin_bit_cast(QOp, hi);
+                    qlo[bi][u] = __builtin_bit_cast(QOp, lo);
+                }
+            }
+        }
+        if (CAUSAL || ch == 0) __syncthreads();   // stage and published state visible
+        // ---- request chunk ch + DEPTH into the registers just consumed
+        issue(ch + DEPTH, slot);
 
 #pragma unroll
         for (int bi = 0; bi < BPW; ++bi) {
             const int tb = tbs[bi];
             const int tq = 16 * tb + r;
-            const bool valid = tq < nval;
-            // phi(q) in fp32 (normaliser against S), then the MFMA operands
-            float fq[NQV][Vec<F32>::N];
-            float dp = 0.f;
+            f32x4 o[CT + 1];   // value tiles, then the normaliser tile
 #pragma unroll
-            for (int u = 0; u < NQV; ++u) {
-                Vec<F32>::to_float(Q[bi].raw[u], fq[u]);
-                const int d0 = QRegs<F32, D>::dim0(u, g);
-#pragma unroll
-                for (int e = 0; e < Vec<F32>::N; ++e) {
-                    fq[u][e] = valid ? phi<F32>(fq[u][e]) : 0.f;
-                    dp += fq[u][e] * sS[d0 + e];
-                }
-            }
-            if (more) {
-                const int tn = t0 + C + tq;
-                Q[bi].load(qh, a.sqn, tn, tn < t_end, g);
-            }
-            f32x4 o[CT];
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) o[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            float rs = 0.f;
+            for (int ct = 0; ct <= CT; ++ct) o[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
             if (F32) {
                 const float *kf = reinterpret_cast<const float *>(sm) + G_::OK;
                 const float *vf = reinterpret_cast<const float *>(sm) + G_::OV;
                 const float *zf = reinterpret_cast<const float *>(sm) + G_::OZ;
-                f32x4 qf[NQV];
+                // inter-chunk term (and phi(q) . S in the extra tile)
 #pragma unroll
-                for (int u = 0; u < NQV; ++u) qf[u] = (f32x4){fq[u][0], fq[u][1], fq[u][2], fq[u][3]};
-                // inter-chunk term: O^T += Z^T phi(Q)^T
+                for (int ct = 0; ct <= CT; ++ct)
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                    for (int u = 0; u < NQV; ++u)
-                        o[ct] = mma1(o[ct], nat4(zf + (16 * ct + r) * G_::RK + 16 * u + 4 * g), qf[u]);
+                    for (int u = 0; u < NQV; ++u) {
+                        f32x4 za = {0.f, 0.f, 0.f, 0.f};
+                        if (ct < CT || r == 0) za = nat4(zf + (16 * ct + r) * G_::RK + 16 * u + 4 * g);
+                        o[ct] = mma1(o[ct], za, *reinterpret_cast<const f32x4 *>(&qhi[bi][u]));
+                    }
                 if (CAUSAL) {
                     for (int sa = 0; sa <= tb; ++sa) {
                         f32x4 pt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int u = 0; u < NQV; ++u)
-                            pt = mma1(pt, nat4(kf + (16 * sa + r) * G_::RK + 16 * u + 4 * g), qf[u]);
+                            pt = mma1(pt, nat4(kf + (16 * sa + r) * G_::RK + 16 * u + 4 * g),
+                                      *reinterpret_cast<const f32x4 *>(&qhi[bi][u]));
                         if (sa == tb) {
 #pragma unroll
                             for (int i = 0; i < 4; ++i) if (4 * g + i > r) pt[i] = 0.f;
                         }
-                        rs += (pt[0] + pt[1]) + (pt[2] + pt[3]);
 #pragma unroll
                         for (int ct = 0; ct < CT; ++ct)
                             o[ct] = mma1(o[ct], trf(vf, G_::RV, 16 * sa, 16 * ct, r, g), pt);
+                        o[CT] = mma1(o[CT], *reinterpret_cast<const f32x4 *>(&ones_row), pt);
                     }
                 }
             } else {
@@ -734,38 +849,34 @@ __global__ void __launch_bounds__(NTHR) k_chunk_fwd(const Args a)
                 const bf16 *vb = reinterpret_cast<const bf16 *>(sm) + G_::OV;
                 const bf16 *zh = reinterpret_cast<const bf16 *>(sm) + G_::OZ;
                 const bf16 *zl = reinterpret_cast<const bf16 *>(sm) + G_::OZL;
-                bf16x8 qh8[NQV], ql8[NQV];
+                // inter-chunk term with Z and phi(q) as hi + lo (and phi(q) . S)
 #pragma unroll
-                for (int u = 0; u < NQV; ++u) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        qh8[u][e] = (bf16)fq[u][e];
-                        ql8[u][e] = (bf16)(fq[u][e] - (float)qh8[u][e]);
-                    }
-                }
-                // inter-chunk term: O^T += Z^T phi(Q)^T with Z and phi(q) as hi + lo
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
+                for (int ct = 0; ct <= CT; ++ct) {
                     const int zo = (16 * ct + r) * G_::RK + 8 * g;
 #pragma unroll
                     for (int u = 0; u < NQV; ++u) {
-                        const bf16x8 a_hi = nat8(zh + zo + 32 * u), a_lo = nat8(zl + zo + 32 * u);
-                        o[ct] = mma8(o[ct], a_hi, qh8[u]);
-                        o[ct] = mma8(o[ct], a_lo, qh8[u]);
-                        o[ct] = mma8(o[ct], a_hi, ql8[u]);
+                        const bf16x8 qh8 = *reinterpret_cast<const bf16x8 *>(&qhi[bi][u]);
+                        const bf16x8 ql8 = *reinterpret_cast<const bf16x8 *>(&qlo[bi][u]);
+                        bf16x8 a_hi = {}, a_lo = {};
+                        if (ct < CT || r == 0) { a_hi = nat8(zh + zo + 32 * u); a_lo = nat8(zl + zo + 32 * u); }
+                        o[ct] = mma8(o[ct], a_hi, qh8);
+                        o[ct] = mma8(o[ct], a_lo, qh8);
+                        o[ct] = mma8(o[ct], a_hi, ql8);
                     }
                 }
                 if (CAUSAL) {
                     // intra-chunk term over key tiles sa <= tb: scores P^T (rows =
                     // keys, columns = queries) feed P V as the B operand directly
                     const bf16 zr = (bf16)0.f;
+                    const bf16x8 ones8 = *reinterpret_cast<const bf16x8 *>(&ones_row);
                     for (int sa = 0; sa <= tb; sa += 2) {
                         const bool two = sa + 1 <= tb;
                         f32x4 pt0 = {0.f, 0.f, 0.f, 0.f}, pt1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int u = 0; u < NQV; ++u) {
-                            pt0 = mma8(pt0, nat8(kb + (16 * sa + r) * G_::RK + 32 * u + 8 * g), qh8[u]);
-                            if (two) pt1 = mma8(pt1, nat8(kb + (16 * sa + 16 + r) * G_::RK + 32 * u + 8 * g), qh8[u]);
+                            const bf16x8 qh8 = *reinterpret_cast<const bf16x8 *>(&qhi[bi][u]);
+                            pt0 = mma8(pt0, nat8(kb + (16 * sa + r) * G_::RK + 32 * u + 8 * g), qh8);
+                            if (two) pt1 = mma8(pt1, nat8(kb + (16 * sa + 16 + r) * G_::RK + 32 * u + 8 * g), qh8);
                         }
                         // causal mask inside the diagonal tile: key 4g+i > query r
                         if (sa == tb) {
@@ -776,13 +887,15 @@ __global__ void __launch_bounds__(NTHR) k_chunk_fwd(const Args a)
 #pragma unroll
                             for (int i = 0; i < 4; ++i) if (4 * g + i > r) pt1[i] = 0.f;
                         }
-                        rs += (pt0[0] + pt0[1]) + (pt0[2] + pt0[3]);
-                        if (two) rs += (pt1[0] + pt1[1]) + (pt1[2] + pt1[3]);
-                        bf16x4 ph0, pl0, ph1 = {zr, zr, zr, zr}, pl1 = {zr, zr, zr, zr};
-                        split_hi_lo(pt0, ph0, pl0);
-                        if (two) split_hi_lo(pt1, ph1, pl1);
-                        const bf16x8 bh8 = __builtin_shufflevector(ph0, ph1, 0, 1, 2, 3, 4, 5, 6, 7);
-                        const bf16x8 bl8 = __builtin_shufflevector(pl0, pl1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        u32x4 phw = {0u, 0u, 0u, 0u}, plw = {0u, 0u, 0u, 0u};
+                        { const uint2 sp_ = split_pk(pt0[0], pt0[1]); phw[0] = sp_.x; plw[0] = sp_.y; }
+                        { const uint2 sp_ = split_pk(pt0[2], pt0[3]); phw[1] = sp_.x; plw[1] = sp_.y; }
+                        if (two) {
+                            { const uint2 sp_ = split_pk(pt1[0], pt1[1]); phw[2] = sp_.x; plw[2] = sp_.y; }
+                            { const uint2 sp_ = split_pk(pt1[2], pt1[3]); phw[3] = sp_.x; plw[3] = sp_.y; }
+                        }
+                        const bf16x8 bh8 = __builtin_bit_cast(bf16x8, phw);
+                        const bf16x8 bl8 = __builtin_bit_cast(bf16x8, plw);
 #pragma unroll
                         for (int ct = 0; ct < CT; ++ct) {
                             bf16x4 va0 = tr4(vb, G_::RV, 16 * sa, 16 * ct, r, g);
@@ -792,23 +905,32 @@ __global__ void __launch_bounds__(NTHR) k_chunk_fwd(const Args a)
                             o[ct] = mma8(o[ct], a8, bh8);
                             o[ct] = mma8(o[ct], a8, bl8);
                         }
+                        o[CT] = mma8(o[CT], ones8, bh8);
+                        o[CT] = mma8(o[CT], ones8, bl8);
                     }
                 }
             }
-            const float den = reduce_lane_groups(dp + rs) + a.eps;
-            if (valid) {
-                const float inv = 1.f / den;
-                float *orow = oh + (int64_t)(t0 + tq) * a.son + 4 * g;
+            // normaliser of query r: row 0 of the extra tile, held by lane r
+            const float den = __shfl(o[CT][0], r) + a.eps;
+            const float inv = 1.f / den;
+            const rsrc_t orr = ov.at(t0);
+            const uint32_t obase = tq < nval ? oo[bi] : OFF_NONE;
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct) *reinterpret_cast<f32x4 *>(orow + 16 * ct) = o[ct] * inv;
-            }
+            for (int ct = 0; ct < CT; ++ct) bstore16(orr, tq < nval ? obase + 64 * ct : OFF_NONE, o[ct] * inv);
         }
 
         if (CAUSAL) {
             state_update<F32, D, DV, C>(sm, w, r, g, Zown, Sown);
-            __syncthreads();   // every wave is done with this chunk's stage, Z and S
-            publish_state<F32, D, DV, C>(sm, sS, w, r, g, Zown, Sown);
+            __syncthreads();   // every wave is done with this chunk's stage and state
+            publish_state<F32, D, DV, C>(sm, w, r, g, Zown, Sown);
         }
+    };
+
+    issue(0, IC<0>{});
+    if (DEPTH == 2) issue(1, IC<DEPTH - 1>{});
+    for (int ch = 0; ch < nch; ch += DEPTH) {   // an odd count runs one empty step
+        step(ch, IC<0>{});
+        if (DEPTH == 2) step(ch + 1, IC<DEPTH - 1>{});
     }
 
     if (CAUSAL && grp == a.G - 1)
@@ -907,12 +1029,12 @@ inline int cols_per_wg(int d) { return d < 64 ? d : 64; }
 template <bool F32, int D, int DV, int C>
 constexpr bool fits() { return lds_bytes(F32, D, DV, C) <= LDS_LIMIT; }
 
-// Chunk of 64 or 128 tokens (requests below 64 run as 64; fp32 inputs use 64),
-// the largest <= the request whose LDS fits one workgroup.
+// Chunk of 64 or 128 tokens (requests below 64 run as 64; fp32 inputs and
+// d = 128 use 64: register budget).
 int pick_chunk(bool f32, int d, int chunk)
 {
     if (chunk == 0 || chunk < 64 || f32) chunk = 64;   // fp32: 64 (register budget)
-    if (chunk >= 128 && lds_bytes(f32, d, cols_per_wg(d), 128) <= LDS_LIMIT) return 128;
+    if (chunk >= 128 && d <= 64 && lds_bytes(f32, d, cols_per_wg(d), 128) <= LDS_LIMIT) return 128;
     return 64;
 }
 
@@ -996,7 +1118,7 @@ template <bool F32, int D, int C>
 void launch_dc(int what, const Args &a, int nwg, hipStream_t st)
 {
     constexpr int DV = D < 64 ? D : 64;
-    if constexpr (fits<F32, D, DV, C>()) {
+    if constexpr (fits<F32, D, DV, C>() && (C == 64 || (!F32 && D <= 64))) {
         if (what == 0) hipLaunchKernelGGL((k_group_state<F32, D, DV, C>), dim3(nwg), dim3(NTHR), 0, st, a);
         else if (what == 1) hipLaunchKernelGGL((k_chunk_fwd<F32, D, DV, C, true>), dim3(nwg), dim3(NTHR), 0, st, a);
         else hipLaunchKernelGGL((k_chunk_fwd<F32, D, DV, C, false>), dim3(nwg), dim3(NTHR), 0, st, a);
