@@ -58,6 +58,22 @@ def time_steps(fn, steps, warmup, n_rot):
     return t_start.elapsed_time(t_end), [a.elapsed_time(b) for a, b in evs]
 
 
+def measured_traffic(name):
+    """HBM bytes per call from the FETCH_SIZE / WRITE_SIZE summary kept in
+    profiles/, or None when that summary was taken on another version of the
+    HIP source (its recorded sha256 no longer matches)."""
+    import hashlib
+    try:
+        text = open(os.path.join(ROOT, "profiles", f"{name}_hbm_bytes.txt")).read()
+        src = open(os.path.join(ROOT, "segment_wise_compressive_amd", "csrc", "linattn.hip"), "rb").read()
+    except OSError:
+        return None
+    fields = dict(l.split(": ", 1) for l in text.splitlines() if l.startswith(("traffic_bytes_per_call:", "source_sha256:")))
+    if fields.get("source_sha256", "").strip() != hashlib.sha256(src).hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_call"])
+
+
 def roofline(bytes_per_call, ms_per_call, traffic=None):
     achieved = bytes_per_call / (ms_per_call * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -76,9 +92,10 @@ def bench_headline(args, torch, la, inp):
     ws = torch.empty(max(1, la.la_causal_fwd_workspace(w.B, w.H, w.N, w.d, w.dtype, w.chunk)),
                      dtype=torch.uint8, device=dev)
 
+    calls = [la.prepare_causal_fwd(a[0], a[1], a[2], a[3], chunk=w.chunk, eps=w.eps, workspace=ws) for a in sets]
+
     def step(i):
-        a = sets[i]
-        la.la_causal_fwd(a[0], a[1], a[2], a[3], chunk=w.chunk, eps=w.eps, workspace=ws)
+        calls[i]()
 
     total_ms, per = time_steps(step, args.steps, args.warmup, n_rot)
     per_call = sum(per) / len(per)
@@ -97,12 +114,16 @@ def bench_segmented(args, torch, la, inp):
                      device=dev)
     nseg = N // w.segment
 
+    calls = []
+    for i in range(nseg):
+        sl = slice(i * w.segment, (i + 1) * w.segment)
+        calls.append(la.prepare_causal_fwd(q[:, :, sl], k[:, :, sl], v[:, :, sl], out[:, :, sl], eps=w.eps,
+                                           z_in=zs[i & 1] if i else None, s_in=ss[i & 1] if i else None,
+                                           z_out=zs[(i + 1) & 1], s_out=ss[(i + 1) & 1], workspace=ws))
+
     def step(_):
-        for i in range(nseg):
-            sl = slice(i * w.segment, (i + 1) * w.segment)
-            la.la_causal_fwd(q[:, :, sl], k[:, :, sl], v[:, :, sl], out[:, :, sl], eps=w.eps,
-                             z_in=zs[i & 1] if i else None, s_in=ss[i & 1] if i else None,
-                             z_out=zs[(i + 1) & 1], s_out=ss[(i + 1) & 1], workspace=ws)
+        for c in calls:
+            c()
 
     steps = max(3, args.steps // 4)
     total_ms, per = time_steps(step, steps, max(1, args.warmup // 2), 1)
@@ -131,12 +152,15 @@ def bench_decode(args, torch, la, inp):
             ss.append(s)
         out = torch.empty(B, H, d, device=dev)
 
-        def step(i):
-            t = i % T
-            la.la_decode_step(sqd[t], skd[t], svd[t], zs[i % nstate], ss[i % nstate], out, eps=w.eps)
+        nst = min(T, 256)
+        calls = [la.prepare_decode_step(sqd[t], skd[t], svd[t], zs[t % nstate], ss[t % nstate], out, eps=w.eps)
+                 for t in range(nst)]
 
-        total_ms, per = time_steps(step, min(T, 256), 16, 10 ** 9)
-        ms = total_ms / min(T, 256)
+        def step(i):
+            calls[i % nst]()
+
+        total_ms, per = time_steps(step, nst, 16, 10 ** 9)
+        ms = total_ms / nst
         per_call = sum(per) / len(per)
         bpc = B * H * (2 * (d * d + d) * 4 + 3 * d * w.dtype.itemsize + d * 4)
         res[label] = {"ms_per_step": round(ms, 5), "value": round(B * H / (ms * 1e-3), 1),
@@ -151,8 +175,10 @@ def bench_noncausal(args, torch, la, inp):
     out = torch.empty(w.B, w.H, w.N, w.d, dtype=torch.float32, device=dev)
     ws = torch.empty(max(1, la.la_noncausal_workspace(w.B, w.H, w.N, w.d, w.dtype)), dtype=torch.uint8, device=dev)
 
+    call = la.prepare_noncausal_fwd(q, k, v, out, eps=w.eps, workspace=ws)
+
     def step(_):
-        la.la_noncausal_fwd(q, k, v, out, eps=w.eps, workspace=ws)
+        call()
 
     steps = max(3, args.steps // 2)
     total_ms, per = time_steps(step, steps, 2, 1)
@@ -161,15 +187,21 @@ def bench_noncausal(args, torch, la, inp):
             "ms_per_step": round(per_call, 4), "roofline": roofline(alg_bytes_causal(w), per_call)}
 
 
-def cpu_baseline(w, qkv):
+def cpu_baseline(w, qkv, seconds):
+    """The fp64 oracle, as it is, on the host cores: whole steps of the same
+    workload repeated until `seconds` of wall time have passed (at least 2)."""
     import oracle
     q, k, v = qkv
+    reps = 0
     t0 = time.perf_counter()
-    oracle.causal(q, k, v, w.eps)
+    while reps < 2 or time.perf_counter() - t0 < seconds:
+        oracle.causal(q, k, v, w.eps)
+        reps += 1
     dt = time.perf_counter() - t0
-    return {"value": round(w.head_tokens / dt, 1), "unit": "head-tokens/s", "cores": oracle.max_threads(),
+    return {"value": round(reps * w.head_tokens / dt, 1), "unit": "head-tokens/s", "cores": oracle.max_threads(),
             "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"one full step of {w.name}: all {w.B * w.H} heads x {w.N} tokens, fp64 recurrent form"}
+            "sample": f"{reps} whole steps of {w.name} (all {w.B * w.H} heads x {w.N} tokens each), "
+                      f"fp64 recurrent form, run back to back for about {seconds:g} s"}
 
 
 def main():
@@ -180,6 +212,10 @@ def main():
     ap.add_argument("--rotate", type=int, default=8, help="input/output sets rotated over the steps")
     ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="wall time given to the oracle baseline")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy 3 times (the reference kernel for scaling "
+                         "FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); run it with --gpus 1.",
@@ -192,6 +228,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        n = 256 * 1024 * 1024  # float32 elements = 1 GiB
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty(n, device="cuda")
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n, "launches": 3}))
+        return
     la.load_library()
 
     log("headline workload ...")
@@ -213,9 +258,9 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "chunk": w.chunk,
                    "input_dtype": "bf16", "state_and_output_dtype": "fp32", "eps": w.eps, "seed": w.seed,
                    "rotated_sets": args.rotate},
-        "roofline": roofline(alg_bytes_causal(w), per_call),
+        "roofline": roofline(alg_bytes_causal(w), per_call, measured_traffic(w.name)),
     }
-    line["roofline"]["kernels"] = "k_group_state + k_chunk_fwd (one la_causal_fwd call)"
+    line["roofline"]["kernels"] = "k_group_state + k_slots + k_chunk_fwd: one la_causal_fwd call, timed as a whole"
     if not args.headline_only:
         log("segmented workload ...")
         line.setdefault("workloads", {})["segmented"] = bench_segmented(args, torch, la, inp)
@@ -225,7 +270,7 @@ def main():
         line["workloads"]["noncausal"] = bench_noncausal(args, torch, la, inp)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        line["cpu_baseline"] = cpu_baseline(w, qkv)
+        line["cpu_baseline"] = cpu_baseline(w, qkv, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

@@ -106,11 +106,6 @@ def _stream(stream, device) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def _check(status: int, where: str):
-    if status != 0:
-        raise LinAttnError(status, where)
-
-
 def _state_check(t, shape, name):
     if t is None:
         return
@@ -143,14 +138,41 @@ def la_causal_fwd_workspace(B: int, H: int, N: int, d: int, dtype: torch.dtype,
     return _causal_ws(B, H, N, d, code, chunk, LA_WS_INPLACE_STATE if inplace_state else 0)
 
 
-def la_causal_fwd(q, k, v, out=None, *, chunk: int = 0, eps: float = 1e-6,
-                  z_in=None, s_in=None, z_out=None, s_out=None,
-                  workspace: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Causal linear attention forward (see la_causal_fwd in linattn.h).
+class Prepared:
+    """A C-ABI call with every argument checked and marshalled once.
+
+    Calling the object issues the C call with those arguments, on the stream
+    given at construction or else on the stream current at call time, and
+    raises LinAttnError on a non-OK status.  For loops that call the library
+    repeatedly on the same buffers (serving loops, benchmarks).  The object
+    keeps the tensors alive; their storage must not be reallocated.
+    """
+
+    def __init__(self, fn, args, device, where, keep):
+        self._fn, self._args, self._dev, self._where, self._keep = fn, list(args), device, where, keep
+        self._fixed_stream = args[-1] is not None
+
+    def __call__(self) -> None:
+        if not self._fixed_stream:
+            self._args[-1] = ctypes.c_void_p(torch.cuda.current_stream(self._dev).cuda_stream)
+        st = self._fn(*self._args)
+        if st != 0:
+            raise LinAttnError(st, self._where)
+
+
+def _opt_stream(stream, device):
+    return None if stream is None else _stream(stream, device)
+
+
+def prepare_causal_fwd(q, k, v, out=None, *, chunk: int = 0, eps: float = 1e-6,
+                       z_in=None, s_in=None, z_out=None, s_out=None,
+                       workspace: Optional[torch.Tensor] = None, stream=None) -> Prepared:
+    """Check and marshal a la_causal_fwd call (nothing runs until it is called).
 
     q, k, v: [B, H, N, d] bf16 or fp32 CUDA tensors (any strides with unit d stride).
     out: float32 [B, H, N, d] or None (state only).  States: float32 contiguous
     [B, H, d, d] / [B, H, d]; z_out/s_out may be the z_in/s_in tensors themselves.
+    A workspace of la_causal_fwd_workspace() bytes is allocated if none is given.
     """
     B, H, N, d = q.shape
     if tuple(k.shape) != (B, H, N, d) or tuple(v.shape) != (B, H, N, d):
@@ -169,19 +191,28 @@ def la_causal_fwd(q, k, v, out=None, *, chunk: int = 0, eps: float = 1e-6,
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     have = 0 if workspace is None else workspace.numel() * workspace.element_size()
     so = _strides(out) if out is not None else la_strides(0, 0, 0)
-    st = load_library().la_causal_fwd(
-        _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v), _dtype_code(q),
-        _ptr(out), so, B, H, N, d, int(chunk), float(eps),
-        _ptr(z_in), _ptr(s_in), _ptr(z_out), _ptr(s_out),
-        _ptr(workspace), have, _stream(stream, q.device))
-    _check(st, "la_causal_fwd")
+    args = [_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v), _dtype_code(q),
+            _ptr(out), so, B, H, N, d, int(chunk), ctypes.c_float(eps),
+            _ptr(z_in), _ptr(s_in), _ptr(z_out), _ptr(s_out), _ptr(workspace), ctypes.c_size_t(have),
+            _opt_stream(stream, q.device)]
+    return Prepared(load_library().la_causal_fwd, args, q.device, "la_causal_fwd",
+                    (q, k, v, out, z_in, s_in, z_out, s_out, workspace))
 
 
-def la_decode_step(q, k, v, z, s, out, *, eps: float = 1e-6, stream=None) -> None:
-    """One recurrent step per head; z, s updated in place (see linattn.h).
+def la_causal_fwd(q, k, v, out=None, *, chunk: int = 0, eps: float = 1e-6,
+                  z_in=None, s_in=None, z_out=None, s_out=None,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Causal linear attention forward (la_causal_fwd in linattn.h); arguments
+    as for prepare_causal_fwd."""
+    prepare_causal_fwd(q, k, v, out, chunk=chunk, eps=eps, z_in=z_in, s_in=s_in, z_out=z_out, s_out=s_out,
+                       workspace=workspace, stream=stream)()
+
+
+def prepare_decode_step(q, k, v, z, s, out, *, eps: float = 1e-6, stream=None) -> Prepared:
+    """Check and marshal a la_decode_step call (nothing runs until it is called).
 
     q, k, v: contiguous [B, H, d]; z float32 [B, H, d, d]; s float32 [B, H, d];
-    out float32 [B, H, d].
+    out float32 [B, H, d].  Each call updates z and s in place.
     """
     B, H, d = q.shape
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
@@ -190,10 +221,14 @@ def la_decode_step(q, k, v, z, s, out, *, eps: float = 1e-6, stream=None) -> Non
     _state_check(z, (B, H, d, d), "z")
     _state_check(s, (B, H, d), "s")
     _state_check(out, (B, H, d), "out")
-    st = load_library().la_decode_step(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q),
-                                       _ptr(z), _ptr(s), _ptr(out), B, H, d, float(eps),
-                                       _stream(stream, q.device))
-    _check(st, "la_decode_step")
+    args = [_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(z), _ptr(s), _ptr(out), B, H, d,
+            ctypes.c_float(eps), _opt_stream(stream, q.device)]
+    return Prepared(load_library().la_decode_step, args, q.device, "la_decode_step", (q, k, v, z, s, out))
+
+
+def la_decode_step(q, k, v, z, s, out, *, eps: float = 1e-6, stream=None) -> None:
+    """One recurrent step per head; z, s updated in place (la_decode_step in linattn.h)."""
+    prepare_decode_step(q, k, v, z, s, out, eps=eps, stream=stream)()
 
 
 def la_noncausal_workspace(B: int, H: int, N: int, d: int, dtype: torch.dtype) -> int:
@@ -201,9 +236,9 @@ def la_noncausal_workspace(B: int, H: int, N: int, d: int, dtype: torch.dtype) -
     return _noncausal_ws(B, H, N, d, code)
 
 
-def la_noncausal_fwd(q, k, v, out, *, eps: float = 1e-6,
-                     workspace: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Non-causal linear attention forward (see la_noncausal_fwd in linattn.h)."""
+def prepare_noncausal_fwd(q, k, v, out, *, eps: float = 1e-6,
+                          workspace: Optional[torch.Tensor] = None, stream=None) -> Prepared:
+    """Check and marshal a la_noncausal_fwd call (nothing runs until it is called)."""
     B, H, N, d = q.shape
     if tuple(k.shape) != (B, H, N, d) or tuple(v.shape) != (B, H, N, d):
         raise ValueError("q, k, v must have the same shape")
@@ -215,84 +250,16 @@ def la_noncausal_fwd(q, k, v, out, *, eps: float = 1e-6,
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     have = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = load_library().la_noncausal_fwd(
-        _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v), _dtype_code(q),
-        _ptr(out), _strides(out), B, H, N, d, float(eps),
-        _ptr(workspace), have, _stream(stream, q.device))
-    _check(st, "la_noncausal_fwd")
-
-
-# ---------------------------------------------------------------- prepared calls
-class Prepared:
-    """A C-ABI call with every argument marshalled once.
-
-    For loops that call the library repeatedly on the same buffers (serving
-    loops, benchmarks): calling the object re-issues the C call with the
-    arguments fixed at construction, on the stream current at call time unless
-    one was given.  The tensors must stay alive and keep their storage.
-    """
-
-    def __init__(self, fn, args, stream_index, device, where):
-        self._fn, self._args, self._si, self._dev, self._where = fn, list(args), stream_index, device, where
-        self._fixed_stream = args[stream_index] is not None
-
-    def __call__(self):
-        if not self._fixed_stream:
-            self._args[self._si] = ctypes.c_void_p(torch.cuda.current_stream(self._dev).cuda_stream)
-        st = self._fn(*self._args)
-        if st != 0:
-            raise LinAttnError(st, self._where)
-
-
-def prepare_causal_fwd(q, k, v, out=None, *, chunk: int = 0, eps: float = 1e-6,
-                       z_in=None, s_in=None, z_out=None, s_out=None,
-                       workspace: Optional[torch.Tensor] = None, stream=None) -> Prepared:
-    """Validate and marshal a la_causal_fwd call once; returns a callable."""
-    B, H, N, d = q.shape
-    la_causal_fwd(q, k, v, out, chunk=chunk, eps=eps, z_in=z_in, s_in=s_in, z_out=z_out, s_out=s_out,
-                  workspace=workspace, stream=stream)   # validates (and runs once)
-    inplace = (z_out is not None and z_in is not None and z_out.data_ptr() == z_in.data_ptr()) or \
-              (s_out is not None and s_in is not None and s_out.data_ptr() == s_in.data_ptr())
-    ws_bytes = la_causal_fwd_workspace(B, H, N, d, q.dtype, chunk, inplace)
-    if workspace is None and ws_bytes > 0:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    have = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    so = _strides(out) if out is not None else la_strides(0, 0, 0)
-    args = [_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v), _dtype_code(q),
-            _ptr(out), so, B, H, N, d, int(chunk), ctypes.c_float(eps),
-            _ptr(z_in), _ptr(s_in), _ptr(z_out), _ptr(s_out), _ptr(workspace), ctypes.c_size_t(have),
-            None if stream is None else _stream(stream, q.device)]
-    p = Prepared(load_library().la_causal_fwd, args, len(args) - 1, q.device, "la_causal_fwd")
-    p._keep = (q, k, v, out, z_in, s_in, z_out, s_out, workspace)
-    return p
-
-
-def prepare_noncausal_fwd(q, k, v, out, *, eps: float = 1e-6,
-                          workspace: Optional[torch.Tensor] = None, stream=None) -> Prepared:
-    """Validate and marshal a la_noncausal_fwd call once; returns a callable."""
-    B, H, N, d = q.shape
-    la_noncausal_fwd(q, k, v, out, eps=eps, workspace=workspace, stream=stream)
-    ws_bytes = la_noncausal_workspace(B, H, N, d, q.dtype)
-    if workspace is None and ws_bytes > 0:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    have = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = [_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v), _dtype_code(q),
             _ptr(out), _strides(out), B, H, N, d, ctypes.c_float(eps), _ptr(workspace), ctypes.c_size_t(have),
-            None if stream is None else _stream(stream, q.device)]
-    p = Prepared(load_library().la_noncausal_fwd, args, len(args) - 1, q.device, "la_noncausal_fwd")
-    p._keep = (q, k, v, out, workspace)
-    return p
+            _opt_stream(stream, q.device)]
+    return Prepared(load_library().la_noncausal_fwd, args, q.device, "la_noncausal_fwd", (q, k, v, out, workspace))
 
 
-def prepare_decode_step(q, k, v, z, s, out, *, eps: float = 1e-6, stream=None) -> Prepared:
-    """Validate and marshal a la_decode_step call once; returns a callable."""
-    B, H, d = q.shape
-    la_decode_step(q, k, v, z, s, out, eps=eps, stream=stream)
-    args = [_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(z), _ptr(s), _ptr(out), B, H, d,
-            ctypes.c_float(eps), None if stream is None else _stream(stream, q.device)]
-    p = Prepared(load_library().la_decode_step, args, len(args) - 1, q.device, "la_decode_step")
-    p._keep = (q, k, v, z, s, out)
-    return p
+def la_noncausal_fwd(q, k, v, out, *, eps: float = 1e-6,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Non-causal linear attention forward (la_noncausal_fwd in linattn.h)."""
+    prepare_noncausal_fwd(q, k, v, out, eps=eps, workspace=workspace, stream=stream)()
 
 
 # ---------------------------------------------------------------- conveniences
