@@ -16,30 +16,35 @@
 //    compressive memory carried from segment to segment.
 //
 // Design for CDNA4 (gfx950), in brief:
-//  * One workgroup owns (head, block of DV value columns, group of tokens).
-//    Each of its waves owns one 16-wide column tile of V, Z and out, so the
-//    fp32 state Z of that tile lives in MFMA accumulator registers for the
-//    whole token loop and never goes through LDS.
-//  * q, k, v are read with 16-byte loads, phi is applied in fp32 right after
-//    the load, and the results are written to LDS (double buffered, one
-//    barrier per chunk) in the two layouts the MFMA operands need.
-//  * All products run on 16x16 MFMA tiles.  Everything is computed in the
-//    transposed orientation (rows = value column or key token, columns =
-//    query token), so a lane's output column is one query token and the
-//    normaliser is lane-local after a 4-lane reduction.  The accumulator of
-//    one product is used directly as the operand of the next one: the score
-//    tile P^T feeds P V, and the state tile Z feeds phi(Q) Z, by ordering the
-//    contraction index the way the accumulator holds it (lane group g holds
-//    rows 4g..4g+3 of a 16-row tile).
-//  * bf16 inputs: phi(q), phi(k) and v are bf16 MFMA operands with fp32
-//    accumulation.  The score tile and the state, which are fp32 sums, are
-//    split into bf16 hi + lo parts (x = hi + lo to ~2^-17) so that rounding
-//    them to an operand type does not cost accuracy.  The normaliser uses the
-//    same rounded phi values as the numerator.  fp32 inputs use fp32 MFMA.
+//  * Causal forward, one launch: a workgroup owns (head, block of DV value
+//    columns, group of tokens).  It first computes its group's own partial
+//    state and publishes it (device-coherent stores and a per-call 64-bit tag
+//    as the flag); it then sums the published states of the earlier groups
+//    of its head (the state before the group) and runs the chunk loop from
+//    it.  Workgroups only wait for lower-indexed ones of the same XCD, which
+//    the hardware dispatches first.
+//  * Inside the chunk loop the 4 waves share the state through LDS (Z^T as
+//    bf16 hi + lo parts, S as an extra row) and each wave owns one 16-row
+//    query tile; phi(K) and V are staged in LDS per 64-token chunk.  When the
+//    group is short enough, every q, k, v load of the group is issued up
+//    front into registers, so the loop itself only stores.
+//  * All products run on 16x16 MFMA tiles in the transposed orientation
+//    (rows = value column or key token, columns = query token): the score
+//    tile P^T feeds P V directly, and the accumulator layout (lane group g
+//    holds rows 4g..4g+3) is the operand layout of the next product.  The
+//    gfx950 LDS transpose read supplies token-major operands.
+//  * bf16 inputs: phi(q), phi(k), v are bf16 operands with fp32 accumulation;
+//    the fp32 sums fed back as operands (scores, state) and phi itself where
+//    precision matters are split into bf16 hi + lo parts.  fp32 inputs use
+//    fp32 MFMA.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
 #include <math.h>
+#include <time.h>
+#include <unistd.h>
+
+#include <atomic>
 
 #include "linattn.h"
 
@@ -62,9 +67,13 @@ template <class A, class B> struct pick<false, A, B> { typedef B type; };
 template <bool F32>
 __device__ __forceinline__ float phi(float x)
 {
-    // elu(x) + 1 (alpha = 1): x + 1 above zero, e^x at or below it.
-    if (F32) return x > 0.f ? x + 1.f : expf(x);
-    return x > 0.f ? x + 1.f : __expf(x);
+    // elu(x) + 1 (alpha = 1): x + 1 above zero, e^x at or below it.  Since
+    // e^x >= x + 1 everywhere, this is max(x + 1, min(e^x, 1)): four
+    // instructions (the min is the clamp bit of v_exp_f32), and the
+    // NaN-propagating maximum keeps phi(NaN) = NaN, phi(+inf) = +inf,
+    // phi(-inf) = 0.  e^x = 2^(x log2 e) to about 2 ulp.
+    const float e = __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(x * 1.44269504088896340736f), 0.f, 1.f);
+    return __builtin_elementwise_maximum(x + 1.f, e);
 }
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -175,6 +184,11 @@ struct Args {
     int NS;       // slots per (head, column block)
     int L;        // tokens per group
     int slot0;    // slot written by group 0 of a group-state launch
+    // single-pass causal kernel: one flag per (head, column block, group),
+    // set to `epoch` (unique per call) when that group's slot is published
+    unsigned long long *flags;
+    unsigned long long epoch;
+    int wait_s;   // s_out is s_in and shared by P > 1 column blocks
 };
 
 // A slot holds one (head, column block) state in the layout of the state
@@ -188,18 +202,25 @@ constexpr int NTHR = NWAVE * WAVE;       // threads per workgroup
 __host__ __device__ constexpr int pad_of(bool f32) { return f32 ? 4 : 8; }  // 16 bytes of row padding
 
 // LDS bytes of one workgroup (one chunk stage, row major as loaded):
-//   phi(K) [C][D+pad]        (x2 for bf16: hi and lo parts)
-//   V      [C][DV+pad]       (the input values)
+//   phi(K) [C][D]            (x2 for bf16: hi and lo parts)
+//   V      [C][DV]           (the input values)
 //   Z^T    [DV+1][D+pad]     (x2 for bf16: hi and lo parts): the shared state
 //                            and S as row DV
+// bf16 phi(K) and V rows are unpadded with their 16-byte pieces XOR-swizzled
+// (see swz_piece); fp32 rows and Z^T rows carry 16 bytes of padding.
+__host__ __device__ constexpr int kv_row(bool f32, int w) { return f32 ? w + pad_of(true) : w; }
 __host__ __device__ constexpr int lds_bytes(bool f32, int d, int dv, int c)
 {
-    return ((f32 ? 1 : 2) * c * (d + pad_of(f32)) + c * (dv + pad_of(f32)) +
+    return ((f32 ? 1 : 2) * c * kv_row(f32, d) + c * kv_row(f32, dv) +
             (f32 ? 1 : 2) * (dv + 1) * (d + pad_of(f32))) * (f32 ? 4 : 2);
 }
 constexpr int LDS_LIMIT = 160 * 1024;  // per workgroup on gfx950
 // workgroups per CU the causal kernel's register budget is sized for
-__host__ __device__ constexpr int minwg_of(int d, int c) { return (d <= 64 && c == 64) ? 3 : 1; }
+__host__ __device__ constexpr int minwg_of(bool f32, int d, int c) { return (d <= 64 && c == 64) ? (f32 && d == 64 ? 2 : 3) : 1; }
+// Register-resident groups (64-token chunks): chunks a workgroup keeps in
+// registers, and the workgroups per CU its register budget is sized for.
+__host__ __device__ constexpr int res_cpg(bool f32, int d) { return d == 128 ? (f32 ? 1 : 2) : (f32 && d == 64 ? 2 : 4); }
+__host__ __device__ constexpr int res_minwg(bool f32, int d) { return (d == 128 || (f32 && d == 64)) ? 1 : 2; }
 
 template <bool F32, int D, int DV, int C>
 struct Geo {
@@ -212,13 +233,14 @@ struct Geo {
     static constexpr int SMAX = (JT + NWAVE - 1) / NWAVE;  // key-sum tiles per wave (at most)
     static constexpr int VEC = Vec<F32>::N;  // values per 16-byte vector
     static constexpr int PAD = pad_of(F32);
-    static constexpr int RK = D + PAD;     // row stride of phi(K) [token][dim] and Z^T [col][dim]
-    static constexpr int RV = DV + PAD;    // row stride of V [token][col]
+    static constexpr int RK = kv_row(F32, D);   // row stride of phi(K) [token][dim]
+    static constexpr int RV = kv_row(F32, DV);  // row stride of V [token][col]
+    static constexpr int RZ = D + PAD;          // row stride of Z^T [col][dim]
     static constexpr int NP = F32 ? 1 : 2; // copies of phi(K) and Z^T (hi, lo)
     static constexpr int OK = 0, OKL = C * RK, OV = NP * C * RK;
     static constexpr int ZR = DV + 1;                      // rows of Z^T: state, then S
-    static constexpr int OZ = OV + C * RV, OZL = OZ + ZR * RK;
-    static constexpr int NE = OZ + NP * ZR * RK;           // E elements in all
+    static constexpr int OZ = OV + C * RV, OZL = OZ + ZR * RZ;
+    static constexpr int NE = OZ + NP * ZR * RZ;           // E elements in all
     static constexpr int LDS_BYTES = lds_bytes(F32, D, DV, C);
     static_assert(NE * (int)sizeof(E) == LDS_BYTES, "LDS layout");
     // register pipeline depth: chunk c+DEPTH is loaded while chunk c is
@@ -252,19 +274,38 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 __device__ __forceinline__ bf16x8 nat8(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 __device__ __forceinline__ f32x4 nat4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 
+// bf16 [row][W] arrays of phi(K) and V: the 16-byte piece p of a row is stored
+// at piece p ^ f(row).  Both ways these arrays are read then spread over all
+// 32 LDS banks: 16-byte reads of one piece from 8 consecutive rows (the
+// scores), and the transpose reads below, which take 32 bytes (two pieces)
+// from each of 4 consecutive rows per 16 lanes.  128-byte and longer rows:
+// f = 2 (row & 3) + ((row >> 2) & 1); 64-byte rows (two per 128 bytes):
+// f = 2 ((row >> 1) & 1) + ((row >> 2) & 1).
+template <int W>
+__device__ __forceinline__ int swz_piece(int row, int piece)
+{
+    if constexpr (W == 32) return piece ^ (2 * ((row >> 1) & 1) + ((row >> 2) & 1));
+    else return piece ^ (2 * (row & 3) + ((row >> 2) & 1));
+}
+// element offset of (row, col) in a swizzled bf16 [row][W] array (col % 4 == 0)
+template <int W>
+__device__ __forceinline__ int swz(int row, int col) { return row * W + swz_piece<W>(row, col >> 3) * 8 + (col & 7); }
+
 // bf16 transposed fragment: lane (n = lane % 16, g = lane / 16) receives rows
-// s0 + 4g .. s0 + 4g + 3 of column col0 + n of a row-major array (stride ld).
+// s0 + 4g .. s0 + 4g + 3 of column col0 + n of a swizzled [row][W] array.
 // Each lane addresses row s0 + 4g + n/4, columns col0 + 4(n%4) .. +3; the
 // transpose read redistributes those 4-element pieces within every 16 lanes.
-__device__ __forceinline__ bf16x4 tr4(const bf16 *base, int ld, int s0, int col0, int n, int g)
+template <int W>
+__device__ __forceinline__ bf16x4 tr4(const bf16 *base, int s0, int col0, int n, int g)
 {
-    const bf16 *p = base + (s0 + 4 * g + (n >> 2)) * ld + col0 + 4 * (n & 3);
+    const bf16 *p = base + swz<W>(s0 + 4 * g + (n >> 2), col0 + 4 * (n & 3));
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(bf16 *)p);
 }
 // two tiles (s0 and s0 + 16) concatenated: the 8 values of one bf16 MFMA
-__device__ __forceinline__ bf16x8 tr8(const bf16 *base, int ld, int s0, int col0, int n, int g)
+template <int W>
+__device__ __forceinline__ bf16x8 tr8(const bf16 *base, int s0, int col0, int n, int g)
 {
-    const bf16x4 a = tr4(base, ld, s0, col0, n, g), b = tr4(base, ld, s0 + 16, col0, n, g);
+    const bf16x4 a = tr4<W>(base, s0, col0, n, g), b = tr4<W>(base, s0 + 16, col0, n, g);
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 // fp32 transposed fragment: rows s0 + 4g + i of column col0 + n.
@@ -321,11 +362,16 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b)
     bf16x2 v = {(bf16)a, (bf16)b};  // round to nearest even
     return __builtin_bit_cast(uint32_t, v);
 }
-// returns {hi word, lo word}
+// returns {hi word, lo word}: hi = a and b rounded to bf16 (nearest even:
+// the scores use hi alone, so it must be unbiased), lo = the remainders
+// rounded to bf16; hi + lo carries ~17 significant bits
 __device__ __forceinline__ uint2 split_pk(float a, float b)
 {
     const uint32_t hi = pk_bf16(a, b);
-    return make_uint2(hi, pk_bf16(a - bf_lo(hi), b - bf_hi(hi)));
+    // hi.low16 << 16 through v_perm_b32 (bytes: 0, 0, hi.b0, hi.b1), so that
+    // the compiler reuses hi instead of converting a again
+    const float ah = __uint_as_float(__builtin_amdgcn_perm(hi, hi, 0x05040c0cu));
+    return make_uint2(hi, pk_bf16(a - ah, b - bf_hi(hi)));
 }
 
 // Query rows of one wave tile: lane (r, g) holds query token r of the tile and
@@ -383,19 +429,27 @@ struct KVRegs {
 
     // phi(K): bf16 hi + lo (the state update sees phi(k) to ~16 bits; the
     // scores use hi), or fp32.  V: the input values unchanged.
+    // Rows at or past `nval` were loaded as zeros (reads past the end of a
+    // resource), which V keeps; phi(K) must be zero there (phi(0) = 1), which
+    // only a ragged chunk needs.
     __device__ __forceinline__ void fill(int tid, typename G_::E *st, int nval) const
+    {
+        if (nval >= C) fill_rows<false>(tid, st, C);
+        else fill_rows<true>(tid, st, nval);
+    }
+    template <bool MASK>
+    __device__ __forceinline__ void fill_rows(int tid, typename G_::E *st, int nval) const
     {
         typedef typename G_::E E;
         constexpr int VEC = G_::VEC;
-        const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int it = 0; it < G_::NK; ++it) {
             const int idx = tid + it * NTHR;
             const int row = idx / (D / VEC), vg = idx % (D / VEC);
             float f[VEC];
             Vec<F32>::to_float(k[it], f);
-            const bool ok = row < nval;
-            E *dst = st + G_::OK + row * G_::RK + vg * VEC;
+            const bool ok = !MASK || row < nval;
+            E *dst = st + G_::OK + row * G_::RK + (F32 ? vg : swz_piece<G_::RK>(row, vg)) * VEC;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) f[e] = ok ? phi<F32>(f[e]) : 0.f;
             if (F32) {
@@ -412,7 +466,7 @@ struct KVRegs {
         for (int it = 0; it < G_::NV; ++it) {
             const int idx = tid + it * NTHR;
             const int row = idx / (DV / VEC), vg = idx % (DV / VEC);
-            *reinterpret_cast<u32x4 *>(st + G_::OV + row * G_::RV + vg * VEC) = row < nval ? v[it] : z;
+            *reinterpret_cast<u32x4 *>(st + G_::OV + row * G_::RV + (F32 ? vg : swz_piece<G_::RV>(row, vg)) * VEC) = v[it];
         }
     }
 };
@@ -458,19 +512,19 @@ __device__ __forceinline__ void state_update(const typename Geo<F32, D, DV, C>::
         const bf16x8 ones = {one, one, one, one, one, one, one, one};
 #pragma unroll
         for (int sa = 0; sa < G_::TBN; sa += 2) {
-            const bf16x8 vb = tr8(v, G_::RV, 16 * sa, 16 * ct, r, g);
+            const bf16x8 vb = tr8<G_::RV>(v, 16 * sa, 16 * ct, r, g);
 #pragma unroll
             for (int m = 0; m < G_::ZT; ++m) {
                 const int jt = own_jt<JT, CT>(w, m);
-                Zown[m] = mma8(Zown[m], tr8(kh, G_::RK, 16 * sa, 16 * jt, r, g), vb);
-                Zown[m] = mma8(Zown[m], tr8(kl, G_::RK, 16 * sa, 16 * jt, r, g), vb);
+                Zown[m] = mma8(Zown[m], tr8<G_::RK>(kh, 16 * sa, 16 * jt, r, g), vb);
+                Zown[m] = mma8(Zown[m], tr8<G_::RK>(kl, 16 * sa, 16 * jt, r, g), vb);
             }
 #pragma unroll
             for (int m = 0; m < G_::SMAX; ++m) {
                 const int jt = w + NWAVE * m;
                 if (jt < JT) {
-                    Sown[m] = mma8(Sown[m], tr8(kh, G_::RK, 16 * sa, 16 * jt, r, g), ones);
-                    Sown[m] = mma8(Sown[m], tr8(kl, G_::RK, 16 * sa, 16 * jt, r, g), ones);
+                    Sown[m] = mma8(Sown[m], tr8<G_::RK>(kh, 16 * sa, 16 * jt, r, g), ones);
+                    Sown[m] = mma8(Sown[m], tr8<G_::RK>(kl, 16 * sa, 16 * jt, r, g), ones);
                 }
             }
         }
@@ -543,17 +597,27 @@ __device__ __forceinline__ void publish_state(typename Geo<F32, D, DV, C>::E *sm
         }
     };
 #pragma unroll
-    for (int m = 0; m < G_::ZT; ++m) put((16 * ct + r) * G_::RK + 16 * own_jt<JT, CT>(w, m) + 4 * g, Zown[m]);
+    for (int m = 0; m < G_::ZT; ++m) put((16 * ct + r) * G_::RZ + 16 * own_jt<JT, CT>(w, m) + 4 * g, Zown[m]);
     if (r == 0) {
 #pragma unroll
         for (int m = 0; m < G_::SMAX; ++m) {
             const int jt = w + NWAVE * m;
-            if (jt < JT) put(DV * G_::RK + 16 * jt + 4 * g, Sown[m]);
+            if (jt < JT) put(DV * G_::RZ + 16 * jt + 4 * g, Sown[m]);
         }
     }
 }
 
 template <int I> struct IC { static constexpr int value = I; };
+
+// f(IC<0>{}), ..., f(IC<N-1>{}): a loop whose index is a compile-time constant
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(IC<I>{});
+        static_for<N, I + 1>(f);
+    }
+}
 
 // ------------------------------------------------------------------ kernels
 // Partial state of one token group: A_g = phi(K_g)^T V_g (column block p),
@@ -566,7 +630,8 @@ __global__ void __launch_bounds__(NTHR) k_group_state(const Args a)
     typedef typename G_::E E;
     __shared__ __attribute__((aligned(16))) char smem_raw[G_::LDS_BYTES];
     E *st = reinterpret_cast<E *>(smem_raw);
-    const int tid = threadIdx.x, w = tid / WAVE, lane = tid % WAVE, r = lane % 16, g = lane / 16;
+    const int tid = threadIdx.x, lane = tid % WAVE, r = lane % 16, g = lane / 16;
+    const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);   // wave-uniform
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
     const int p = wg % a.P, rest = wg / a.P, grp = rest % a.G, bh = rest / a.G;
     const int b = bh / a.H, h = bh % a.H;
@@ -678,39 +743,103 @@ __global__ void __launch_bounds__(256) k_slots(const Args a, int nslots, int mod
     }
 }
 
-// Chunk-sequential forward of one token group (mode 3 inside the group).
-// Wave w owns query tile w (and 2*NWAVE-1-w for 128-token chunks):
-// CAUSAL: out_t = [phi(q_t) Z_prev + sum_{s<=t in chunk} P_ts v_s] /
-//                 [phi(q_t) . S_prev + sum_{s<=t in chunk} P_ts + eps],
-//         P = phi(Q_c) phi(K_c)^T; then Z += phi(K_c)^T V_c, S += phi(K_c)^T 1
-//         on the owned state tiles, published to LDS for the next chunk.  The
-//         group starts from its slot (or z_in/s_in when there is one group);
-//         the last group writes z_out/s_out.
-// !CAUSAL (non-causal apply): out_t = phi(q_t) Z / (phi(q_t) . S + eps) with
-//         the reduced global state.
-// The normaliser comes out of the same MFMAs: S is an extra row of Z^T and an
-// all-ones row is an extra row of V^T, so an extra 16-row output tile (whose
-// other rows are zero operands) accumulates phi(q_t) . S_prev + sum_s P_ts in
-// its first row.
-// Loaded registers are consumed at one point per chunk (before the first
-// barrier); chunk c+DEPTH is requested right after it.
-template <bool F32, int D, int DV, int C, bool CAUSAL>
-__global__ void __launch_bounds__(NTHR, minwg_of(D, C)) k_chunk_fwd(const Args a)
+// ---- device-coherent slot traffic between workgroups of one call.  The
+// slots and flags are read and written with the sc0 sc1 cache policy (what
+// device-scope atomics use on gfx950), so a value stored by a workgroup on one
+// XCD is seen by a workgroup on another XCD without flushing any cache.
+constexpr int CPOL_DEVICE = 1 | 16;   // sc0 | sc1
+__device__ __forceinline__ void dstore16(rsrc_t r, uint32_t off, f32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, CPOL_DEVICE);
+}
+__device__ __forceinline__ f32x4 dload16(rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL_DEVICE));
+}
+
+// Slot of one (head, column block, token group) in the single-pass kernel:
+// the Z tiles as the lanes hold them (lane-contiguous 16-byte pieces, so a
+// wave moves 1 KB per instruction), then S [D].
+template <int D, int DV> struct FSlot {
+    static constexpr int ZT = (D / 16) * (DV / 16) / NWAVE;
+    static constexpr int ZF = D * DV;                 // floats of Z
+    static constexpr int BYTES = (ZF + D) * 4;
+    __device__ static uint32_t zoff(int w, int m, int lane) { return (uint32_t)(((w * ZT + m) * WAVE + lane) * 16); }
+    __device__ static uint32_t soff(int jt, int g) { return (uint32_t)((ZF + 16 * jt + 4 * g) * 4); }
+};
+
+// Spin limit of a flag wait (each poll sleeps ~1 us): a call whose flags never
+// arrive (a bug, or memory not meant for this call) ends instead of hanging.
+constexpr int SPIN_LIMIT = 1 << 20;
+
+// Wait until base[i * stride] == epoch for i < n (lane i watches entry i, in
+// rounds of 64 entries).  Every lane of the wave runs this.
+__device__ __forceinline__ void wait_flags(const unsigned long long *base, int stride, int n,
+                                           unsigned long long epoch, int lane)
+{
+    for (int i0 = 0; i0 < n; i0 += WAVE) {
+        const int i = i0 + lane;
+        const unsigned long long *f = base + (int64_t)(i < n ? i : 0) * stride;
+        for (int spin = 0; spin < SPIN_LIMIT; ++spin) {
+            const bool ok = i >= n || __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
+            if (__all(ok)) break;
+            __builtin_amdgcn_s_sleep(16);
+        }
+    }
+}
+
+// The causal forward of one token group in a single pass (modes 3 and 4 of
+// "How to accelerate causal linear attention" fused):
+//  A. the group's own partial state A_g = phi(K_g)^T V_g, S_g = sum phi(k)
+//     (group 0 adds the carried-in state), published to the group's slot
+//     unless the group is the last one;
+//  B. its starting state: the carried-in state (group 0) or the sum of the
+//     published slots of all earlier groups of the same (head, column block);
+//  C. the chunk loop (mode 3): out_t = [phi(q_t) Z_prev + sum_{s<=t in chunk}
+//     P_ts v_s] / [phi(q_t) . S_prev + sum_{s<=t in chunk} P_ts + eps],
+//     P = phi(Q_c) phi(K_c)^T, then Z += phi(K_c)^T V_c, S += phi(K_c)^T 1 on
+//     the owned state tiles, published to LDS for the next chunk; the last
+//     group writes z_out/s_out.
+// MODE_STATE (no output) stops after A and B: the last group writes the sum.
+// MODE_APPLY (non-causal): out_t = phi(q_t) Z / (phi(q_t) . S + eps) with the
+// reduced global state.
+// Waiting in B is only on groups with lower workgroup indices of the same XCD
+// (the logical index order is the dispatch order within an XCD), so the
+// groups a workgroup waits for have been dispatched before it.
+// The normaliser comes out of the same MFMAs as the numerator: S is an extra
+// row of Z^T and an all-ones row is an extra row of V^T, so an extra 16-row
+// output tile (whose other rows are zero operands) accumulates
+// phi(q_t) . S_prev + sum_s P_ts in its first row.
+constexpr int MODE_OUT = 0, MODE_STATE = 1, MODE_APPLY = 2;
+
+// CPG > 0 (MODE_OUT only): the group has at most CPG chunks, and all of its
+// q, k, v loads are issued at the start into registers; steps A and C then
+// run without waiting for memory, and the chunk loop issues stores only.
+// CPG = 0: loads are streamed one chunk ahead.
+template <bool F32, int D, int DV, int C, int MODE, int CPG>
+__global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F32, D, C)) k_chunk_fwd(const Args a)
 {
     typedef Geo<F32, D, DV, C> G_;
     typedef typename G_::E E;
+    typedef FSlot<D, DV> FS;
     constexpr int JT = G_::JT, CT = G_::CT, TBN = G_::TBN, BPW = G_::BPW, NQV = G_::NQV;
     constexpr int DEPTH = G_::DEPTH;
     constexpr int ES = F32 ? 4 : 2;
     constexpr int SL = Slot<D, DV>::SIZE;
+    constexpr bool CAUSAL = MODE != MODE_APPLY;
+    constexpr bool RES = CPG > 0;
+    constexpr int NR = RES ? CPG : DEPTH;   // chunk register sets
+    static_assert(!RES || MODE == MODE_OUT, "resident chunks: causal with output only");
     typedef typename pick<F32, f32x4, bf16x8>::type QOp;   // one MFMA operand of phi(q)
     __shared__ __attribute__((aligned(16))) char smem_raw[G_::LDS_BYTES];
     E *sm = reinterpret_cast<E *>(smem_raw);
 
-    const int tid = threadIdx.x, w = tid / WAVE, lane = tid % WAVE, r = lane % 16, g = lane / 16;
+    const int tid = threadIdx.x, lane = tid % WAVE, r = lane % 16, g = lane / 16;
+    const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);   // wave-uniform
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
     const int p = wg % a.P, rest = wg / a.P, grp = rest % a.G, bh = rest / a.G;
     const int b = bh / a.H, h = bh % a.H;
+    const int hp = bh * a.P + p;
     const int t_begin = grp * a.L, t_end = min(t_begin + a.L, a.N);
     const RowView qv{(const char *)a.q + (b * a.sqb + h * a.sqh) * ES, a.sqn * ES, (a.N - 1) * a.sqn * ES + D * ES};
     const RowView kv{(const char *)a.k + (b * a.skb + h * a.skh) * ES, a.skn * ES, (a.N - 1) * a.skn * ES + D * ES};
@@ -727,40 +856,100 @@ __global__ void __launch_bounds__(NTHR, minwg_of(D, C)) k_chunk_fwd(const Args a
         QRegs<F32, D>::offsets(qo[bi], 16 * tbs[bi] + r, qv.rs, g);
         oo[bi] = (uint32_t)((16 * tbs[bi] + r) * ov.rs + 16 * g);
     }
-
-    // ---- starting state: owned tiles, published to LDS
-    f32x4 Zown[G_::ZT], Sown[G_::SMAX];
-    if (CAUSAL) {
-        if (a.NS > 0) {
-            const float *sl = a.part + ((int64_t)(bh * a.P + p) * a.NS + grp) * SL;
-            load_owned<JT, CT, G_::ZT, G_::SMAX>(sl, DV, sl + Slot<D, DV>::Z, w, r, g, Zown, Sown);
-        } else {
-            load_owned<JT, CT, G_::ZT, G_::SMAX>(a.z_in ? a.z_in + (int64_t)bh * D * D + p * DV : nullptr, D,
-                                                 a.s_in ? a.s_in + (int64_t)bh * D : nullptr, w, r, g, Zown, Sown);
-        }
-    } else {
-        const float *sl = a.fin + (int64_t)(bh * a.P + p) * SL;
-        load_owned<JT, CT, G_::ZT, G_::SMAX>(sl, DV, sl + Slot<D, DV>::Z, w, r, g, Zown, Sown);
-    }
-    publish_state<F32, D, DV, C>(sm, w, r, g, Zown, Sown);
-
-    KVRegs<F32, D, DV, C> R[DEPTH];
-    QRegs<F32, D> Q[DEPTH][BPW];
     const int nch = (t_end - t_begin + C - 1) / C;
+
+    f32x4 Zown[G_::ZT], Sown[G_::SMAX];
+    auto zero_state = [&]() {
+#pragma unroll
+        for (int m = 0; m < G_::ZT; ++m) Zown[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < G_::SMAX; ++m) Sown[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    };
+
+    // chunk registers and loads
+    KVRegs<F32, D, DV, C> R[NR];
+    QRegs<F32, D> Q[NR][BPW];
     // Every memory access is issued unconditionally (chunks past the group
     // read an empty resource; stores of rows outside the group use an
     // out-of-range offset), so the compiler can count outstanding accesses
     // and wait only for the chunk it is about to use.
-    auto issue = [&](int ch, auto slot) {
-        constexpr int S_ = decltype(slot)::value;
+    auto issue_kv = [&](int ch, auto slot) {
         const int t0 = t_begin + ch * C;
-        const bool live = ch < nch;
-        if (CAUSAL) R[S_].load(kv.at(t0, live), vv.at(t0, live), ko, vo);
-        const rsrc_t qr = qv.at(t0, live);
+        if (CAUSAL) R[decltype(slot)::value].load(kv.at(t0, ch < nch), vv.at(t0, ch < nch), ko, vo);
+    };
+    auto issue_q = [&](int ch, auto slot) {
+        const rsrc_t qr = qv.at(t_begin + ch * C, ch < nch);
 #pragma unroll
-        for (int bi = 0; bi < BPW; ++bi) Q[S_][bi].load(qr, qo[bi]);
+        for (int bi = 0; bi < BPW; ++bi) Q[decltype(slot)::value][bi].load(qr, qo[bi]);
+    };
+    auto issue = [&](int ch, auto slot) {
+        issue_kv(ch, slot);
+        issue_q(ch, slot);
     };
 
+    // ---- slot helpers: add the published slots of groups 0..n-1 of this
+    // (head, column block); write z_out / s_out from (Zown + Zadd, Sown + Sadd)
+    auto add_slots = [&](int n) {
+        wait_flags(a.flags + (int64_t)hp * a.G, 1, n, a.epoch, lane);
+        constexpr int LB = (G_::ZT + G_::SMAX) <= 5 ? 4 : 2;   // slots in flight
+        const char *base = (const char *)a.part + (size_t)hp * a.G * FS::BYTES;
+        for (int g0 = 0; g0 < n; g0 += LB) {
+            f32x4 tz[LB][G_::ZT], ts[LB][G_::SMAX];
+#pragma unroll
+            for (int u = 0; u < LB; ++u) {
+                const bool live = g0 + u < n;
+                const rsrc_t sr = make_rsrc(base + (size_t)(live ? g0 + u : 0) * FS::BYTES, live ? FS::BYTES : 0);
+#pragma unroll
+                for (int m = 0; m < G_::ZT; ++m) tz[u][m] = dload16(sr, FS::zoff(w, m, lane));
+#pragma unroll
+                for (int m = 0; m < G_::SMAX; ++m) {
+                    const int jt = w + NWAVE * m;
+                    ts[u][m] = dload16(sr, (r == 0 && jt < JT) ? FS::soff(jt, g) : OFF_NONE);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < LB; ++u) {
+#pragma unroll
+                for (int m = 0; m < G_::ZT; ++m) Zown[m] += tz[u][m];
+#pragma unroll
+                for (int m = 0; m < G_::SMAX; ++m) Sown[m] += ts[u][m];
+            }
+        }
+    };
+    // this group's slot <- (za, sa), plus (Zown, Sown) if `add`
+    auto publish_slot = [&](const f32x4 *za, const f32x4 *sa, bool add) {
+        const rsrc_t sr = make_rsrc((const char *)a.part + (size_t)(hp * a.G + grp) * FS::BYTES, FS::BYTES);
+#pragma unroll
+        for (int m = 0; m < G_::ZT; ++m) dstore16(sr, FS::zoff(w, m, lane), add ? za[m] + Zown[m] : za[m]);
+#pragma unroll
+        for (int m = 0; m < G_::SMAX; ++m) {
+            const int jt = w + NWAVE * m;
+            dstore16(sr, (r == 0 && jt < JT) ? FS::soff(jt, g) : OFF_NONE, add ? sa[m] + Sown[m] : sa[m]);
+        }
+    };
+    // all of the workgroup's memory accesses so far are complete, then the flag
+    auto set_flag = [&]() {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_store(a.flags + (int64_t)hp * a.G + grp, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto store_final = [&](const f32x4 *Zadd, const f32x4 *Sadd) {
+        // s_out is written by the last column block; with in-place states it
+        // first waits until group 0 of every column block has read s_in
+        const bool s_writer = p == a.P - 1;
+        if (a.wait_s && s_writer) wait_flags(a.flags + (int64_t)bh * a.P * a.G, a.G, a.P, a.epoch, lane);
+        f32x4 zf[G_::ZT], sf[G_::SMAX];
+#pragma unroll
+        for (int m = 0; m < G_::ZT; ++m) zf[m] = Zadd ? Zown[m] + Zadd[m] : Zown[m];
+#pragma unroll
+        for (int m = 0; m < G_::SMAX; ++m) sf[m] = Sadd ? Sown[m] + Sadd[m] : Sown[m];
+        store_owned<JT, CT, G_::ZT, G_::SMAX>(a.z_out ? a.z_out + (int64_t)bh * D * D + p * DV : nullptr, D,
+                                              (a.s_out && s_writer) ? a.s_out + (int64_t)bh * D : nullptr,
+                                              w, r, g, zf, sf);
+    };
+
+    // ---- per-chunk pieces of the output
     // all-ones row of V^T (lane row 0 of the extra tile), a constant operand
     QOp ones_row;
     {
@@ -774,151 +963,167 @@ __global__ void __launch_bounds__(NTHR, minwg_of(D, C)) k_chunk_fwd(const Args a
             ones_row = *reinterpret_cast<QOp *>(&o8);
         }
     }
+    // phi(q) of one query tile as MFMA operands (bf16: hi + lo).  No mask is
+    // needed: a query row feeds only its own output row, which is not stored
+    // past the end.
+    auto phi_q = [&](const QRegs<F32, D> &qr, QOp *qh, QOp *ql) {
+#pragma unroll
+        for (int u = 0; u < NQV; ++u) {
+            float f[Vec<F32>::N];
+            Vec<F32>::to_float(qr.raw[u], f);
+#pragma unroll
+            for (int e = 0; e < Vec<F32>::N; ++e) f[e] = phi<F32>(f[e]);
+            if (F32) {
+                f32x4 x = {f[0], f[1], f[2], f[3]};
+                qh[u] = *reinterpret_cast<QOp *>(&x);
+            } else {
+                u32x4 hi, lo;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { const uint2 sp_ = split_pk(f[2 * e], f[2 * e + 1]); hi[e] = sp_.x; lo[e] = sp_.y; }
+                qh[u] = __builtin_bit_cast(QOp, hi);
+                ql[u] = __builtin_bit_cast(QOp, lo);
+            }
+        }
+    };
+    // o += phi(Q_tile) Z_shared (Z^T and S from LDS): the value tiles and, in
+    // the extra tile, phi(q) . S
+    // (In the extra tile every lane reads the S row: all 16 rows of that tile
+    // then hold phi(q) . S, and row 0, the one that is read, also collects
+    // the row sums of P.)
+    auto inter = [&](f32x4 *o, const QOp *qh, const QOp *ql) {
+        if (F32) {
+            const float *zf = reinterpret_cast<const float *>(sm) + G_::OZ;
+#pragma unroll
+            for (int ct = 0; ct <= CT; ++ct)
+#pragma unroll
+                for (int u = 0; u < NQV; ++u) {
+                    const f32x4 za = nat4(zf + (ct < CT ? 16 * ct + r : DV) * G_::RZ + 16 * u + 4 * g);
+                    o[ct] = mma1(o[ct], za, *reinterpret_cast<const f32x4 *>(&qh[u]));
+                }
+        } else {
+            const bf16 *zh = reinterpret_cast<const bf16 *>(sm) + G_::OZ;
+            const bf16 *zl = reinterpret_cast<const bf16 *>(sm) + G_::OZL;
+#pragma unroll
+            for (int ct = 0; ct <= CT; ++ct) {
+                const int zo = (ct < CT ? 16 * ct + r : DV) * G_::RZ + 8 * g;
+                bf16x8 a_hi[NQV], a_lo[NQV];
+#pragma unroll
+                for (int u = 0; u < NQV; ++u) { a_hi[u] = nat8(zh + zo + 32 * u); a_lo[u] = nat8(zl + zo + 32 * u); }
+#pragma unroll
+                for (int u = 0; u < NQV; ++u) {
+                    const bf16x8 qh8 = *reinterpret_cast<const bf16x8 *>(&qh[u]);
+                    const bf16x8 ql8 = *reinterpret_cast<const bf16x8 *>(&ql[u]);
+                    o[ct] = mma8(o[ct], a_hi[u], qh8);
+                    o[ct] = mma8(o[ct], a_lo[u], qh8);
+                    o[ct] = mma8(o[ct], a_hi[u], ql8);
+                }
+            }
+        }
+    };
+    // o += intra-chunk term of query tile tb over key tiles sa <= tb: scores
+    // P^T (rows = keys, columns = queries) feed P V as the B operand directly;
+    // the extra tile gets the row sums of P
+    auto intra = [&](f32x4 *o, const QOp *qh, int tb) {
+        if (F32) {
+            const float *kf = reinterpret_cast<const float *>(sm) + G_::OK;
+            const float *vf = reinterpret_cast<const float *>(sm) + G_::OV;
+            for (int sa = 0; sa <= tb; ++sa) {
+                f32x4 pt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int u = 0; u < NQV; ++u)
+                    pt = mma1(pt, nat4(kf + (16 * sa + r) * G_::RK + 16 * u + 4 * g), *reinterpret_cast<const f32x4 *>(&qh[u]));
+                if (sa == tb) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) if (4 * g + i > r) pt[i] = 0.f;
+                }
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) o[ct] = mma1(o[ct], trf(vf, G_::RV, 16 * sa, 16 * ct, r, g), pt);
+                o[CT] = mma1(o[CT], *reinterpret_cast<const f32x4 *>(&ones_row), pt);
+            }
+        } else {
+            const bf16 *kb = reinterpret_cast<const bf16 *>(sm) + G_::OK;
+            const bf16 *vb = reinterpret_cast<const bf16 *>(sm) + G_::OV;
+            const bf16 zr = (bf16)0.f;
+            const bf16x8 ones8 = *reinterpret_cast<const bf16x8 *>(&ones_row);
+            for (int sa = 0; sa <= tb; sa += 2) {
+                const bool two = sa + 1 <= tb;
+                f32x4 pt0 = {0.f, 0.f, 0.f, 0.f}, pt1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int u = 0; u < NQV; ++u) {
+                    const bf16x8 qh8 = *reinterpret_cast<const bf16x8 *>(&qh[u]);
+                    pt0 = mma8(pt0, nat8(kb + swz<G_::RK>(16 * sa + r, 32 * u + 8 * g)), qh8);
+                    if (two) pt1 = mma8(pt1, nat8(kb + swz<G_::RK>(16 * sa + 16 + r, 32 * u + 8 * g)), qh8);
+                }
+                // causal mask inside the diagonal tile: key 4g+i > query r
+                if (sa == tb) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) if (4 * g + i > r) pt0[i] = 0.f;
+                }
+                if (two && sa + 1 == tb) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) if (4 * g + i > r) pt1[i] = 0.f;
+                }
+                u32x4 phw = {0u, 0u, 0u, 0u}, plw = {0u, 0u, 0u, 0u};
+                { const uint2 sp_ = split_pk(pt0[0], pt0[1]); phw[0] = sp_.x; plw[0] = sp_.y; }
+                { const uint2 sp_ = split_pk(pt0[2], pt0[3]); phw[1] = sp_.x; plw[1] = sp_.y; }
+                if (two) {
+                    { const uint2 sp_ = split_pk(pt1[0], pt1[1]); phw[2] = sp_.x; plw[2] = sp_.y; }
+                    { const uint2 sp_ = split_pk(pt1[2], pt1[3]); phw[3] = sp_.x; plw[3] = sp_.y; }
+                }
+                const bf16x8 bh8 = __builtin_bit_cast(bf16x8, phw);
+                const bf16x8 bl8 = __builtin_bit_cast(bf16x8, plw);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    bf16x4 va0 = tr4<G_::RV>(vb, 16 * sa, 16 * ct, r, g);
+                    bf16x4 va1 = {zr, zr, zr, zr};
+                    if (two) va1 = tr4<G_::RV>(vb, 16 * sa + 16, 16 * ct, r, g);
+                    const bf16x8 a8 = __builtin_shufflevector(va0, va1, 0, 1, 2, 3, 4, 5, 6, 7);
+                    o[ct] = mma8(o[ct], a8, bh8);
+                    o[ct] = mma8(o[ct], a8, bl8);
+                }
+                o[CT] = mma8(o[CT], ones8, bh8);
+                o[CT] = mma8(o[CT], ones8, bl8);
+            }
+        }
+    };
+    // out rows of query tile tb in chunk ch = value tiles / (normaliser + eps)
+    auto finish = [&](const f32x4 *o, int ch, int tb) {
+        const int t0 = t_begin + ch * C;
+        const int nval = min(C, t_end - t0);
+        const int tq = 16 * tb + r;
+        // normaliser of query r: row 0 of the extra tile, held by lane r
+        const float den = __shfl(o[CT][0], r) + a.eps;
+        const float inv = __builtin_amdgcn_rcpf(den);   // within 1 ulp
+        const rsrc_t orr = ov.at(t0);
+        const uint32_t obase = tq < nval ? (uint32_t)(tq * ov.rs + 16 * g) : OFF_NONE;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) bstore16(orr, tq < nval ? obase + 64 * ct : OFF_NONE, o[ct] * inv);
+    };
+    auto zero_o = [&](f32x4 *o) {
+#pragma unroll
+        for (int ct = 0; ct <= CT; ++ct) o[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    };
 
+    // ---- one chunk of the streaming loop (and of the non-causal readout):
+    // stage K, V and phi(q); the output rows; the state update
     auto step = [&](int ch, auto slot) {
         constexpr int S_ = decltype(slot)::value;
         const int t0 = t_begin + ch * C;
-        const int nval = max(0, min(C, t_end - t0));
-        // ---- consume the registers of chunk ch: K, V into the stage, phi(q)
-        if (CAUSAL) R[S_].fill(tid, sm, nval);
+        if (CAUSAL) R[S_].fill(tid, sm, min(C, t_end - t0));
         QOp qhi[BPW][NQV], qlo[BPW][NQV];
 #pragma unroll
-        for (int bi = 0; bi < BPW; ++bi) {
-            const bool valid = 16 * tbs[bi] + r < nval;
-#pragma unroll
-            for (int u = 0; u < NQV; ++u) {
-                float f[Vec<F32>::N];
-                Vec<F32>::to_float(Q[S_][bi].raw[u], f);
-#pragma unroll
-                for (int e = 0; e < Vec<F32>::N; ++e) f[e] = valid ? phi<F32>(f[e]) : 0.f;
-                if (F32) {
-                    f32x4 x = {f[0], f[1], f[2], f[3]};
-                    qhi[bi][u] = *reinterpret_cast<QOp *>(&x);
-                } else {
-                    u32x4 hi, lo;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) { const uint2 sp_ = split_pk(f[2 * e], f[2 * e + 1]); hi[e] = sp_.x; lo[e] = sp_.y; }
-                    qhi[bi][u] = __builtin_bit_cast(QOp, hi);
-                    qlo[bi][u] = __builtin_bit_cast(QOp, lo);
-                }
-            }
-        }
+        for (int bi = 0; bi < BPW; ++bi) phi_q(Q[S_][bi], qhi[bi], qlo[bi]);
         if (CAUSAL || ch == 0) __syncthreads();   // stage and published state visible
         // ---- request chunk ch + DEPTH into the registers just consumed
-        issue(ch + DEPTH, slot);
-
+        if constexpr (!RES) issue(ch + DEPTH, slot);
 #pragma unroll
         for (int bi = 0; bi < BPW; ++bi) {
-            const int tb = tbs[bi];
-            const int tq = 16 * tb + r;
             f32x4 o[CT + 1];   // value tiles, then the normaliser tile
-#pragma unroll
-            for (int ct = 0; ct <= CT; ++ct) o[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            if (F32) {
-                const float *kf = reinterpret_cast<const float *>(sm) + G_::OK;
-                const float *vf = reinterpret_cast<const float *>(sm) + G_::OV;
-                const float *zf = reinterpret_cast<const float *>(sm) + G_::OZ;
-                // inter-chunk term (and phi(q) . S in the extra tile)
-#pragma unroll
-                for (int ct = 0; ct <= CT; ++ct)
-#pragma unroll
-                    for (int u = 0; u < NQV; ++u) {
-                        f32x4 za = {0.f, 0.f, 0.f, 0.f};
-                        if (ct < CT || r == 0) za = nat4(zf + (16 * ct + r) * G_::RK + 16 * u + 4 * g);
-                        o[ct] = mma1(o[ct], za, *reinterpret_cast<const f32x4 *>(&qhi[bi][u]));
-                    }
-                if (CAUSAL) {
-                    for (int sa = 0; sa <= tb; ++sa) {
-                        f32x4 pt = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int u = 0; u < NQV; ++u)
-                            pt = mma1(pt, nat4(kf + (16 * sa + r) * G_::RK + 16 * u + 4 * g),
-                                      *reinterpret_cast<const f32x4 *>(&qhi[bi][u]));
-                        if (sa == tb) {
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) if (4 * g + i > r) pt[i] = 0.f;
-                        }
-#pragma unroll
-                        for (int ct = 0; ct < CT; ++ct)
-                            o[ct] = mma1(o[ct], trf(vf, G_::RV, 16 * sa, 16 * ct, r, g), pt);
-                        o[CT] = mma1(o[CT], *reinterpret_cast<const f32x4 *>(&ones_row), pt);
-                    }
-                }
-            } else {
-                const bf16 *kb = reinterpret_cast<const bf16 *>(sm) + G_::OK;
-                const bf16 *vb = reinterpret_cast<const bf16 *>(sm) + G_::OV;
-                const bf16 *zh = reinterpret_cast<const bf16 *>(sm) + G_::OZ;
-                const bf16 *zl = reinterpret_cast<const bf16 *>(sm) + G_::OZL;
-                // inter-chunk term with Z and phi(q) as hi + lo (and phi(q) . S)
-#pragma unroll
-                for (int ct = 0; ct <= CT; ++ct) {
-                    const int zo = (16 * ct + r) * G_::RK + 8 * g;
-#pragma unroll
-                    for (int u = 0; u < NQV; ++u) {
-                        const bf16x8 qh8 = *reinterpret_cast<const bf16x8 *>(&qhi[bi][u]);
-                        const bf16x8 ql8 = *reinterpret_cast<const bf16x8 *>(&qlo[bi][u]);
-                        bf16x8 a_hi = {}, a_lo = {};
-                        if (ct < CT || r == 0) { a_hi = nat8(zh + zo + 32 * u); a_lo = nat8(zl + zo + 32 * u); }
-                        o[ct] = mma8(o[ct], a_hi, qh8);
-                        o[ct] = mma8(o[ct], a_lo, qh8);
-                        o[ct] = mma8(o[ct], a_hi, ql8);
-                    }
-                }
-                if (CAUSAL) {
-                    // intra-chunk term over key tiles sa <= tb: scores P^T (rows =
-                    // keys, columns = queries) feed P V as the B operand directly
-                    const bf16 zr = (bf16)0.f;
-                    const bf16x8 ones8 = *reinterpret_cast<const bf16x8 *>(&ones_row);
-                    for (int sa = 0; sa <= tb; sa += 2) {
-                        const bool two = sa + 1 <= tb;
-                        f32x4 pt0 = {0.f, 0.f, 0.f, 0.f}, pt1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int u = 0; u < NQV; ++u) {
-                            const bf16x8 qh8 = *reinterpret_cast<const bf16x8 *>(&qhi[bi][u]);
-                            pt0 = mma8(pt0, nat8(kb + (16 * sa + r) * G_::RK + 32 * u + 8 * g), qh8);
-                            if (two) pt1 = mma8(pt1, nat8(kb + (16 * sa + 16 + r) * G_::RK + 32 * u + 8 * g), qh8);
-                        }
-                        // causal mask inside the diagonal tile: key 4g+i > query r
-                        if (sa == tb) {
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) if (4 * g + i > r) pt0[i] = 0.f;
-                        }
-                        if (two && sa + 1 == tb) {
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) if (4 * g + i > r) pt1[i] = 0.f;
-                        }
-                        u32x4 phw = {0u, 0u, 0u, 0u}, plw = {0u, 0u, 0u, 0u};
-                        { const uint2 sp_ = split_pk(pt0[0], pt0[1]); phw[0] = sp_.x; plw[0] = sp_.y; }
-                        { const uint2 sp_ = split_pk(pt0[2], pt0[3]); phw[1] = sp_.x; plw[1] = sp_.y; }
-                        if (two) {
-                            { const uint2 sp_ = split_pk(pt1[0], pt1[1]); phw[2] = sp_.x; plw[2] = sp_.y; }
-                            { const uint2 sp_ = split_pk(pt1[2], pt1[3]); phw[3] = sp_.x; plw[3] = sp_.y; }
-                        }
-                        const bf16x8 bh8 = __builtin_bit_cast(bf16x8, phw);
-                        const bf16x8 bl8 = __builtin_bit_cast(bf16x8, plw);
-#pragma unroll
-                        for (int ct = 0; ct < CT; ++ct) {
-                            bf16x4 va0 = tr4(vb, G_::RV, 16 * sa, 16 * ct, r, g);
-                            bf16x4 va1 = {zr, zr, zr, zr};
-                            if (two) va1 = tr4(vb, G_::RV, 16 * sa + 16, 16 * ct, r, g);
-                            const bf16x8 a8 = __builtin_shufflevector(va0, va1, 0, 1, 2, 3, 4, 5, 6, 7);
-                            o[ct] = mma8(o[ct], a8, bh8);
-                            o[ct] = mma8(o[ct], a8, bl8);
-                        }
-                        o[CT] = mma8(o[CT], ones8, bh8);
-                        o[CT] = mma8(o[CT], ones8, bl8);
-                    }
-                }
-            }
-            // normaliser of query r: row 0 of the extra tile, held by lane r
-            const float den = __shfl(o[CT][0], r) + a.eps;
-            const float inv = 1.f / den;
-            const rsrc_t orr = ov.at(t0);
-            const uint32_t obase = tq < nval ? oo[bi] : OFF_NONE;
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) bstore16(orr, tq < nval ? obase + 64 * ct : OFF_NONE, o[ct] * inv);
+            zero_o(o);
+            inter(o, qhi[bi], qlo[bi]);
+            if (CAUSAL) intra(o, qhi[bi], tbs[bi]);
+            finish(o, ch, tbs[bi]);
         }
-
         if (CAUSAL) {
             state_update<F32, D, DV, C>(sm, w, r, g, Zown, Sown);
             __syncthreads();   // every wave is done with this chunk's stage and state
@@ -926,17 +1131,140 @@ __global__ void __launch_bounds__(NTHR, minwg_of(D, C)) k_chunk_fwd(const Args a
         }
     };
 
-    issue(0, IC<0>{});
-    if (DEPTH == 2) issue(1, IC<DEPTH - 1>{});
-    for (int ch = 0; ch < nch; ch += DEPTH) {   // an odd count runs one empty step
-        step(ch, IC<0>{});
-        if (DEPTH == 2) step(ch + 1, IC<DEPTH - 1>{});
+    if constexpr (MODE == MODE_APPLY) {
+        const float *sl = a.fin + (int64_t)hp * SL;
+        load_owned<JT, CT, G_::ZT, G_::SMAX>(sl, DV, sl + Slot<D, DV>::Z, w, r, g, Zown, Sown);
+        publish_state<F32, D, DV, C>(sm, w, r, g, Zown, Sown);
+        issue(0, IC<0>{});
+        for (int ch = 0; ch < nch; ++ch) step(ch, IC<0>{});
+        return;
+    } else {
+        f32x4 Zin[G_::ZT], Sin[G_::SMAX];
+        if (grp == 0) {
+            load_owned<JT, CT, G_::ZT, G_::SMAX>(a.z_in ? a.z_in + (int64_t)bh * D * D + p * DV : nullptr, D,
+                                                 a.s_in ? a.s_in + (int64_t)bh * D : nullptr, w, r, g, Zin, Sin);
+        }
+        const bool last = grp == a.G - 1;
+        if constexpr (RES) {
+            // ================= register-resident group: A, B, C with every load
+            // of the group held in registers.  k and v stream two chunks
+            // ahead through A (loads only, so the compiler waits for exactly
+            // the chunk in use); q is requested after the last k and v; the
+            // chunk loop C then issues stores only.
+            constexpr int KV0 = CPG < 2 ? CPG : 2;   // k, v chunks requested up front
+            auto issue_rest = [&]() {   // k, v of the remaining chunks, then all q
+                static_for<CPG>([&](auto c) { if constexpr (c.value >= KV0) issue_kv(c.value, c); });
+                static_for<CPG>([&](auto c) { issue_q(c.value, c); });
+            };
+            static_for<KV0>([&](auto c) { issue_kv(c.value, c); });
+            if (!last) {
+                if (grp == 0) {
+#pragma unroll
+                    for (int m = 0; m < G_::ZT; ++m) Zown[m] = Zin[m];
+#pragma unroll
+                    for (int m = 0; m < G_::SMAX; ++m) Sown[m] = Sin[m];
+                } else {
+                    zero_state();
+                }
+                static_for<CPG>([&](auto cc) {
+                    constexpr int c = decltype(cc)::value;
+                    // k, v of chunk c + 2 (q after the last of them) while chunk c is used
+                    if constexpr (c + 2 < CPG) issue_kv(c + 2, IC<c + 2>{});
+                    if constexpr (c == (CPG >= 3 ? CPG - 3 : 0))
+                        static_for<CPG>([&](auto j) { issue_q(j.value, j); });
+                    if (c < nch) {
+                        R[c].fill(tid, sm, min(C, t_end - (t_begin + c * C)));
+                        __syncthreads();
+                        state_update<F32, D, DV, C>(sm, w, r, g, Zown, Sown);
+                        __syncthreads();
+                    }
+                });
+                publish_slot(Zown, Sown, false);
+                set_flag();
+            } else {
+                issue_rest();
+                if (grp == 0 && a.wait_s) set_flag();   // only signals that z_in / s_in have been read
+            }
+            // ---- B: the state before the group
+            if (grp == 0) {
+#pragma unroll
+                for (int m = 0; m < G_::ZT; ++m) Zown[m] = Zin[m];
+#pragma unroll
+                for (int m = 0; m < G_::SMAX; ++m) Sown[m] = Sin[m];
+            } else {
+                zero_state();
+                add_slots(grp);
+            }
+            publish_state<F32, D, DV, C>(sm, w, r, g, Zown, Sown);
+            // ---- C: the chunk loop from registers
+            static_for<CPG>([&](auto c) {
+                if (c.value < nch) step(c.value, c);
+            });
+            if (last) store_final(nullptr, nullptr);
+            return;
+        } else {
+            // ================= streamed group: A, B, C as described above
+            const bool publish = !last;
+            const bool need_a = publish || MODE == MODE_STATE;
+            if (need_a) {
+                if (grp == 0) {
+#pragma unroll
+                    for (int m = 0; m < G_::ZT; ++m) Zown[m] = Zin[m];
+#pragma unroll
+                    for (int m = 0; m < G_::SMAX; ++m) Sown[m] = Sin[m];
+                } else {
+                    zero_state();
+                }
+                // chunks in reverse order, so that the chunk loop's first chunks
+                // are the most recently read; loads run two chunks ahead
+                KVRegs<F32, D, DV, C> RA[2];
+                auto issue_a = [&](int i, auto slot) {
+                    const int ch = max(nch - 1 - i, 0);
+                    const int t0 = t_begin + ch * C;
+                    RA[decltype(slot)::value].load(kv.at(t0, i < nch), vv.at(t0, i < nch), ko, vo);
+                };
+                auto step_a = [&](int i, auto slot) {
+                    const int t0 = t_begin + max(nch - 1 - i, 0) * C;
+                    RA[decltype(slot)::value].fill(tid, sm, i < nch ? min(C, t_end - t0) : 0);
+                    __syncthreads();
+                    issue_a(i + 2, slot);
+                    state_update<F32, D, DV, C>(sm, w, r, g, Zown, Sown);
+                    __syncthreads();
+                };
+                issue_a(0, IC<0>{});
+                issue_a(1, IC<1>{});
+                for (int i = 0; i < nch; i += 2) {   // an odd count runs one empty step
+                    step_a(i, IC<0>{});
+                    step_a(i + 1, IC<1>{});
+                }
+                if (publish) publish_slot(Zown, Sown, false);
+            }
+            // group 0 also signals that it has read z_in / s_in (in-place states)
+            if (publish || (grp == 0 && a.wait_s)) set_flag();
+            if constexpr (MODE == MODE_STATE) {
+                if (last) {
+                    add_slots(grp);
+                    store_final(nullptr, nullptr);
+                }
+                return;
+            } else {
+                issue(0, IC<0>{});   // the first chunk's loads overlap the look-back
+                if (grp == 0) {
+#pragma unroll
+                    for (int m = 0; m < G_::ZT; ++m) Zown[m] = Zin[m];
+#pragma unroll
+                    for (int m = 0; m < G_::SMAX; ++m) Sown[m] = Sin[m];
+                } else {
+                    zero_state();
+                    add_slots(grp);
+                }
+                publish_state<F32, D, DV, C>(sm, w, r, g, Zown, Sown);
+                static_assert(DEPTH == 1, "one chunk of loads in flight");
+                for (int ch = 0; ch < nch; ++ch) step(ch, IC<0>{});
+                if (last) store_final(nullptr, nullptr);
+            }
+        }
     }
-
-    if (CAUSAL && grp == a.G - 1)
-        store_owned<JT, CT, G_::ZT, G_::SMAX>(a.z_out ? a.z_out + (int64_t)bh * D * D + p * DV : nullptr, D,
-                                              (a.s_out && p == 0) ? a.s_out + (int64_t)bh * D : nullptr,
-                                              w, r, g, Zown, Sown);
 }
 
 // One recurrent step for every head: Z += phi(k) v^T, S += phi(k),
@@ -1041,7 +1369,7 @@ int pick_chunk(bool f32, int d, int chunk)
 struct Plan {
     int C, DV, P, G, L, NS;
     size_t slot_floats;
-    size_t part_bytes, fin_off, fin_bytes, total;
+    size_t part_bytes, fin_off, fin_bytes, flags_off, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1054,14 +1382,19 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 #ifndef LA_CAUSAL_TARGET_WGS
 #define LA_CAUSAL_TARGET_WGS 512
 #endif
-int pick_groups(int64_t units, int N, int C, int target)
+// The last group of a causal call reads the slots of all earlier groups of its
+// (head, column block): at most this many bytes.
+#ifndef LA_LOOKBACK_BYTES
+#define LA_LOOKBACK_BYTES (256 * 1024)
+#endif
+int pick_groups(int64_t units, int N, int C, int target, int max_groups = LA_MAX_GROUPS)
 {
     if (N <= 0) return 1;
     int64_t maxg = (N + C - 1) / C;
     int64_t g = (target + units - 1) / units;
     if (g < 1) g = 1;
     if (g > maxg) g = maxg;
-    if (g > LA_MAX_GROUPS) g = LA_MAX_GROUPS;
+    if (g > max_groups) g = max_groups;
     return (int)g;
 }
 
@@ -1075,24 +1408,41 @@ void set_groups(Plan &pl, int N)
 
 // want_out: the output is computed (else state only).  inplace: z_out/s_out
 // equal z_in/s_in.
-Plan plan_causal(int B, int H, int N, int d, la_dtype dt, int chunk, bool inplace, bool want_out)
+// Single-pass causal plan: G token groups per (head, column block), one slot
+// and one flag per group.
+Plan plan_causal(int B, int H, int N, int d, la_dtype dt, int chunk, bool want_out)
 {
     Plan pl;
     pl.C = pick_chunk(dt == LA_F32, d, chunk);
     pl.DV = cols_per_wg(d);
     pl.P = d / pl.DV;
     const int64_t BH = (int64_t)B * H;
-    pl.G = pick_groups(BH * pl.P, N, pl.C, want_out ? LA_CAUSAL_TARGET_WGS : 2 * LA_CAUSAL_TARGET_WGS);
-    set_groups(pl, N);
-    if (N == 0) pl.NS = 0;
-    else if (!want_out) pl.NS = pl.G;
-    else pl.NS = (pl.G > 1 || (inplace && pl.P > 1)) ? pl.G : 0;
     pl.slot_floats = (size_t)pl.DV * d + d;
-    pl.part_bytes = align256((size_t)BH * pl.P * pl.NS * pl.slot_floats * 4);
+    const int max_g = 1 + (int)(LA_LOOKBACK_BYTES / (pl.slot_floats * 4));
+    pl.G = pick_groups(BH * pl.P, N, pl.C, want_out ? LA_CAUSAL_TARGET_WGS : 2 * LA_CAUSAL_TARGET_WGS,
+                       max_g < LA_MAX_GROUPS ? max_g : LA_MAX_GROUPS);
+    set_groups(pl, N);
+    pl.NS = N > 0 ? pl.G : 0;
+    pl.part_bytes = pl.G > 1 ? align256((size_t)BH * pl.P * pl.G * pl.slot_floats * 4) : 0;
     pl.fin_off = pl.part_bytes;
     pl.fin_bytes = 0;
-    pl.total = pl.part_bytes;
+    pl.flags_off = pl.part_bytes;
+    pl.total = N > 0 ? pl.flags_off + align256((size_t)BH * pl.P * pl.G * 8) : 0;
     return pl;
+}
+
+// A 64-bit tag unique to each call (splitmix64 of a per-process sequence):
+// a flag counts as set only when it holds the tag of the running call, so the
+// workspace needs no clearing between calls.
+unsigned long long next_epoch()
+{
+    static std::atomic<unsigned long long> seq{(unsigned long long)time(nullptr) * 0x9E3779B97F4A7C15ull ^
+                                               ((unsigned long long)getpid() << 32) ^ (uintptr_t)&seq};
+    unsigned long long z = seq.fetch_add(0x9E3779B97F4A7C15ull) + 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return z ? z : 1;
 }
 
 Plan plan_noncausal(int B, int H, int N, int d, la_dtype dt)
@@ -1109,6 +1459,7 @@ Plan plan_noncausal(int B, int H, int N, int d, la_dtype dt)
     pl.part_bytes = align256((size_t)BH * pl.P * pl.NS * pl.slot_floats * 4);
     pl.fin_off = pl.part_bytes;
     pl.fin_bytes = align256((size_t)BH * pl.P * pl.slot_floats * 4);
+    pl.flags_off = pl.fin_off + pl.fin_bytes;
     pl.total = N > 0 ? pl.fin_off + pl.fin_bytes : 0;
     return pl;
 }
@@ -1120,15 +1471,19 @@ void launch_dc(int what, const Args &a, int nwg, hipStream_t st)
     constexpr int DV = D < 64 ? D : 64;
     if constexpr (fits<F32, D, DV, C>() && (C == 64 || (!F32 && D <= 64))) {
         if (what == 0) hipLaunchKernelGGL((k_group_state<F32, D, DV, C>), dim3(nwg), dim3(NTHR), 0, st, a);
-        else if (what == 1) hipLaunchKernelGGL((k_chunk_fwd<F32, D, DV, C, true>), dim3(nwg), dim3(NTHR), 0, st, a);
-        else hipLaunchKernelGGL((k_chunk_fwd<F32, D, DV, C, false>), dim3(nwg), dim3(NTHR), 0, st, a);
+        else if (what == 1) hipLaunchKernelGGL((k_chunk_fwd<F32, D, DV, C, MODE_OUT, 0>), dim3(nwg), dim3(NTHR), 0, st, a);
+        else if (what == 2) hipLaunchKernelGGL((k_chunk_fwd<F32, D, DV, C, MODE_APPLY, 0>), dim3(nwg), dim3(NTHR), 0, st, a);
+        else if (what == 3) hipLaunchKernelGGL((k_chunk_fwd<F32, D, DV, C, MODE_STATE, 0>), dim3(nwg), dim3(NTHR), 0, st, a);
+        else if constexpr (C == 64)
+            hipLaunchKernelGGL((k_chunk_fwd<F32, D, DV, C, MODE_OUT, res_cpg(F32, D)>), dim3(nwg), dim3(NTHR), 0, st, a);
     }
 }
 
 template <bool F32, int D>
 void dispatch_c(int C, int what, const Args &a, int nwg, hipStream_t st)
 {
-    // what: 0 = group state, 1 = causal chunk, 2 = non-causal apply
+    // what: 0 = group state, 1 = causal with output, 2 = non-causal apply,
+    // 3 = causal state only, 4 = causal with output, register-resident groups
     if (C == 128) launch_dc<F32, D, 128>(what, a, nwg, st);
     else launch_dc<F32, D, 64>(what, a, nwg, st);
 }
@@ -1219,10 +1574,11 @@ size_t la_causal_fwd_workspace(int B, int H, int N, int d, la_dtype dt, int chun
 {
     if (check_common(B, H, N, d, dt, 0.f) != LA_OK) return 0;
     if (chunk != 0 && chunk != 16 && chunk != 32 && chunk != 64 && chunk != 128) return 0;
-    // the larger of the with-output and state-only plans
-    const bool inplace = (flags & LA_WS_INPLACE_STATE) != 0;
-    Plan a = plan_causal(B, H, N, d, dt, chunk, inplace, true);
-    Plan b = plan_causal(B, H, N, d, dt, chunk, inplace, false);
+    // the larger of the with-output and state-only plans (the flags argument
+    // is accepted for compatibility: in-place states need no extra space)
+    (void)flags;
+    Plan a = plan_causal(B, H, N, d, dt, chunk, true);
+    Plan b = plan_causal(B, H, N, d, dt, chunk, false);
     return a.total > b.total ? a.total : b.total;
 }
 
@@ -1255,8 +1611,7 @@ la_status la_causal_fwd(const void *q, la_strides sq, const void *k, la_strides 
     if (s_out && s_in && s_out != (float *)s_in && overlaps(s_out, sb, s_in, sb)) return LA_ERR_ALIAS;
     if (overlaps(z_out, zb, s_in, sb) || overlaps(s_out, sb, z_in, zb) || overlaps(z_out, zb, s_out, sb))
         return LA_ERR_ALIAS;
-    const bool inplace = (z_out && z_out == z_in) || (s_out && s_out == s_in);
-    Plan pl = plan_causal(B, H, N, d, dt, chunk, inplace, want_out);
+    Plan pl = plan_causal(B, H, N, d, dt, chunk, want_out);
     if (ws_bytes < pl.total || (pl.total > 0 && !workspace)) return LA_ERR_WORKSPACE;
     if (BH == 0) return LA_OK;
 
@@ -1264,31 +1619,20 @@ la_status la_causal_fwd(const void *q, la_strides sq, const void *k, la_strides 
     (void)hipGetLastError();
     Args a = make_args(q, sq, k, sk, v, sv, out, so, B, H, N, eps);
     a.z_in = z_in; a.s_in = s_in; a.z_out = z_out; a.s_out = s_out;
-    a.P = pl.P; a.L = pl.L; a.NS = pl.NS;
+    a.P = pl.P; a.L = pl.L; a.NS = pl.NS; a.G = pl.G;
     a.part = (float *)workspace;
     const bool f32 = dt == LA_F32;
 
-    if (N == 0 || !want_out) {
-        // state only: group partials, then carried-in state + their sum
-        if (N > 0) {
-            a.G = pl.G; a.slot0 = 0;
-            dispatch(f32, d, pl.C, 0, a, (int)(BH * pl.P * pl.G), stream);
-        }
-        launch_slots(d, a, BH, pl.P, N > 0 ? pl.G : 0, 1, stream);
+    if (N == 0) {
+        // the carried-in state (or zeros) passes through
+        launch_slots(d, a, BH, pl.P, 0, 1, stream);
         return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
     }
-    if (pl.NS > 0) {
-        // group partials (groups 0..G-2 into slots 1..G-1), then the scan that
-        // turns the slots into the starting state of every group; the chunk
-        // kernel never reads z_in/s_in, so in-place state is safe
-        if (pl.G > 1) {
-            a.G = pl.G - 1; a.slot0 = 1;
-            dispatch(f32, d, pl.C, 0, a, (int)(BH * pl.P * (pl.G - 1)), stream);
-        }
-        launch_slots(d, a, BH, pl.P, pl.NS, 0, stream);
-    }
-    a.G = pl.G;
-    dispatch(f32, d, pl.C, 1, a, (int)(BH * pl.P * pl.G), stream);
+    a.flags = (unsigned long long *)((char *)workspace + pl.flags_off);
+    a.epoch = next_epoch();
+    a.wait_s = (s_out && s_out == s_in && pl.P > 1) ? 1 : 0;
+    const bool resident = pl.C == 64 && pl.L <= res_cpg(f32, d) * pl.C;
+    dispatch(f32, d, pl.C, want_out ? (resident ? 4 : 1) : 3, a, (int)(BH * pl.P * pl.G), stream);
     return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }
 
