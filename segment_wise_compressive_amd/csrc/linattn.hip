@@ -216,7 +216,7 @@ __host__ __device__ constexpr int lds_bytes(bool f32, int d, int dv, int c)
 }
 constexpr int LDS_LIMIT = 160 * 1024;  // per workgroup on gfx950
 // workgroups per CU the causal kernel's register budget is sized for
-__host__ __device__ constexpr int minwg_of(bool f32, int d, int c) { return (d <= 64 && c == 64) ? (f32 && d == 64 ? 2 : 3) : 1; }
+__host__ __device__ constexpr int minwg_of(bool f32, int d, int c) { return (d <= 64 && c == 64) ? (d == 64 ? 2 : 3) : 1; }
 // Register-resident groups (64-token chunks): chunks a workgroup keeps in
 // registers, and the workgroups per CU its register budget is sized for.
 __host__ __device__ constexpr int res_cpg(bool f32, int d) { return d == 128 ? (f32 ? 1 : 2) : (f32 && d == 64 ? 2 : 4); }
@@ -437,6 +437,46 @@ struct KVRegs {
         if (nval >= C) fill_rows<false>(tid, st, C);
         else fill_rows<true>(tid, st, nval);
     }
+
+    // bf16 only: phi(K) split into hi + lo once (kh, kl), for chunks staged
+    // twice (the group's own state, then the chunk loop); stage() then only
+    // copies registers to LDS.
+    u32x4 kh[G_::NK], kl[G_::NK];
+    __device__ __forceinline__ void phi_split(int tid, int nval)
+    {
+#pragma unroll
+        for (int it = 0; it < G_::NK; ++it) {
+            const int row = (tid + it * NTHR) / (D / G_::VEC);
+            const bool ok = nval >= C || row < nval;
+            float f[G_::VEC];
+            Vec<F32>::to_float(k[it], f);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint2 sp_ = split_pk(ok ? phi<F32>(f[2 * e]) : 0.f, ok ? phi<F32>(f[2 * e + 1]) : 0.f);
+                kh[it][e] = sp_.x;
+                kl[it][e] = sp_.y;
+            }
+        }
+    }
+    __device__ __forceinline__ void stage(int tid, typename G_::E *st) const
+    {
+        typedef typename G_::E E;
+        constexpr int VEC = G_::VEC;
+#pragma unroll
+        for (int it = 0; it < G_::NK; ++it) {
+            const int idx = tid + it * NTHR;
+            const int row = idx / (D / VEC), vg = idx % (D / VEC);
+            E *dst = st + G_::OK + row * G_::RK + swz_piece<G_::RK>(row, vg) * VEC;
+            *reinterpret_cast<u32x4 *>(dst) = kh[it];
+            *reinterpret_cast<u32x4 *>(dst + (G_::OKL - G_::OK)) = kl[it];
+        }
+#pragma unroll
+        for (int it = 0; it < G_::NV; ++it) {
+            const int idx = tid + it * NTHR;
+            const int row = idx / (DV / VEC), vg = idx % (DV / VEC);
+            *reinterpret_cast<u32x4 *>(st + G_::OV + row * G_::RV + swz_piece<G_::RV>(row, vg) * VEC) = v[it];
+        }
+    }
     template <bool MASK>
     __device__ __forceinline__ void fill_rows(int tid, typename G_::E *st, int nval) const
     {
@@ -512,21 +552,34 @@ __device__ __forceinline__ void state_update(const typename Geo<F32, D, DV, C>::
         const bf16x8 ones = {one, one, one, one, one, one, one, one};
 #pragma unroll
         for (int sa = 0; sa < G_::TBN; sa += 2) {
+            // operands of this 32-token slice first, then the products with
+            // the owned accumulators interleaved
             const bf16x8 vb = tr8<G_::RV>(v, 16 * sa, 16 * ct, r, g);
+            bf16x8 kah[G_::ZT], kal[G_::ZT], ksh[G_::SMAX], ksl[G_::SMAX];
 #pragma unroll
             for (int m = 0; m < G_::ZT; ++m) {
                 const int jt = own_jt<JT, CT>(w, m);
-                Zown[m] = mma8(Zown[m], tr8<G_::RK>(kh, 16 * sa, 16 * jt, r, g), vb);
-                Zown[m] = mma8(Zown[m], tr8<G_::RK>(kl, 16 * sa, 16 * jt, r, g), vb);
+                kah[m] = tr8<G_::RK>(kh, 16 * sa, 16 * jt, r, g);
+                kal[m] = tr8<G_::RK>(kl, 16 * sa, 16 * jt, r, g);
             }
 #pragma unroll
             for (int m = 0; m < G_::SMAX; ++m) {
                 const int jt = w + NWAVE * m;
                 if (jt < JT) {
-                    Sown[m] = mma8(Sown[m], tr8<G_::RK>(kh, 16 * sa, 16 * jt, r, g), ones);
-                    Sown[m] = mma8(Sown[m], tr8<G_::RK>(kl, 16 * sa, 16 * jt, r, g), ones);
+                    ksh[m] = tr8<G_::RK>(kh, 16 * sa, 16 * jt, r, g);
+                    ksl[m] = tr8<G_::RK>(kl, 16 * sa, 16 * jt, r, g);
                 }
             }
+#pragma unroll
+            for (int m = 0; m < G_::ZT; ++m) Zown[m] = mma8(Zown[m], kah[m], vb);
+#pragma unroll
+            for (int m = 0; m < G_::SMAX; ++m)
+                if (w + NWAVE * m < JT) Sown[m] = mma8(Sown[m], ksh[m], ones);
+#pragma unroll
+            for (int m = 0; m < G_::ZT; ++m) Zown[m] = mma8(Zown[m], kal[m], vb);
+#pragma unroll
+            for (int m = 0; m < G_::SMAX; ++m)
+                if (w + NWAVE * m < JT) Sown[m] = mma8(Sown[m], ksl[m], ones);
         }
     }
 }
@@ -748,13 +801,22 @@ __global__ void __launch_bounds__(256) k_slots(const Args a, int nslots, int mod
 // device-scope atomics use on gfx950), so a value stored by a workgroup on one
 // XCD is seen by a workgroup on another XCD without flushing any cache.
 constexpr int CPOL_DEVICE = 1 | 16;   // sc0 | sc1
+constexpr int CPOL_XCD = 1;            // sc0: past the CU's L1, served by the XCD's L2
 __device__ __forceinline__ void dstore16(rsrc_t r, uint32_t off, f32x4 v)
 {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, CPOL_DEVICE);
 }
+template <int CPOL>
 __device__ __forceinline__ f32x4 dload16(rsrc_t r, uint32_t off)
 {
-    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL_DEVICE));
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL));
+}
+// Index of the XCD (and so of the L2) the calling wave runs on.
+__device__ __forceinline__ unsigned xcc_id()
+{
+    unsigned x;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+    return x & 0xfu;
 }
 
 // Slot of one (head, column block, token group) in the single-pass kernel:
@@ -768,24 +830,36 @@ template <int D, int DV> struct FSlot {
     __device__ static uint32_t soff(int jt, int g) { return (uint32_t)((ZF + 16 * jt + 4 * g) * 4); }
 };
 
+// chunks of a register-resident group whose phi(K) split is held from the
+// group's own-state step to the chunk loop (registers permitting)
+#ifndef LA_KEEP_SPLIT
+#define LA_KEEP_SPLIT 0
+#endif
+
 // Spin limit of a flag wait (each poll sleeps ~1 us): a call whose flags never
 // arrive (a bug, or memory not meant for this call) ends instead of hanging.
 constexpr int SPIN_LIMIT = 1 << 20;
 
-// Wait until base[i * stride] == epoch for i < n (lane i watches entry i, in
-// rounds of 64 entries).  Every lane of the wave runs this.
-__device__ __forceinline__ void wait_flags(const unsigned long long *base, int stride, int n,
-                                           unsigned long long epoch, int lane)
+// A flag holds the call's tag (low 4 bits zero) plus the XCD index of the
+// workgroup that set it.  Wait until base[i * stride] carries `epoch` for
+// i < n (lane i watches entry i, in rounds of 64 entries); returns whether
+// all of them were set on XCD `xcc`.  Every lane of the wave runs this.
+__device__ __forceinline__ bool wait_flags(const unsigned long long *base, int stride, int n,
+                                           unsigned long long epoch, unsigned xcc, int lane)
 {
+    bool local = true;
     for (int i0 = 0; i0 < n; i0 += WAVE) {
         const int i = i0 + lane;
         const unsigned long long *f = base + (int64_t)(i < n ? i : 0) * stride;
+        unsigned long long v = 0;
         for (int spin = 0; spin < SPIN_LIMIT; ++spin) {
-            const bool ok = i >= n || __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
-            if (__all(ok)) break;
+            v = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (__all(i >= n || (v & ~0xfull) == epoch)) break;
             __builtin_amdgcn_s_sleep(16);
         }
+        local = local && __all(i >= n || (v & 0xfull) == xcc);
     }
+    return local;
 }
 
 // The causal forward of one token group in a single pass (modes 3 and 4 of
@@ -889,32 +963,40 @@ __global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F
 
     // ---- slot helpers: add the published slots of groups 0..n-1 of this
     // (head, column block); write z_out / s_out from (Zown + Zadd, Sown + Sadd)
+    // (slots written on this workgroup's XCD are read from its L2; others
+    // from memory)
+    const unsigned my_xcc = xcc_id();
     auto add_slots = [&](int n) {
-        wait_flags(a.flags + (int64_t)hp * a.G, 1, n, a.epoch, lane);
+        const bool local = wait_flags(a.flags + (int64_t)hp * a.G, 1, n, a.epoch, my_xcc, lane);
         constexpr int LB = (G_::ZT + G_::SMAX) <= 5 ? 4 : 2;   // slots in flight
         const char *base = (const char *)a.part + (size_t)hp * a.G * FS::BYTES;
-        for (int g0 = 0; g0 < n; g0 += LB) {
-            f32x4 tz[LB][G_::ZT], ts[LB][G_::SMAX];
+        auto sum = [&](auto cpol) {
+            constexpr int CP = decltype(cpol)::value;
+            for (int g0 = 0; g0 < n; g0 += LB) {
+                f32x4 tz[LB][G_::ZT], ts[LB][G_::SMAX];
 #pragma unroll
-            for (int u = 0; u < LB; ++u) {
-                const bool live = g0 + u < n;
-                const rsrc_t sr = make_rsrc(base + (size_t)(live ? g0 + u : 0) * FS::BYTES, live ? FS::BYTES : 0);
+                for (int u = 0; u < LB; ++u) {
+                    const bool live = g0 + u < n;
+                    const rsrc_t sr = make_rsrc(base + (size_t)(live ? g0 + u : 0) * FS::BYTES, live ? FS::BYTES : 0);
 #pragma unroll
-                for (int m = 0; m < G_::ZT; ++m) tz[u][m] = dload16(sr, FS::zoff(w, m, lane));
+                    for (int m = 0; m < G_::ZT; ++m) tz[u][m] = dload16<CP>(sr, FS::zoff(w, m, lane));
 #pragma unroll
-                for (int m = 0; m < G_::SMAX; ++m) {
-                    const int jt = w + NWAVE * m;
-                    ts[u][m] = dload16(sr, (r == 0 && jt < JT) ? FS::soff(jt, g) : OFF_NONE);
+                    for (int m = 0; m < G_::SMAX; ++m) {
+                        const int jt = w + NWAVE * m;
+                        ts[u][m] = dload16<CP>(sr, (r == 0 && jt < JT) ? FS::soff(jt, g) : OFF_NONE);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < LB; ++u) {
+#pragma unroll
+                    for (int m = 0; m < G_::ZT; ++m) Zown[m] += tz[u][m];
+#pragma unroll
+                    for (int m = 0; m < G_::SMAX; ++m) Sown[m] += ts[u][m];
                 }
             }
-#pragma unroll
-            for (int u = 0; u < LB; ++u) {
-#pragma unroll
-                for (int m = 0; m < G_::ZT; ++m) Zown[m] += tz[u][m];
-#pragma unroll
-                for (int m = 0; m < G_::SMAX; ++m) Sown[m] += ts[u][m];
-            }
-        }
+        };
+        if (local) sum(IC<CPOL_XCD>{});
+        else sum(IC<CPOL_DEVICE>{});
     };
     // this group's slot <- (za, sa), plus (Zown, Sown) if `add`
     auto publish_slot = [&](const f32x4 *za, const f32x4 *sa, bool add) {
@@ -932,13 +1014,14 @@ __global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (tid == 0)
-            __hip_atomic_store(a.flags + (int64_t)hp * a.G + grp, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.flags + (int64_t)hp * a.G + grp, a.epoch | my_xcc, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     };
     auto store_final = [&](const f32x4 *Zadd, const f32x4 *Sadd) {
         // s_out is written by the last column block; with in-place states it
         // first waits until group 0 of every column block has read s_in
         const bool s_writer = p == a.P - 1;
-        if (a.wait_s && s_writer) wait_flags(a.flags + (int64_t)bh * a.P * a.G, a.G, a.P, a.epoch, lane);
+        if (a.wait_s && s_writer) (void)wait_flags(a.flags + (int64_t)bh * a.P * a.G, a.G, a.P, a.epoch, my_xcc, lane);
         f32x4 zf[G_::ZT], sf[G_::SMAX];
 #pragma unroll
         for (int m = 0; m < G_::ZT; ++m) zf[m] = Zadd ? Zown[m] + Zadd[m] : Zown[m];
@@ -1003,20 +1086,25 @@ __global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F
         } else {
             const bf16 *zh = reinterpret_cast<const bf16 *>(sm) + G_::OZ;
             const bf16 *zl = reinterpret_cast<const bf16 *>(sm) + G_::OZL;
+            // all operands first, then the products with the CT + 1
+            // accumulators interleaved (independent MFMA chains)
+            bf16x8 a_hi[CT + 1][NQV], a_lo[CT + 1][NQV];
 #pragma unroll
             for (int ct = 0; ct <= CT; ++ct) {
                 const int zo = (ct < CT ? 16 * ct + r : DV) * G_::RZ + 8 * g;
-                bf16x8 a_hi[NQV], a_lo[NQV];
 #pragma unroll
-                for (int u = 0; u < NQV; ++u) { a_hi[u] = nat8(zh + zo + 32 * u); a_lo[u] = nat8(zl + zo + 32 * u); }
+                for (int u = 0; u < NQV; ++u) { a_hi[ct][u] = nat8(zh + zo + 32 * u); a_lo[ct][u] = nat8(zl + zo + 32 * u); }
+            }
 #pragma unroll
-                for (int u = 0; u < NQV; ++u) {
-                    const bf16x8 qh8 = *reinterpret_cast<const bf16x8 *>(&qh[u]);
-                    const bf16x8 ql8 = *reinterpret_cast<const bf16x8 *>(&ql[u]);
-                    o[ct] = mma8(o[ct], a_hi[u], qh8);
-                    o[ct] = mma8(o[ct], a_lo[u], qh8);
-                    o[ct] = mma8(o[ct], a_hi[u], ql8);
-                }
+            for (int u = 0; u < NQV; ++u) {
+                const bf16x8 qh8 = *reinterpret_cast<const bf16x8 *>(&qh[u]);
+                const bf16x8 ql8 = *reinterpret_cast<const bf16x8 *>(&ql[u]);
+#pragma unroll
+                for (int ct = 0; ct <= CT; ++ct) o[ct] = mma8(o[ct], a_hi[ct][u], qh8);
+#pragma unroll
+                for (int ct = 0; ct <= CT; ++ct) o[ct] = mma8(o[ct], a_lo[ct][u], qh8);
+#pragma unroll
+                for (int ct = 0; ct <= CT; ++ct) o[ct] = mma8(o[ct], a_hi[ct][u], ql8);
             }
         }
     };
@@ -1106,10 +1194,21 @@ __global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F
 
     // ---- one chunk of the streaming loop (and of the non-causal readout):
     // stage K, V and phi(q); the output rows; the state update
+    // (resident bf16 groups: phi(K) is split in registers once; `split_done`
+    // says the group's own-state step already did it)
+    bool split_done = false;
     auto step = [&](int ch, auto slot) {
         constexpr int S_ = decltype(slot)::value;
         const int t0 = t_begin + ch * C;
-        if (CAUSAL) R[S_].fill(tid, sm, min(C, t_end - t0));
+        if constexpr (RES && !F32) {
+            // the split of the first KEEP chunks is held from the group's own-
+            // state step; later ones are split again (register budget)
+            constexpr int KEEP = LA_KEEP_SPLIT;
+            if (!split_done || S_ >= KEEP) R[S_].phi_split(tid, min(C, t_end - t0));
+            R[S_].stage(tid, sm);
+        } else if (CAUSAL) {
+            R[S_].fill(tid, sm, min(C, t_end - t0));
+        }
         QOp qhi[BPW][NQV], qlo[BPW][NQV];
 #pragma unroll
         for (int bi = 0; bi < BPW; ++bi) phi_q(Q[S_][bi], qhi[bi], qlo[bi]);
@@ -1173,7 +1272,12 @@ __global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F
                     if constexpr (c == (CPG >= 3 ? CPG - 3 : 0))
                         static_for<CPG>([&](auto j) { issue_q(j.value, j); });
                     if (c < nch) {
-                        R[c].fill(tid, sm, min(C, t_end - (t_begin + c * C)));
+                        if constexpr (F32) {
+                            R[c].fill(tid, sm, min(C, t_end - (t_begin + c * C)));
+                        } else {
+                            R[c].phi_split(tid, min(C, t_end - (t_begin + c * C)));
+                            R[c].stage(tid, sm);
+                        }
                         __syncthreads();
                         state_update<F32, D, DV, C>(sm, w, r, g, Zown, Sown);
                         __syncthreads();
@@ -1181,6 +1285,7 @@ __global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F
                 });
                 publish_slot(Zown, Sown, false);
                 set_flag();
+                split_done = true;
             } else {
                 issue_rest();
                 if (grp == 0 && a.wait_s) set_flag();   // only signals that z_in / s_in have been read
@@ -1442,7 +1547,8 @@ unsigned long long next_epoch()
     z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
     z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
     z ^= z >> 31;
-    return z ? z : 1;
+    z &= ~0xfull;   // the low 4 bits of a flag carry the XCD index
+    return z ? z : 16;
 }
 
 Plan plan_noncausal(int B, int H, int N, int d, la_dtype dt)

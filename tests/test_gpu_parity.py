@@ -296,6 +296,25 @@ def test_bitwise_deterministic():
     assert torch.equal(n1, n2)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_reused_workspace_new_inputs(d):
+    """Back-to-back multi-group calls on one workspace, each with new inputs:
+    the partial states published between workgroups must be this call's."""
+    B, H, N = 1, 2, 2048 if d == 128 else 4096
+    _log(f"reused workspace d={d}")
+    ws = torch.empty(la.la_causal_fwd_workspace(B, H, N, d, torch.bfloat16), dtype=torch.uint8, device=DEV)
+    out = torch.empty(B, H, N, d, dtype=torch.float32, device=DEV)
+    z = torch.empty(B, H, d, d, dtype=torch.float32, device=DEV)
+    s = torch.empty(B, H, d, dtype=torch.float32, device=DEV)
+    for call in range(3):
+        q, k, v = inp.qkv((B, H, N, d), 60 + call, torch.bfloat16, d ** -0.5)
+        la.la_causal_fwd(q.to(DEV), k.to(DEV), v.to(DEV), out, z_out=z, s_out=s, workspace=ws)
+        torch.cuda.synchronize()
+        ro, rz, rs = oracle.causal(q, k, v, 1e-6)
+        assert heads_err(out.cpu(), ro, d) < TOL[torch.bfloat16], call
+        assert state_err(z.cpu(), rz) < TOL[torch.bfloat16], call
+
+
 def test_nan_key_propagates_forward_only():
     B, H, N, d = 1, 1, 500, 64
     q, k, v = inp.qkv((B, H, N, d), 48, torch.bfloat16, 0.125)
