@@ -1215,6 +1215,7 @@ __global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F
         if (CAUSAL || ch == 0) __syncthreads();   // stage and published state visible
         // ---- request chunk ch + DEPTH into the registers just consumed
         if constexpr (!RES) issue(ch + DEPTH, slot);
+        else if constexpr (S_ + 2 < NR) issue_q(ch + 2, IC<S_ + 2>{});
 #pragma unroll
         for (int bi = 0; bi < BPW; ++bi) {
             f32x4 o[CT + 1];   // value tiles, then the normaliser tile
@@ -1251,9 +1252,8 @@ __global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F
             // the chunk in use); q is requested after the last k and v; the
             // chunk loop C then issues stores only.
             constexpr int KV0 = CPG < 2 ? CPG : 2;   // k, v chunks requested up front
-            auto issue_rest = [&]() {   // k, v of the remaining chunks, then all q
+            auto issue_rest = [&]() {   // k, v of the remaining chunks
                 static_for<CPG>([&](auto c) { if constexpr (c.value >= KV0) issue_kv(c.value, c); });
-                static_for<CPG>([&](auto c) { issue_q(c.value, c); });
             };
             static_for<KV0>([&](auto c) { issue_kv(c.value, c); });
             if (!last) {
@@ -1267,10 +1267,8 @@ __global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F
                 }
                 static_for<CPG>([&](auto cc) {
                     constexpr int c = decltype(cc)::value;
-                    // k, v of chunk c + 2 (q after the last of them) while chunk c is used
+                    // k, v of chunk c + 2 while chunk c is used
                     if constexpr (c + 2 < CPG) issue_kv(c + 2, IC<c + 2>{});
-                    if constexpr (c == (CPG >= 3 ? CPG - 3 : 0))
-                        static_for<CPG>([&](auto j) { issue_q(j.value, j); });
                     if (c < nch) {
                         if constexpr (F32) {
                             R[c].fill(tid, sm, min(C, t_end - (t_begin + c * C)));
@@ -1290,6 +1288,8 @@ __global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F
                 issue_rest();
                 if (grp == 0 && a.wait_s) set_flag();   // only signals that z_in / s_in have been read
             }
+            // q streams through the chunk loop two chunks ahead; the first two
+            // are requested here, after the look-back's loads
             // ---- B: the state before the group
             if (grp == 0) {
 #pragma unroll
@@ -1300,6 +1300,7 @@ __global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F
                 zero_state();
                 add_slots(grp);
             }
+            static_for<KV0>([&](auto c) { issue_q(c.value, c); });
             publish_state<F32, D, DV, C>(sm, w, r, g, Zown, Sown);
             // ---- C: the chunk loop from registers
             static_for<CPG>([&](auto c) {
