@@ -39,23 +39,24 @@ def alg_bytes_causal(w, with_state_io=False):
 
 
 def time_steps(fn, steps, warmup, n_rot):
-    """Run fn(i) warmup + steps times; return (total_ms, per-step event ms list)."""
+    """Run fn(i) warmup times untimed, then exactly `steps` times back to back
+    between two HIP events on the current stream (a device synchronize on both
+    sides); return the elapsed ms.  No event is recorded between the steps:
+    per-step events cost several microseconds of host time each and would
+    leave the GPU idle between launches."""
     import torch
     for i in range(warmup):
         fn(i % n_rot)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
     for i in range(steps):
-        evs[i][0].record()
         fn((warmup + i) % n_rot)
-        evs[i][1].record()
     t_end.record()
     torch.cuda.synchronize()
-    return t_start.elapsed_time(t_end), [a.elapsed_time(b) for a, b in evs]
+    return t_start.elapsed_time(t_end)
 
 
 def measured_traffic(name):
@@ -97,9 +98,8 @@ def bench_headline(args, torch, la, inp):
     def step(i):
         calls[i]()
 
-    total_ms, per = time_steps(step, args.steps, args.warmup, n_rot)
-    per_call = sum(per) / len(per)
-    return w, total_ms, per_call, (q, k, v)
+    total_ms = time_steps(step, args.steps, args.warmup, n_rot)
+    return w, total_ms, total_ms / args.steps, (q, k, v)
 
 
 def bench_segmented(args, torch, la, inp):
@@ -126,7 +126,7 @@ def bench_segmented(args, torch, la, inp):
             c()
 
     steps = max(3, args.steps // 4)
-    total_ms, per = time_steps(step, steps, max(1, args.warmup // 2), 1)
+    total_ms = time_steps(step, steps, max(1, args.warmup // 2), 1)
     ms = total_ms / steps
     seg_w = inp.Workload("segment", "causal", w.dtype, w.B, w.H, w.segment, w.d, 0, 1.0)
     b_call = alg_bytes_causal(seg_w, with_state_io=True)
@@ -159,12 +159,11 @@ def bench_decode(args, torch, la, inp):
         def step(i):
             calls[i % nst]()
 
-        total_ms, per = time_steps(step, nst, 16, 10 ** 9)
+        total_ms = time_steps(step, nst, 16, 10 ** 9)
         ms = total_ms / nst
-        per_call = sum(per) / len(per)
         bpc = B * H * (2 * (d * d + d) * 4 + 3 * d * w.dtype.itemsize + d * 4)
         res[label] = {"ms_per_step": round(ms, 5), "value": round(B * H / (ms * 1e-3), 1),
-                      "roofline": roofline(bpc, per_call)}
+                      "roofline": roofline(bpc, ms)}
     return {"workload": w.name, "unit": "head-tokens/s", **res}
 
 
@@ -181,8 +180,8 @@ def bench_noncausal(args, torch, la, inp):
         call()
 
     steps = max(3, args.steps // 2)
-    total_ms, per = time_steps(step, steps, 2, 1)
-    per_call = sum(per) / len(per)
+    total_ms = time_steps(step, steps, 2, 1)
+    per_call = total_ms / steps
     return {"workload": w.name, "value": round(w.head_tokens / (per_call * 1e-3), 1), "unit": "head-tokens/s",
             "ms_per_step": round(per_call, 4), "roofline": roofline(alg_bytes_causal(w), per_call)}
 
@@ -260,7 +259,8 @@ def main():
                    "rotated_sets": args.rotate},
         "roofline": roofline(alg_bytes_causal(w), per_call, measured_traffic(w.name)),
     }
-    line["roofline"]["kernels"] = "k_group_state + k_slots + k_chunk_fwd: one la_causal_fwd call, timed as a whole"
+    line["roofline"]["kernels"] = ("k_chunk_fwd (one launch per la_causal_fwd call); duration = HIP-event time "
+                                   "of the timed back-to-back calls / calls")
     if not args.headline_only:
         log("segmented workload ...")
         line.setdefault("workloads", {})["segmented"] = bench_segmented(args, torch, la, inp)
