@@ -166,6 +166,14 @@ __device__ __forceinline__ int xcd_remap(int id, int n)
     if ((n & 7) != 0) return id;
     return (id & 7) * (n >> 3) + (id >> 3);
 }
+// Whether logical ids first .. first + count - 1 all run on one XCD under
+// xcd_remap (each XCD holds a contiguous range of n / 8 logical ids).
+__device__ __forceinline__ bool ids_on_one_xcd(int first, int count, int n)
+{
+    if ((n & 7) != 0) return count == 1;
+    const int per = n >> 3;
+    return first / per == (first + count - 1) / per;
+}
 
 // ------------------------------------------------------------------ kernel arguments
 struct Args {
@@ -806,6 +814,13 @@ __device__ __forceinline__ void dstore16(rsrc_t r, uint32_t off, f32x4 v)
 {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, CPOL_DEVICE);
 }
+// store with the cache policy CPOL (CPOL_XCD: into the XCD's L2, for readers
+// on the same XCD only)
+template <int CPOL>
+__device__ __forceinline__ void cstore16(rsrc_t r, uint32_t off, f32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, CPOL);
+}
 template <int CPOL>
 __device__ __forceinline__ f32x4 dload16(rsrc_t r, uint32_t off)
 {
@@ -834,6 +849,12 @@ template <int D, int DV> struct FSlot {
 // group's own-state step to the chunk loop (registers permitting)
 #ifndef LA_KEEP_SPLIT
 #define LA_KEEP_SPLIT 0
+#endif
+
+// bf16 causal calls with output and register-resident groups run the
+// column-split kernel (k_cs_fwd) where it is instantiated
+#ifndef LA_COLUMN_SPLIT
+#define LA_COLUMN_SPLIT 1
 #endif
 
 // Spin limit of a flag wait (each poll sleeps ~1 us): a call whose flags never
@@ -1373,6 +1394,540 @@ __global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F
     }
 }
 
+// ================================================================ column-split causal kernel
+// bf16 inputs, 64-token chunks, a group of at most CPG chunks per workgroup
+// with every q, k, v load of the group held in registers.  Each of the 4 waves
+// owns 16 of the workgroup's 64 value columns for the whole group: its slice
+// of the state Z (all D key dims x 16 columns) and a copy of S stay in its
+// registers, so the chunk loop shares no state through LDS.  Per chunk a wave
+// computes the scores of all 64 queries (the same in every wave), the inter-
+// and intra-chunk terms of its 16 columns, and the normaliser of one 16-query
+// tile, which goes to the other waves through LDS with the chunk's barrier.
+//
+// Precision: phi = 1 + psi with psi = elu, and only psi(q), psi(k) are bf16
+// MFMA operands (exact for positive inputs; the all-ones part of phi is
+// carried in fp32).  So
+//   phi(q) . z     = sum_i z_i + psi(q) . z            (z a column of Z, or S)
+//   phi(q) . phi(k) = d + sum psi(q) + sum psi(k) + psi(q) . psi(k)
+//   Z += psi(K)^T V + 1 (column sums of V)^T,  S += psi(K)^T 1 + (tokens) 1,
+// where the sums over dims of psi come from the stage (fp32, of the rounded
+// values) and the sums over dims of Z and S are MFMA products with an all-ones
+// operand.  The fp32 values fed back as operands -- the scores P and the state
+// (Z, S) -- are split into bf16 hi + lo.
+//
+// State tile layout: tile jt = 2u + hf, row m = 4g + i of the tile holds key
+// dim pi(jt, m) = 32u + 8g + 4hf + i.  Then tiles 2u and 2u + 1 of a lane hold
+// dims 32u + 8g .. 32u + 8g + 7 in order: the natural operand layout of a
+// 32-dim contraction step, which is also how phi(q) and phi(k) rows are read.
+template <int D> struct CSGeo {
+    static constexpr int C = 64, DV = 64;
+    static constexpr int JT = D / 16;              // state tiles (key dims) per wave
+    static constexpr int KS = D / 32;              // 32-dim contraction steps
+    static constexpr int VPR = D / 8;              // 16-byte vectors per q / k row
+    static constexpr int NK = C * VPR / NTHR;      // k (and q) vectors per thread per chunk
+    static constexpr int NV = C * (DV / 8) / NTHR; // v vectors per thread per chunk
+    // LDS, bf16 elements: two stage buffers of psi(K) [C][D] and of V [C][DV]
+    // (rows swizzled, swz); the score operands [6 pairs][hi, lo][64 lanes][8];
+    // the S operands [2][hi, lo][KS][4 lane groups][8]; psi(Q) of every chunk
+    // of the group [CPG][C][D] (swizzled); then fp32: the normalisers
+    // [CPG][C] and the sums of S [2].
+    static constexpr int OK = 0, OV = 2 * C * D, OP = OV + 2 * C * DV, OSO = OP + 6 * 2 * 64 * 8;
+    static constexpr int OQ = OSO + 2 * 2 * KS * 4 * 8;
+    static constexpr int bf16_elems(int cpg) { return OQ + cpg * C * D; }
+    static constexpr int lds_bytes(int cpg) { return bf16_elems(cpg) * 2 + (cpg * C + 4) * 4; }
+    static_assert(NK * NTHR == C * VPR && NV * NTHR == C * DV / 8, "whole vectors per thread");
+};
+__device__ __forceinline__ int cs_dim(int jt, int m) { return 32 * (jt >> 1) + 8 * (m >> 2) + 4 * (jt & 1) + (m & 3); }
+
+// phi(K)^T operand of state tile jt for tokens s0 + 4g .. s0 + 4g + 3: lane n
+// addresses token row s0 + 4g + n/4 and the 4 dims starting at
+// 32u + 8(n%4) + 4hf; the transpose read then hands lane n the dim
+// cs_dim(jt, n) (element n%4 of the piece addressed by lane 4*row + n/4).
+template <int W>
+__device__ __forceinline__ bf16x4 cs_ktr4(const bf16 *base, int s0, int jt, int n, int g)
+{
+    const bf16 *p = base + swz<W>(s0 + 4 * g + (n >> 2), 32 * (jt >> 1) + 8 * (n & 3) + 4 * (jt & 1));
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(bf16 *)p);
+}
+template <int W>
+__device__ __forceinline__ bf16x8 cs_ktr8(const bf16 *base, int s0, int jt, int n, int g)
+{
+    const bf16x4 x = cs_ktr4<W>(base, s0, jt, n, g), y = cs_ktr4<W>(base, s0 + 16, jt, n, g);
+    return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// bf16 hi + lo operands of two fp32 fragments (8 values in order)
+__device__ __forceinline__ void cs_split(f32x4 x, f32x4 y, bf16x8 &hi, bf16x8 &lo)
+{
+    u32x4 h, l;
+    { const uint2 s_ = split_pk(x[0], x[1]); h[0] = s_.x; l[0] = s_.y; }
+    { const uint2 s_ = split_pk(x[2], x[3]); h[1] = s_.x; l[1] = s_.y; }
+    { const uint2 s_ = split_pk(y[0], y[1]); h[2] = s_.x; l[2] = s_.y; }
+    { const uint2 s_ = split_pk(y[2], y[3]); h[3] = s_.x; l[3] = s_.y; }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
+// psi(x) = elu(x) = phi(x) - 1: x above zero, e^x - 1 at or below it.  As
+// e^x - 1 >= x everywhere, this is max(x, min(e^x, 1) - 1): four
+// instructions (the min is the clamp bit of v_exp_f32; the NaN-propagating
+// maximum keeps psi(NaN) = NaN; psi(-inf) = -1, psi(+inf) = +inf).
+__device__ __forceinline__ float psi(float x)
+{
+    const float e = __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(x * 1.44269504088896340736f), 0.f, 1.f);
+    return __builtin_elementwise_maximum(x, e - 1.f);
+}
+// psi of 8 packed bf16 values rounded to bf16 (nearest even)
+__device__ __forceinline__ u32x4 cs_psi8(u32x4 x)
+{
+    float f[8];
+    Vec<false>::to_float(x, f);
+    u32x4 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = pk_bf16(psi(f[2 * e]), psi(f[2 * e + 1]));
+    return y;
+}
+
+template <int D, int CPG>
+__global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
+{
+    typedef CSGeo<D> T;
+    typedef FSlot<D, 64> FS;
+    constexpr int C = T::C, DV = T::DV, JT = T::JT, KS = T::KS, VPR = T::VPR, NK = T::NK, NV = T::NV;
+    static_assert(FS::ZT == JT, "slot tiles per wave");
+    __shared__ __attribute__((aligned(16))) char smem_raw[T::lds_bytes(CPG)];
+    bf16 *sm = reinterpret_cast<bf16 *>(smem_raw);
+    float *den_s = reinterpret_cast<float *>(smem_raw + T::bf16_elems(CPG) * 2);   // [CPG][C]
+    float *ssum_s = den_s + CPG * C;                                                // [2]
+    auto kbuf = [&](int buf) { return sm + T::OK + buf * C * D; };
+    auto vbuf = [&](int buf) { return sm + T::OV + buf * C * DV; };
+    auto qslot = [&](int c) { return sm + T::OQ + c * C * D; };
+
+    const int tid = threadIdx.x, lane = tid % WAVE, r = lane % 16, g = lane / 16;
+    const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);   // wave-uniform
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    const int p = wg % a.P, rest = wg / a.P, grp = rest % a.G, bh = rest / a.G;
+    const int b = bh / a.H, h = bh % a.H;
+    const int hp = bh * a.P + p;
+    const int t_begin = grp * a.L, t_end = min(t_begin + a.L, a.N);
+    const int nch = (t_end - t_begin + C - 1) / C;
+    const bool last = grp == a.G - 1;
+    const bool s_writer = p == a.P - 1;
+    const RowView qv{(const char *)a.q + (b * a.sqb + h * a.sqh) * 2, a.sqn * 2, (a.N - 1) * a.sqn * 2 + D * 2};
+    const RowView kv{(const char *)a.k + (b * a.skb + h * a.skh) * 2, a.skn * 2, (a.N - 1) * a.skn * 2 + D * 2};
+    const RowView vv{(const char *)a.v + (b * a.svb + h * a.svh + p * DV) * 2, a.svn * 2,
+                     (a.N - 1) * a.svn * 2 + DV * 2};
+    const RowView ov{(const char *)(a.out + b * a.sob + h * a.soh + p * DV), a.son * 4, (a.N - 1) * a.son * 4 + DV * 4};
+
+    // cooperative loads: vector `it` of a thread is item tid + it * NTHR of the
+    // chunk, row item / (vectors per row); q, k, v are requested two chunks
+    // ahead
+    uint32_t ko[NK], qo[NK], vo[NV];
+#pragma unroll
+    for (int it = 0; it < NK; ++it) {
+        const int item = tid + it * NTHR, row = item / VPR, vec = item % VPR;
+        ko[it] = (uint32_t)(row * kv.rs + vec * 16);
+        qo[it] = (uint32_t)(row * qv.rs + vec * 16);
+    }
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+        const int item = tid + it * NTHR;
+        vo[it] = (uint32_t)((item / 8) * vv.rs + (item % 8) * 16);
+    }
+    u32x4 Kr[CPG][NK], Vr[CPG][NV], Qr[CPG][NK];
+    auto issue = [&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        const int t0 = t_begin + c * C;
+        const rsrc_t kr = kv.at(t0, c < nch), vr = vv.at(t0, c < nch), qr = qv.at(t0, c < nch);
+#pragma unroll
+        for (int it = 0; it < NK; ++it) Kr[c][it] = bload16(kr, ko[it]);
+#pragma unroll
+        for (int it = 0; it < NV; ++it) Vr[c][it] = bload16(vr, vo[it]);
+#pragma unroll
+        for (int it = 0; it < NK; ++it) Qr[c][it] = bload16(qr, qo[it]);
+    };
+    auto nval_of = [&](int c) { return min(C, t_end - (t_begin + c * C)); };
+    // the stage of chunk c: psi(K) and V into buffer c % 2, psi(Q) into slot c.
+    // Rows past the end of the sequence read as zeros (outside the buffer
+    // resource), and psi(0) = 0, so they add nothing to the state; the scores
+    // mask those keys.
+    auto stage = [&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        const int buf = c & 1;
+        bf16 *Kb = kbuf(buf), *Qb = qslot(c), *Vb = vbuf(buf);
+#pragma unroll
+        for (int it = 0; it < NK; ++it) {
+            const int item = tid + it * NTHR, row = item / VPR, vec = item % VPR;
+            *reinterpret_cast<u32x4 *>(Kb + swz<D>(row, vec * 8)) = cs_psi8(Kr[c][it]);
+            *reinterpret_cast<u32x4 *>(Qb + swz<D>(row, vec * 8)) = cs_psi8(Qr[c][it]);
+        }
+#pragma unroll
+        for (int it = 0; it < NV; ++it) {
+            const int item = tid + it * NTHR, row = item / 8, vec = item % 8;
+            *reinterpret_cast<u32x4 *>(Vb + swz<64>(row, vec * 8)) = Vr[c][it];
+        }
+    };
+
+    bf16x8 ones8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones8[e] = (bf16)1.f;
+    // ---- the wave's state: Z[dims][16w + r]; wave 0 also holds S[dims] (every
+    // column of an S tile holds S).  First the group-local running state
+    // (group 0: from the carried-in state), then the state before the group
+    // (Ze, Se).
+    f32x4 Z[JT], S[JT], Ze[JT], Se[JT];
+    auto load_state = [&](f32x4 *z4, f32x4 *s4, const float *z, const float *s) {
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int dim = cs_dim(jt, 4 * g + i);
+                z4[jt][i] = z ? z[(int64_t)dim * D + p * DV + 16 * w + r] : 0.f;
+                s4[jt][i] = s ? s[dim] : 0.f;
+            }
+    };
+    // hi + lo operands of a state, and its sums over the key dims (every row
+    // of the result: sum_i z[i][column])
+    auto state_ops = [&](const f32x4 *z4, bf16x8 *zh, bf16x8 *zl, f32x4 &zsum) {
+        zsum = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < KS; ++u) {
+            cs_split(z4[2 * u], z4[2 * u + 1], zh[u], zl[u]);
+            zsum = mma8(zsum, zh[u], ones8);
+            zsum = mma8(zsum, zl[u], ones8);
+        }
+    };
+    // S operands for the normalisers, shared through LDS by wave 0 (the hi/lo
+    // operand of a lane depends only on its lane group g): [2][hi, lo][KS][g]
+    auto sops_at = [&](int buf, int hl, int u, int gg) { return sm + T::OSO + (((buf * 2 + hl) * KS + u) * 4 + gg) * 8; };
+    auto put_sops = [&](const f32x4 *s4, int buf) {   // wave 0
+        bf16x8 sh[KS], sl[KS];
+        f32x4 ss;
+        state_ops(s4, sh, sl, ss);
+        if (r == 0) {
+#pragma unroll
+            for (int u = 0; u < KS; ++u) {
+                *reinterpret_cast<bf16x8 *>(sops_at(buf, 0, u, g)) = sh[u];
+                *reinterpret_cast<bf16x8 *>(sops_at(buf, 1, u, g)) = sl[u];
+            }
+        }
+        if (lane == 0) ssum_s[buf] = ss[0];
+    };
+    // the normaliser of query tile m: ssum + S . psi(q) + (intra, by the caller)
+    auto sdot = [&](int buf, const bf16x8 *qb) {
+        f32x4 dn;
+        const float s0 = ssum_s[buf];
+        dn = (f32x4){s0, s0, s0, s0};
+#pragma unroll
+        for (int u = 0; u < KS; ++u) {
+            dn = mma8(dn, nat8(sops_at(buf, 0, u, g)), qb[u]);
+            dn = mma8(dn, nat8(sops_at(buf, 1, u, g)), qb[u]);
+        }
+        return dn;
+    };
+    auto q_ops = [&](const bf16 *Qb, int m, bf16x8 *qb) {
+#pragma unroll
+        for (int u = 0; u < KS; ++u) qb[u] = nat8(Qb + swz<D>(16 * m + r, 32 * u + 8 * g));
+    };
+    // ---- scores: tile (sa, m) of P^T (keys 16 sa.., queries 16 m..) is
+    // computed by one wave, split into bf16 hi + lo and written to LDS as half
+    // of the P V operand of pair (m, sa / 2): [pair][hi, lo][lane][8]
+    // first pair of query tile m: 0, 1, 2, 4
+    auto pbase = [](int m) { return m + (m == 3 ? 1 : 0); };
+    auto pop_at = [&](int pair, int hl, int ln) { return sm + T::OP + ((pair * 2 + hl) * WAVE + ln) * 8; };
+    // tiles above the diagonal that complete a pair: zero once
+    if (tid < 4 * WAVE) {
+        const int which = tid / WAVE, ln = tid % WAVE;   // (pair 0 | pair 3) x (hi | lo)
+        *reinterpret_cast<uint2 *>(pop_at(which < 2 ? 0 : 3, which & 1, ln) + 4) = make_uint2(0u, 0u);
+    }
+    auto score_tile = [&](const bf16x8 *ka, const bf16x8 *qb, int sa, int m, int nv) {
+        f32x4 pt = {(float)D, (float)D, (float)D, (float)D};
+#pragma unroll
+        for (int u = 0; u < KS; ++u) {
+            pt = mma8(pt, ka[u], ones8);   // + sum psi(k_s)
+            pt = mma8(pt, ones8, qb[u]);   // + sum psi(q_t)
+            pt = mma8(pt, ka[u], qb[u]);   // + psi(k_s) . psi(q_t)
+        }
+        // causal mask inside the diagonal tile (key 4g + i > query r) and keys
+        // past the end of a ragged chunk (selects, no branches)
+        const int lim = min(sa == m ? r - 4 * g : 3, nv - 1 - 16 * sa - 4 * g);   // last kept i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pt[i] = i <= lim ? pt[i] : 0.f;
+        uint2 hi, lo;
+        { const uint2 s_ = split_pk(pt[0], pt[1]); hi.x = s_.x; lo.x = s_.y; }
+        { const uint2 s_ = split_pk(pt[2], pt[3]); hi.y = s_.x; lo.y = s_.y; }
+        const int pair = pbase(m) + sa / 2, half = sa & 1;
+        *reinterpret_cast<uint2 *>(pop_at(pair, 0, lane) + 4 * half) = hi;
+        *reinterpret_cast<uint2 *>(pop_at(pair, 1, lane) + 4 * half) = lo;
+    };
+
+    // ================= A: every chunk of the group against the group-local
+    // state: numerators in registers, normalisers (one query tile per wave)
+    // in LDS; the local state runs through the chunks and ends as the
+    // group's partial state (group 0: including the carried-in state)
+    f32x4 O[CPG][4];
+    if (grp == 0) load_state(Z, S, a.z_in ? a.z_in + (int64_t)bh * D * D : nullptr, a.s_in ? a.s_in + (int64_t)bh * D : nullptr);
+    else load_state(Z, S, nullptr, nullptr);
+    if (w == 0) put_sops(S, 0);
+    issue(IC<0>{});
+    if constexpr (CPG > 1) issue(IC<1>{});
+    stage(IC<0>{});
+    static_for<CPG>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        if (c < nch) {
+            const int buf = c & 1, nv = nval_of(c);
+            __syncthreads();   // the stage is visible; the previous chunk is done with the other buffer and the scores
+            if constexpr (c + 2 < CPG) issue(IC<c + 2>{});
+            const bf16 *Kb = kbuf(buf), *Qb = qslot(c), *Vb = vbuf(buf);
+            // this wave's score tiles: three table entries (sa, m) per wave,
+            // 4 bits each; waves 2 and 3 repeat tile (0, 0), which writes the
+            // same values as wave 0
+            //   w0: (0,0) (0,3) (1,3)   w1: (0,1) (1,1) (2,3)
+            //   w2: (0,2) (1,2) (0,0)   w3: (2,2) (3,3) (0,0)
+            {
+                const uint32_t tab = (0x000000u | 0x03u << 8 | 0x13u << 16) * (w == 0) +
+                                     (0x01u | 0x11u << 8 | 0x23u << 16) * (w == 1) +
+                                     (0x02u | 0x12u << 8 | 0x00u << 16) * (w == 2) +
+                                     (0x22u | 0x33u << 8 | 0x00u << 16) * (w == 3);
+                bf16x8 ka[3][KS], qa[3][KS];   // every operand read before the products
+#pragma unroll
+                for (int i = 0; i < 3; ++i) {
+                    const int e = (tab >> (8 * i)) & 0xff;
+#pragma unroll
+                    for (int u = 0; u < KS; ++u) {
+                        ka[i][u] = nat8(Kb + swz<D>(16 * (e >> 4) + r, 32 * u + 8 * g));
+                        qa[i][u] = nat8(Qb + swz<D>(16 * (e & 15) + r, 32 * u + 8 * g));
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < 3; ++i) {
+                    const int e = (tab >> (8 * i)) & 0xff;
+                    score_tile(ka[i], qa[i], e >> 4, e & 15, nv);
+                }
+            }
+            // inter-chunk term of every query tile: column sums of Z plus
+            // Z^T psi(q)
+            bf16x8 zh[KS], zl[KS];
+            f32x4 cz;
+            state_ops(Z, zh, zl, cz);
+            f32x4 o[4];
+            {
+                bf16x8 qb[4][KS];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) q_ops(Qb, m, qb[m]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    o[m] = cz;
+#pragma unroll
+                    for (int u = 0; u < KS; ++u) {
+                        o[m] = mma8(o[m], zh[u], qb[m][u]);
+                        o[m] = mma8(o[m], zl[u], qb[m][u]);
+                    }
+                }
+            }
+            __syncthreads();   // the score operands are visible
+            // the next chunk's stage (its buffer's readers finished before
+            // this chunk's first barrier); its VALU work can overlap the
+            // products below
+            // (chunks past the group stage zeros, never read)
+            if constexpr (c + 1 < CPG) stage(IC<c + 1>{});
+            // intra-chunk term: V^T P^T over key tile pairs (2sg, 2sg + 1)
+            bf16x8 va[2];
+#pragma unroll
+            for (int sg = 0; sg < 2; ++sg) va[sg] = tr8<64>(Vb, 32 * sg, 16 * w, r, g);
+            {
+                bf16x8 pp[6][2];   // the 6 score operand pairs, read before the products
+#pragma unroll
+                for (int pr = 0; pr < 6; ++pr) { pp[pr][0] = nat8(pop_at(pr, 0, lane)); pp[pr][1] = nat8(pop_at(pr, 1, lane)); }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+#pragma unroll
+                    for (int sg = 0; 2 * sg <= m; ++sg) {
+                        o[m] = mma8(o[m], va[sg], pp[pbase(m) + sg][0]);
+                        o[m] = mma8(o[m], va[sg], pp[pbase(m) + sg][1]);
+                    }
+                    O[c][m] = o[m];
+                }
+            }
+            // normaliser of this wave's query tile w: sum_i S_i + S . psi(q) +
+            // sum_s P (the second key pair only for w >= 2: a zero operand
+            // otherwise)
+            {
+                bf16x8 qw[KS];
+                q_ops(Qb, w, qw);
+                f32x4 dn = sdot(buf, qw);
+                const int pw = pbase(w);
+                const bf16x8 z8 = {};
+                const bool two = w >= 2;
+#pragma unroll
+                for (int sg = 0; sg < 2; ++sg) {
+                    bf16x8 ph = nat8(pop_at(pw + (sg & (int)two), 0, lane)), pl = nat8(pop_at(pw + (sg & (int)two), 1, lane));
+                    if (sg == 1) { ph = two ? ph : z8; pl = two ? pl : z8; }
+                    dn = mma8(dn, ones8, ph);
+                    dn = mma8(dn, ones8, pl);
+                }
+                if (g == 0) den_s[c * C + 16 * w + r] = dn[0];
+            }
+            // state update: Z += psi(K)^T V + 1 (column sums of V)^T,
+            // S += psi(K)^T 1 + nv (every wave: no branch in the loop; wave 0's
+            // S is the one used), and wave 0 writes the S operands of the next
+            // chunk
+            f32x4 cv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int sg = 0; sg < 2; ++sg) cv = mma8(cv, ones8, va[sg]);
+            const float fn = (float)nv;
+            bf16x8 kt[JT][2];   // every operand read before the products
+#pragma unroll
+            for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+                for (int sg = 0; sg < 2; ++sg) kt[jt][sg] = cs_ktr8<D>(Kb, 32 * sg, jt, r, g);
+#pragma unroll
+            for (int jt = 0; jt < JT; ++jt) {
+#pragma unroll
+                for (int sg = 0; sg < 2; ++sg) {
+                    Z[jt] = mma8(Z[jt], kt[jt][sg], va[sg]);
+                    S[jt] = mma8(S[jt], kt[jt][sg], ones8);
+                }
+                Z[jt] += cv;
+                S[jt] += (f32x4){fn, fn, fn, fn};
+            }
+            // interleave the stage's VALU work with the products of this block
+#pragma unroll
+            for (int i = 0; i < 40; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+            }
+            if (w == 0 && c + 1 < nch) put_sops(S, buf ^ 1);
+        }
+    });
+
+    // ---- publish the group's partial state (all but the last group).  When
+    // every workgroup of the head runs on this XCD (the usual case), the slot
+    // stays in the XCD's L2; otherwise it is written through for every XCD.
+    const unsigned my_xcc = xcc_id();
+    if (!last) {
+        const rsrc_t sr = make_rsrc((const char *)a.part + (size_t)(hp * a.G + grp) * FS::BYTES, FS::BYTES);
+        auto put = [&](auto cpol) {
+            constexpr int CP = decltype(cpol)::value;
+#pragma unroll
+            for (int jt = 0; jt < JT; ++jt) cstore16<CP>(sr, FS::zoff(w, jt, lane), Z[jt]);
+#pragma unroll
+            for (int jt = 0; jt < JT; ++jt) cstore16<CP>(sr, (w == 0 && r == 0) ? FS::soff(jt, g) : OFF_NONE, S[jt]);
+        };
+        if (ids_on_one_xcd(bh * a.G * a.P, a.G * a.P, gridDim.x)) put(IC<CPOL_XCD>{});
+        else put(IC<CPOL_DEVICE>{});
+    }
+    // the flag: this workgroup's memory accesses (slot stores; group 0: its
+    // reads of the carried-in state) are complete.  A last group 0 sets it
+    // only to signal that s_in has been read.
+    if (!last || (grp == 0 && a.wait_s)) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_store(a.flags + (int64_t)hp * a.G + grp, a.epoch | my_xcc, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // ================= B: the state before the group (groups after the
+    // first): the sum of the published partial states of all earlier groups
+    // (S by wave 0 only)
+    if (grp > 0) {
+        load_state(Ze, Se, nullptr, nullptr);
+        const bool local = wait_flags(a.flags + (int64_t)hp * a.G, 1, grp, a.epoch, my_xcc, lane);
+        constexpr int LB = 4;   // slots in flight
+        const char *base = (const char *)a.part + (size_t)hp * a.G * FS::BYTES;
+        // x[jt] += the tiles at offset off(jt) of slots 0 .. grp - 1
+        auto sum_tiles = [&](auto cpol, f32x4 *x, auto off) {
+            constexpr int CP = decltype(cpol)::value;
+            for (int g0 = 0; g0 < grp; g0 += LB) {
+                f32x4 t[LB][JT];
+#pragma unroll
+                for (int u = 0; u < LB; ++u) {
+                    const bool live = g0 + u < grp;
+                    const rsrc_t sr = make_rsrc(base + (size_t)(live ? g0 + u : 0) * FS::BYTES, live ? FS::BYTES : 0);
+#pragma unroll
+                    for (int jt = 0; jt < JT; ++jt) t[u][jt] = dload16<CP>(sr, off(jt));
+                }
+#pragma unroll
+                for (int u = 0; u < LB; ++u)
+#pragma unroll
+                    for (int jt = 0; jt < JT; ++jt) x[jt] += t[u][jt];
+            }
+        };
+        auto sum = [&](auto cpol) {
+            sum_tiles(cpol, Ze, [&](int jt) { return FS::zoff(w, jt, lane); });
+            if (w == 0) sum_tiles(cpol, Se, [&](int jt) { return FS::soff(jt, g); });
+        };
+        if (local) sum(IC<CPOL_XCD>{});
+        else sum(IC<CPOL_DEVICE>{});
+        // S operands of the state before the group, into the S buffer the
+        // last chunk did not read
+        const int eb = nch & 1;
+        if (w == 0) put_sops(Se, eb);
+        __syncthreads();
+
+        // ================= C: add the state before the group to every chunk:
+        // numerators += column sums of Ze + Ze^T psi(q); normalisers (own
+        // query tile) += sum_i Se_i + Se . psi(q)
+        bf16x8 zh[KS], zl[KS];
+        f32x4 cz;
+        state_ops(Ze, zh, zl, cz);
+        static_for<CPG>([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            if (c < nch) {
+                const bf16 *Qb = qslot(c);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    bf16x8 qb[KS];
+                    q_ops(Qb, m, qb);
+                    f32x4 o = O[c][m] + cz;
+#pragma unroll
+                    for (int u = 0; u < KS; ++u) {
+                        o = mma8(o, zh[u], qb[u]);
+                        o = mma8(o, zl[u], qb[u]);
+                    }
+                    O[c][m] = o;
+                    if (m == w) {
+                        const f32x4 dn = sdot(eb, qb);
+                        if (g == 0) den_s[c * C + 16 * m + r] += dn[0];
+                    }
+                }
+            }
+        });
+    }
+    __syncthreads();   // every normaliser is complete
+    // ---- the outputs
+    static_for<CPG>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        if (c < nch) {
+            const int t0 = t_begin + c * C, nv = nval_of(c);
+            const rsrc_t orr = ov.at(t0);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int t = 16 * m + r;
+                const float inv = __builtin_amdgcn_rcpf(den_s[c * C + t] + a.eps);
+                bstore16(orr, t < nv ? (uint32_t)(t * ov.rs + (16 * w + 4 * g) * 4) : OFF_NONE, O[c][m] * inv);
+            }
+        }
+    });
+    // ---- the final state (last group): local state + state before the group
+    if (last) {
+        if (a.wait_s && s_writer) (void)wait_flags(a.flags + (int64_t)bh * a.P * a.G, a.G, a.P, a.epoch, my_xcc, lane);
+        float *zo = a.z_out ? a.z_out + (int64_t)bh * D * D + p * DV + 16 * w + r : nullptr;
+        float *so = (a.s_out && s_writer && w == 0 && r == 0) ? a.s_out + (int64_t)bh * D : nullptr;
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int dim = cs_dim(jt, 4 * g + i);
+                const float zf = grp > 0 ? Z[jt][i] + Ze[jt][i] : Z[jt][i];
+                const float sf = grp > 0 ? S[jt][i] + Se[jt][i] : S[jt][i];
+                if (zo) zo[(int64_t)dim * D] = zf;
+                if (so) so[dim] = sf;
+            }
+    }
+}
+
 // One recurrent step for every head: Z += phi(k) v^T, S += phi(k),
 // out = phi(q)^T Z / (phi(q) . S + eps).  Pure streaming over Z (read, update,
 // write back once); every state element is read and written by one thread.
@@ -1739,7 +2294,11 @@ la_status la_causal_fwd(const void *q, la_strides sq, const void *k, la_strides 
     a.epoch = next_epoch();
     a.wait_s = (s_out && s_out == s_in && pl.P > 1) ? 1 : 0;
     const bool resident = pl.C == 64 && pl.L <= res_cpg(f32, d) * pl.C;
-    dispatch(f32, d, pl.C, want_out ? (resident ? 4 : 1) : 3, a, (int)(BH * pl.P * pl.G), stream);
+    const int nwg = (int)(BH * pl.P * pl.G);
+    if (LA_COLUMN_SPLIT && want_out && resident && !f32 && d == 64)
+        hipLaunchKernelGGL((k_cs_fwd<64, res_cpg(false, 64)>), dim3(nwg), dim3(NTHR), 0, stream, a);
+    else
+        dispatch(f32, d, pl.C, want_out ? (resident ? 4 : 1) : 3, a, nwg, stream);
     return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }
 
