@@ -1726,11 +1726,6 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
                 }
             }
             __syncthreads();   // the score operands are visible
-            // the next chunk's stage (its buffer's readers finished before
-            // this chunk's first barrier); its VALU work can overlap the
-            // products below
-            // (chunks past the group stage zeros, never read)
-            if constexpr (c + 1 < CPG) stage(IC<c + 1>{});
             // intra-chunk term: V^T P^T over key tile pairs (2sg, 2sg + 1)
             bf16x8 va[2];
 #pragma unroll
@@ -1791,11 +1786,17 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
                 Z[jt] += cv;
                 S[jt] += (f32x4){fn, fn, fn, fn};
             }
-            // interleave the stage's VALU work with the products of this block
+            // the next chunk's stage (its buffer's readers finished before
+            // this chunk's first barrier; chunks past the group stage zeros,
+            // never read).  It comes after this block's operand reads, so its
+            // VALU work can be scheduled between the products: the reads
+            // first, then one product per six VALU.
+            if constexpr (c + 1 < CPG) stage(IC<c + 1>{});
+            __builtin_amdgcn_sched_group_barrier(0x100, 32, 0);
 #pragma unroll
-            for (int i = 0; i < 40; ++i) {
+            for (int i = 0; i < 44; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
             }
             if (w == 0 && c + 1 < nch) put_sops(S, buf ^ 1);
         }
@@ -1925,6 +1926,217 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
                 if (zo) zo[(int64_t)dim * D] = zf;
                 if (so) so[dim] = sf;
             }
+    }
+}
+
+// ================================================================ non-causal, column split
+// (bf16 inputs, 64-token chunks, DV = 64 columns per workgroup, each wave 16)
+//
+// k_cs_state: the partial state of one share of the tokens, Z[:, block] =
+// sum_t phi(k_t) v_t^T and S = sum_t phi(k_t), written to slot grp of
+// (head, column block) in the layout of the state tensors ([D][DV] row major,
+// then S [D]).  phi = 1 + psi: Z += psi(K)^T V + 1 (column sums of V)^T,
+// S += psi(K)^T 1 + tokens, with psi(K) in bf16 and V as loaded.  Share grp
+// of G takes the 64-token chunks grp, grp + G, grp + 2G, ... (the G
+// workgroups of a head read neighbouring chunks at any one time).
+template <int D>
+__global__ void __launch_bounds__(NTHR, 4) k_cs_state(const Args a)
+{
+    typedef CSGeo<D> T;
+    constexpr int C = T::C, DV = T::DV, JT = T::JT, VPR = T::VPR, NK = T::NK, NV = T::NV;
+    constexpr int SL = Slot<D, DV>::SIZE;
+    __shared__ __attribute__((aligned(16))) bf16 sm[2 * C * D + 2 * C * DV];   // psi(K) [2][C][D], V [2][C][DV]
+    const int tid = threadIdx.x, lane = tid % WAVE, r = lane % 16, g = lane / 16;
+    const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    const int p = wg % a.P, rest = wg / a.P, grp = rest % a.G, bh = rest / a.G;
+    const int b = bh / a.H, h = bh % a.H;
+    const int hp = bh * a.P + p;
+    const int nall = (a.N + C - 1) / C;                    // chunks of the sequence
+    const int nch = grp < nall ? (nall - grp + a.G - 1) / a.G : 0;   // chunks of this share
+    auto t0_of = [&](int ch) { return (grp + ch * a.G) * C; };
+    const RowView kv{(const char *)a.k + (b * a.skb + h * a.skh) * 2, a.skn * 2, (a.N - 1) * a.skn * 2 + D * 2};
+    const RowView vv{(const char *)a.v + (b * a.svb + h * a.svh + p * DV) * 2, a.svn * 2,
+                     (a.N - 1) * a.svn * 2 + DV * 2};
+    uint32_t ko[NK], vo[NV];
+#pragma unroll
+    for (int it = 0; it < NK; ++it) {
+        const int item = tid + it * NTHR;
+        ko[it] = (uint32_t)((item / VPR) * kv.rs + (item % VPR) * 16);
+    }
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+        const int item = tid + it * NTHR;
+        vo[it] = (uint32_t)((item / 8) * vv.rs + (item % 8) * 16);
+    }
+    u32x4 Kr[2][NK], Vr[2][NV];   // chunks ch + 1 and ch + 2 in flight
+    auto issue = [&](int ch, int slot) {
+        const int t0 = ch < nch ? t0_of(ch) : 0;
+        const rsrc_t kr = kv.at(t0, ch < nch), vr = vv.at(t0, ch < nch);
+#pragma unroll
+        for (int it = 0; it < NK; ++it) Kr[slot][it] = bload16(kr, ko[it]);
+#pragma unroll
+        for (int it = 0; it < NV; ++it) Vr[slot][it] = bload16(vr, vo[it]);
+    };
+    bf16x8 ones8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones8[e] = (bf16)1.f;
+    f32x4 Z[JT], S[JT];
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) { Z[jt] = (f32x4){0.f, 0.f, 0.f, 0.f}; S[jt] = Z[jt]; }
+    float ntok = 0.f;
+    // one chunk from register slot `slot` through stage buffer `buf`
+    auto step = [&](int ch, int slot, int buf) {
+        bf16 *Kb = sm + buf * C * D, *Vb = sm + 2 * C * D + buf * C * DV;
+#pragma unroll
+        for (int it = 0; it < NK; ++it) {
+            const int item = tid + it * NTHR, row = item / VPR, vec = item % VPR;
+            *reinterpret_cast<u32x4 *>(Kb + swz<D>(row, vec * 8)) = cs_psi8(Kr[slot][it]);
+        }
+#pragma unroll
+        for (int it = 0; it < NV; ++it) {
+            const int item = tid + it * NTHR, row = item / 8, vec = item % 8;
+            *reinterpret_cast<u32x4 *>(Vb + swz<64>(row, vec * 8)) = Vr[slot][it];
+        }
+        issue(ch + 2, slot);
+        __syncthreads();   // the stage is visible; the other buffer's readers are done
+        bf16x8 va[2];
+#pragma unroll
+        for (int sg = 0; sg < 2; ++sg) va[sg] = tr8<64>(Vb, 32 * sg, 16 * w, r, g);
+        bf16x8 kt[JT][2];
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+            for (int sg = 0; sg < 2; ++sg) kt[jt][sg] = cs_ktr8<D>(Kb, 32 * sg, jt, r, g);
+        f32x4 cv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sg = 0; sg < 2; ++sg) cv = mma8(cv, ones8, va[sg]);
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+#pragma unroll
+            for (int sg = 0; sg < 2; ++sg) {
+                Z[jt] = mma8(Z[jt], kt[jt][sg], va[sg]);
+                S[jt] = mma8(S[jt], kt[jt][sg], ones8);
+            }
+            Z[jt] += cv;
+        }
+        ntok += ch < nch ? (float)min(C, a.N - t0_of(ch)) : 0.f;   // 0 for the empty step
+    };
+    issue(0, 0);
+    issue(1, 1);
+    for (int ch = 0; ch < nch; ch += 2) {   // an odd count runs one empty step (zeros)
+        step(ch, 0, 0);
+        step(ch + 1, 1, 1);
+    }
+    // the slot: Z in [D][DV] layout, S (wave 0)
+    float *slot = a.part + ((int64_t)hp * a.NS + grp) * SL;
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int dim = cs_dim(jt, 4 * g + i);
+            slot[dim * DV + 16 * w + r] = Z[jt][i];
+            if (w == 0 && r == 0) slot[DV * D + dim] = S[jt][i] + ntok;
+        }
+}
+
+// k_cs_apply: out_t = phi(q_t)^T Z / (phi(q_t) . S + eps) for a group of
+// tokens against the reduced global state (fin [hp] in the slot layout):
+// numerator = sum_i Z[i][:] + Z^T psi(q_t), normaliser = sum_i S_i +
+// S . psi(q_t), with Z and S as bf16 hi + lo operands.  Every wave computes
+// the normalisers of all queries (no exchange).
+template <int D>
+__global__ void __launch_bounds__(NTHR, 4) k_cs_apply(const Args a)
+{
+    typedef CSGeo<D> T;
+    constexpr int C = T::C, DV = T::DV, JT = T::JT, KS = T::KS, VPR = T::VPR, NK = T::NK;
+    constexpr int SL = Slot<D, DV>::SIZE;
+    __shared__ __attribute__((aligned(16))) bf16 sm[2 * C * D];   // psi(Q) [2][C][D]
+    const int tid = threadIdx.x, lane = tid % WAVE, r = lane % 16, g = lane / 16;
+    const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    const int p = wg % a.P, rest = wg / a.P, grp = rest % a.G, bh = rest / a.G;
+    const int b = bh / a.H, h = bh % a.H;
+    const int hp = bh * a.P + p;
+    const int t_begin = grp * a.L, t_end = min(t_begin + a.L, a.N);
+    const int nch = (t_end - t_begin + C - 1) / C;
+    const RowView qv{(const char *)a.q + (b * a.sqb + h * a.sqh) * 2, a.sqn * 2, (a.N - 1) * a.sqn * 2 + D * 2};
+    const RowView ov{(const char *)(a.out + b * a.sob + h * a.soh + p * DV), a.son * 4, (a.N - 1) * a.son * 4 + DV * 4};
+    uint32_t qo[NK];
+#pragma unroll
+    for (int it = 0; it < NK; ++it) {
+        const int item = tid + it * NTHR;
+        qo[it] = (uint32_t)((item / VPR) * qv.rs + (item % VPR) * 16);
+    }
+    u32x4 Qr[2][NK];
+    auto issue = [&](int ch, int slot) {
+        const rsrc_t qr = qv.at(t_begin + ch * C, ch < nch);
+#pragma unroll
+        for (int it = 0; it < NK; ++it) Qr[slot][it] = bload16(qr, qo[it]);
+    };
+    issue(0, 0);
+    issue(1, 1);
+    bf16x8 ones8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones8[e] = (bf16)1.f;
+    // the state's operands: Z (this wave's 16 columns) and S, hi + lo, and
+    // their sums over the key dims
+    const float *fin = a.fin + (int64_t)hp * SL;
+    bf16x8 zh[KS], zl[KS], sh[KS], sl[KS];
+    f32x4 cz = {0.f, 0.f, 0.f, 0.f}, cs = cz;
+    {
+        f32x4 Z[JT], S[JT];
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int dim = cs_dim(jt, 4 * g + i);
+                Z[jt][i] = fin[dim * DV + 16 * w + r];
+                S[jt][i] = fin[DV * D + dim];
+            }
+#pragma unroll
+        for (int u = 0; u < KS; ++u) {
+            cs_split(Z[2 * u], Z[2 * u + 1], zh[u], zl[u]);
+            cs_split(S[2 * u], S[2 * u + 1], sh[u], sl[u]);
+            cz = mma8(cz, zh[u], ones8);
+            cz = mma8(cz, zl[u], ones8);
+            cs = mma8(cs, sh[u], ones8);
+            cs = mma8(cs, sl[u], ones8);
+        }
+    }
+    auto step = [&](int ch, int slot, int buf) {
+        bf16 *Qb = sm + buf * C * D;
+#pragma unroll
+        for (int it = 0; it < NK; ++it) {
+            const int item = tid + it * NTHR, row = item / VPR, vec = item % VPR;
+            *reinterpret_cast<u32x4 *>(Qb + swz<D>(row, vec * 8)) = cs_psi8(Qr[slot][it]);
+        }
+        issue(ch + 2, slot);
+        __syncthreads();   // the stage is visible; the other buffer's readers are done
+        const int t0 = t_begin + ch * C, nv = min(C, t_end - t0);
+        const rsrc_t orr = ov.at(t0);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            bf16x8 qb[KS];
+#pragma unroll
+            for (int u = 0; u < KS; ++u) qb[u] = nat8(Qb + swz<D>(16 * m + r, 32 * u + 8 * g));
+            f32x4 o = cz, dn = cs;
+#pragma unroll
+            for (int u = 0; u < KS; ++u) {
+                o = mma8(o, zh[u], qb[u]);
+                o = mma8(o, zl[u], qb[u]);
+                dn = mma8(dn, sh[u], qb[u]);
+                dn = mma8(dn, sl[u], qb[u]);
+            }
+            // dn holds the normaliser of query r in every row
+            const float inv = __builtin_amdgcn_rcpf(dn[0] + a.eps);
+            const int t = 16 * m + r;
+            bstore16(orr, t < nv ? (uint32_t)(t * ov.rs + (16 * w + 4 * g) * 4) : OFF_NONE, o * inv);
+        }
+    };
+    for (int ch = 0; ch < nch; ch += 2) {
+        step(ch, 0, 0);
+        if (ch + 1 < nch) step(ch + 1, 1, 1);
     }
 }
 
@@ -2361,12 +2573,15 @@ la_status la_noncausal_fwd(const void *q, la_strides sq, const void *k, la_strid
     // 1) partial states of the token groups, 2) their sum per head in group
     // order, 3) every query against the global state
     a.G = pl.G; a.L = pl.L; a.slot0 = 0;
-    dispatch(f32, d, pl.C, 0, a, (int)(BH * pl.P * pl.G), stream);
+    const bool cs = LA_COLUMN_SPLIT && !f32 && d == 64 && pl.C == 64;
+    if (cs) hipLaunchKernelGGL((k_cs_state<64>), dim3((unsigned)(BH * pl.P * pl.G)), dim3(NTHR), 0, stream, a);
+    else dispatch(f32, d, pl.C, 0, a, (int)(BH * pl.P * pl.G), stream);
     launch_slots(d, a, BH, pl.P, pl.G, 2, stream);
     const int la = pl.C * 4;
     a.L = la;
     a.G = (N + la - 1) / la;
-    dispatch(f32, d, pl.C, 2, a, (int)(BH * pl.P * a.G), stream);
+    if (cs) hipLaunchKernelGGL((k_cs_apply<64>), dim3((unsigned)(BH * pl.P * a.G)), dim3(NTHR), 0, stream, a);
+    else dispatch(f32, d, pl.C, 2, a, (int)(BH * pl.P * a.G), stream);
     return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }
 
