@@ -17,26 +17,28 @@
 //
 // Design for CDNA4 (gfx950), in brief:
 //  * Causal forward, one launch: a workgroup owns (head, block of DV value
-//    columns, group of tokens).  It first computes its group's own partial
-//    state and publishes it (device-coherent stores and a per-call 64-bit tag
-//    as the flag); it then sums the published states of the earlier groups
-//    of its head (the state before the group) and runs the chunk loop from
-//    it.  Workgroups only wait for lower-indexed ones of the same XCD, which
-//    the hardware dispatches first.
-//  * Inside the chunk loop the 4 waves share the state through LDS (Z^T as
-//    bf16 hi + lo parts, S as an extra row) and each wave owns one 16-row
-//    query tile; phi(K) and V are staged in LDS per 64-token chunk.  When the
-//    group is short enough, every q, k, v load of the group is issued up
-//    front into registers, so the loop itself only stores.
+//    columns, group of tokens).  It publishes its group's partial state
+//    (device-visible stores, then a per-call 64-bit tag as the flag), and sums
+//    the published states of the earlier groups of its head (the state before
+//    the group).  Workgroups only wait for lower-indexed ones of the same XCD,
+//    which the hardware dispatches first.
+//  * bf16 inputs at d = 64 (k_cs_fwd): each of the 4 waves owns 16 value
+//    columns for the whole group, so its slice of the state never leaves its
+//    registers.  Every chunk is first computed against the group-local state
+//    while the loads stream in; once the earlier groups' state is known it is
+//    added to the held numerators and normalisers, and the outputs are stored
+//    once.  Only psi = phi - 1 (bf16) enters the MFMAs; the all-ones part of
+//    phi is carried in fp32 (see k_cs_fwd).
+//  * Other dtype / d pairs (k_chunk_fwd): the 4 waves share the state through
+//    LDS (Z^T as bf16 hi + lo parts, S as an extra row) and each wave owns one
+//    16-row query tile; the published state is summed before the chunk loop.
 //  * All products run on 16x16 MFMA tiles in the transposed orientation
 //    (rows = value column or key token, columns = query token): the score
 //    tile P^T feeds P V directly, and the accumulator layout (lane group g
 //    holds rows 4g..4g+3) is the operand layout of the next product.  The
 //    gfx950 LDS transpose read supplies token-major operands.
-//  * bf16 inputs: phi(q), phi(k), v are bf16 operands with fp32 accumulation;
-//    the fp32 sums fed back as operands (scores, state) and phi itself where
-//    precision matters are split into bf16 hi + lo parts.  fp32 inputs use
-//    fp32 MFMA.
+//  * The fp32 sums fed back as operands (scores, state) are split into bf16
+//    hi + lo parts; fp32 inputs use fp32 MFMA.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
