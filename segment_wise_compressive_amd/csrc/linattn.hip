@@ -168,14 +168,6 @@ __device__ __forceinline__ int xcd_remap(int id, int n)
     if ((n & 7) != 0) return id;
     return (id & 7) * (n >> 3) + (id >> 3);
 }
-// Whether logical ids first .. first + count - 1 all run on one XCD under
-// xcd_remap (each XCD holds a contiguous range of n / 8 logical ids).
-__device__ __forceinline__ bool ids_on_one_xcd(int first, int count, int n)
-{
-    if ((n & 7) != 0) return count == 1;
-    const int per = n >> 3;
-    return first / per == (first + count - 1) / per;
-}
 
 // ------------------------------------------------------------------ kernel arguments
 struct Args {
@@ -816,13 +808,6 @@ __device__ __forceinline__ void dstore16(rsrc_t r, uint32_t off, f32x4 v)
 {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, CPOL_DEVICE);
 }
-// store with the cache policy CPOL (CPOL_XCD: into the XCD's L2, for readers
-// on the same XCD only)
-template <int CPOL>
-__device__ __forceinline__ void cstore16(rsrc_t r, uint32_t off, f32x4 v)
-{
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, CPOL);
-}
 template <int CPOL>
 __device__ __forceinline__ f32x4 dload16(rsrc_t r, uint32_t off)
 {
@@ -859,8 +844,9 @@ template <int D, int DV> struct FSlot {
 #define LA_COLUMN_SPLIT 1
 #endif
 
-// Spin limit of a flag wait (each poll sleeps ~1 us): a call whose flags never
-// arrive (a bug, or memory not meant for this call) ends instead of hanging.
+// Spin limit of a flag wait (a poll is a memory round trip plus a short
+// sleep): a call whose flags never arrive (a bug, or memory not meant for
+// this call) ends instead of hanging.
 constexpr int SPIN_LIMIT = 1 << 20;
 
 // A flag holds the call's tag (low 4 bits zero) plus the XCD index of the
@@ -878,7 +864,7 @@ __device__ __forceinline__ bool wait_flags(const unsigned long long *base, int s
         for (int spin = 0; spin < SPIN_LIMIT; ++spin) {
             v = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (__all(i >= n || (v & ~0xfull) == epoch)) break;
-            __builtin_amdgcn_s_sleep(16);
+            __builtin_amdgcn_s_sleep(2);
         }
         local = local && __all(i >= n || (v & 0xfull) == xcc);
     }
@@ -1432,11 +1418,12 @@ template <int D> struct CSGeo {
     // (rows swizzled, swz); the score operands [6 pairs][hi, lo][64 lanes][8];
     // the S operands [2][hi, lo][KS][4 lane groups][8]; psi(Q) of every chunk
     // of the group [CPG][C][D] (swizzled); then fp32: the normalisers
-    // [CPG][C] and the sums of S [2].
+    // [CPG][C], the per-wave sums of S [2][4], the row sums of psi(q) and of
+    // psi(k) [2][C] each.
     static constexpr int OK = 0, OV = 2 * C * D, OP = OV + 2 * C * DV, OSO = OP + 6 * 2 * 64 * 8;
     static constexpr int OQ = OSO + 2 * 2 * KS * 4 * 8;
     static constexpr int bf16_elems(int cpg) { return OQ + cpg * C * D; }
-    static constexpr int lds_bytes(int cpg) { return bf16_elems(cpg) * 2 + (cpg * C + 4) * 4; }
+    static constexpr int lds_bytes(int cpg) { return bf16_elems(cpg) * 2 + (cpg * C + 8 + 4 * C) * 4; }
     static_assert(NK * NTHR == C * VPR && NV * NTHR == C * DV / 8, "whole vectors per thread");
 };
 __device__ __forceinline__ int cs_dim(int jt, int m) { return 32 * (jt >> 1) + 8 * (m >> 2) + 4 * (jt & 1) + (m & 3); }
@@ -1477,7 +1464,22 @@ __device__ __forceinline__ float psi(float x)
     const float e = __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(x * 1.44269504088896340736f), 0.f, 1.f);
     return __builtin_elementwise_maximum(x, e - 1.f);
 }
-// psi of 8 packed bf16 values rounded to bf16 (nearest even)
+// psi of 8 packed bf16 values rounded to bf16 (nearest even); `sum` += the
+// sum of the values before rounding (it enters only the scores, where the
+// difference, below 2^-9 of each |psi|, is far below their split precision)
+__device__ __forceinline__ u32x4 cs_psi8(u32x4 x, float &sum)
+{
+    float f[8];
+    Vec<false>::to_float(x, f);
+    u32x4 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float a = psi(f[2 * e]), b = psi(f[2 * e + 1]);
+        y[e] = pk_bf16(a, b);
+        sum += a + b;
+    }
+    return y;
+}
 __device__ __forceinline__ u32x4 cs_psi8(u32x4 x)
 {
     float f[8];
@@ -1498,7 +1500,8 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
     __shared__ __attribute__((aligned(16))) char smem_raw[T::lds_bytes(CPG)];
     bf16 *sm = reinterpret_cast<bf16 *>(smem_raw);
     float *den_s = reinterpret_cast<float *>(smem_raw + T::bf16_elems(CPG) * 2);   // [CPG][C]
-    float *ssum_s = den_s + CPG * C;                                                // [2]
+    float *ssum_s = den_s + CPG * C;                                                // [2][4]
+    float *qsum_s = ssum_s + 8, *ksum_s = qsum_s + 2 * C;                           // [2][C] each
     auto kbuf = [&](int buf) { return sm + T::OK + buf * C * D; };
     auto vbuf = [&](int buf) { return sm + T::OV + buf * C * DV; };
     auto qslot = [&](int c) { return sm + T::OQ + c * C * D; };
@@ -1558,8 +1561,19 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
 #pragma unroll
         for (int it = 0; it < NK; ++it) {
             const int item = tid + it * NTHR, row = item / VPR, vec = item % VPR;
-            *reinterpret_cast<u32x4 *>(Kb + swz<D>(row, vec * 8)) = cs_psi8(Kr[c][it]);
-            *reinterpret_cast<u32x4 *>(Qb + swz<D>(row, vec * 8)) = cs_psi8(Qr[c][it]);
+            float ks = 0.f, qs = 0.f;
+            *reinterpret_cast<u32x4 *>(Kb + swz<D>(row, vec * 8)) = cs_psi8(Kr[c][it], ks);
+            *reinterpret_cast<u32x4 *>(Qb + swz<D>(row, vec * 8)) = cs_psi8(Qr[c][it], qs);
+            // row sums over the VPR consecutive lanes of the row
+#pragma unroll
+            for (int m = 1; m < VPR; m <<= 1) {
+                ks += __shfl_xor(ks, m);
+                qs += __shfl_xor(qs, m);
+            }
+            if (vec == 0) {
+                ksum_s[buf * C + row] = ks;
+                qsum_s[buf * C + row] = qs;
+            }
         }
 #pragma unroll
         for (int it = 0; it < NV; ++it) {
@@ -1571,20 +1585,22 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
     bf16x8 ones8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones8[e] = (bf16)1.f;
-    // ---- the wave's state: Z[dims][16w + r]; wave 0 also holds S[dims] (every
-    // column of an S tile holds S).  First the group-local running state
-    // (group 0: from the carried-in state), then the state before the group
-    // (Ze, Se).
-    f32x4 Z[JT], S[JT], Ze[JT], Se[JT];
+    // ---- the wave's state: Z[dims][16w + r] over all key dims, and the S
+    // tiles jt = w + NWAVE m (SPW of them; every column of an S tile holds
+    // S).  First the group-local running state (group 0: from the carried-in
+    // state), then the state before the group (Ze, Se).
+    constexpr int SPW = JT / NWAVE;
+    static_assert(JT % NWAVE == 0, "S tiles split evenly over the waves");
+    f32x4 Z[JT], S[SPW], Ze[JT], Se[SPW];
     auto load_state = [&](f32x4 *z4, f32x4 *s4, const float *z, const float *s) {
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int dim = cs_dim(jt, 4 * g + i);
-                z4[jt][i] = z ? z[(int64_t)dim * D + p * DV + 16 * w + r] : 0.f;
-                s4[jt][i] = s ? s[dim] : 0.f;
-            }
+            for (int i = 0; i < 4; ++i) z4[jt][i] = z ? z[(int64_t)cs_dim(jt, 4 * g + i) * D + p * DV + 16 * w + r] : 0.f;
+#pragma unroll
+        for (int m = 0; m < SPW; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s4[m][i] = s ? s[cs_dim(w + NWAVE * m, 4 * g + i)] : 0.f;
     };
     // hi + lo operands of a state, and its sums over the key dims (every row
     // of the result: sum_i z[i][column])
@@ -1597,26 +1613,33 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
             zsum = mma8(zsum, zl[u], ones8);
         }
     };
-    // S operands for the normalisers, shared through LDS by wave 0 (the hi/lo
-    // operand of a lane depends only on its lane group g): [2][hi, lo][KS][g]
+    // S operands for the normalisers, shared through LDS (the hi/lo operand
+    // of a lane depends only on its lane group g): [2][hi, lo][KS][g][8];
+    // every wave writes the halves of its S tiles and the sum of their values
     auto sops_at = [&](int buf, int hl, int u, int gg) { return sm + T::OSO + (((buf * 2 + hl) * KS + u) * 4 + gg) * 8; };
-    auto put_sops = [&](const f32x4 *s4, int buf) {   // wave 0
-        bf16x8 sh[KS], sl[KS];
-        f32x4 ss;
-        state_ops(s4, sh, sl, ss);
-        if (r == 0) {
+    auto put_sops = [&](const f32x4 *s4, int buf) {
+        float part = 0.f;
 #pragma unroll
-            for (int u = 0; u < KS; ++u) {
-                *reinterpret_cast<bf16x8 *>(sops_at(buf, 0, u, g)) = sh[u];
-                *reinterpret_cast<bf16x8 *>(sops_at(buf, 1, u, g)) = sl[u];
+        for (int m = 0; m < SPW; ++m) {
+            const int jt = w + NWAVE * m;
+            uint2 hi, lo;
+            { const uint2 s_ = split_pk(s4[m][0], s4[m][1]); hi.x = s_.x; lo.x = s_.y; }
+            { const uint2 s_ = split_pk(s4[m][2], s4[m][3]); hi.y = s_.x; lo.y = s_.y; }
+            if (r == 0) {
+                *reinterpret_cast<uint2 *>(sops_at(buf, 0, jt >> 1, g) + 4 * (jt & 1)) = hi;
+                *reinterpret_cast<uint2 *>(sops_at(buf, 1, jt >> 1, g) + 4 * (jt & 1)) = lo;
             }
+            part += (s4[m][0] + s4[m][1]) + (s4[m][2] + s4[m][3]);
         }
-        if (lane == 0) ssum_s[buf] = ss[0];
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        if (lane == 0) ssum_s[buf * 4 + w] = part;
     };
-    // the normaliser of query tile m: ssum + S . psi(q) + (intra, by the caller)
+    // the normaliser of query tile m: sum S + S . psi(q) + (intra, by the caller)
     auto sdot = [&](int buf, const bf16x8 *qb) {
         f32x4 dn;
-        const float s0 = ssum_s[buf];
+        const f32x4 s4 = *reinterpret_cast<const f32x4 *>(ssum_s + buf * 4);
+        const float s0 = (s4[0] + s4[1]) + (s4[2] + s4[3]);
         dn = (f32x4){s0, s0, s0, s0};
 #pragma unroll
         for (int u = 0; u < KS; ++u) {
@@ -1640,14 +1663,13 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
         const int which = tid / WAVE, ln = tid % WAVE;   // (pair 0 | pair 3) x (hi | lo)
         *reinterpret_cast<uint2 *>(pop_at(which < 2 ? 0 : 3, which & 1, ln) + 4) = make_uint2(0u, 0u);
     }
-    auto score_tile = [&](const bf16x8 *ka, const bf16x8 *qb, int sa, int m, int nv) {
-        f32x4 pt = {(float)D, (float)D, (float)D, (float)D};
+    auto score_tile = [&](const bf16x8 *ka, const bf16x8 *qb, int sa, int m, int nv, int buf) {
+        // d + sum psi(q_t) + sum psi(k_s) (row sums from the stage), then
+        // + psi(k_s) . psi(q_t)
+        f32x4 pt = *reinterpret_cast<const f32x4 *>(ksum_s + buf * C + 16 * sa + 4 * g) +
+                   ((float)D + qsum_s[buf * C + 16 * m + r]);
 #pragma unroll
-        for (int u = 0; u < KS; ++u) {
-            pt = mma8(pt, ka[u], ones8);   // + sum psi(k_s)
-            pt = mma8(pt, ones8, qb[u]);   // + sum psi(q_t)
-            pt = mma8(pt, ka[u], qb[u]);   // + psi(k_s) . psi(q_t)
-        }
+        for (int u = 0; u < KS; ++u) pt = mma8(pt, ka[u], qb[u]);
         // causal mask inside the diagonal tile (key 4g + i > query r) and keys
         // past the end of a ragged chunk (selects, no branches)
         const int lim = min(sa == m ? r - 4 * g : 3, nv - 1 - 16 * sa - 4 * g);   // last kept i
@@ -1668,10 +1690,11 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
     f32x4 O[CPG][4];
     if (grp == 0) load_state(Z, S, a.z_in ? a.z_in + (int64_t)bh * D * D : nullptr, a.s_in ? a.s_in + (int64_t)bh * D : nullptr);
     else load_state(Z, S, nullptr, nullptr);
-    if (w == 0) put_sops(S, 0);
+    put_sops(S, 0);
+    // chunk 0 first for every workgroup (it gates the start), then chunk 1
     issue(IC<0>{});
-    if constexpr (CPG > 1) issue(IC<1>{});
     stage(IC<0>{});
+    if constexpr (CPG > 1) issue(IC<1>{});
     static_for<CPG>([&](auto cc) {
         constexpr int c = decltype(cc)::value;
         if (c < nch) {
@@ -1703,7 +1726,7 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
 #pragma unroll
                 for (int i = 0; i < 3; ++i) {
                     const int e = (tab >> (8 * i)) & 0xff;
-                    score_tile(ka[i], qa[i], e >> 4, e & 15, nv);
+                    score_tile(ka[i], qa[i], e >> 4, e & 15, nv, buf);
                 }
             }
             // inter-chunk term of every query tile: column sums of Z plus
@@ -1752,7 +1775,7 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
             {
                 bf16x8 qw[KS];
                 q_ops(Qb, w, qw);
-                f32x4 dn = sdot(buf, qw);
+                f32x4 dn = sdot(buf, qw), dp = {0.f, 0.f, 0.f, 0.f};   // two independent chains
                 const int pw = pbase(w);
                 const bf16x8 z8 = {};
                 const bool two = w >= 2;
@@ -1760,15 +1783,15 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
                 for (int sg = 0; sg < 2; ++sg) {
                     bf16x8 ph = nat8(pop_at(pw + (sg & (int)two), 0, lane)), pl = nat8(pop_at(pw + (sg & (int)two), 1, lane));
                     if (sg == 1) { ph = two ? ph : z8; pl = two ? pl : z8; }
-                    dn = mma8(dn, ones8, ph);
-                    dn = mma8(dn, ones8, pl);
+                    dp = mma8(dp, ones8, ph);
+                    dp = mma8(dp, ones8, pl);
                 }
+                dn += dp;
                 if (g == 0) den_s[c * C + 16 * w + r] = dn[0];
             }
-            // state update: Z += psi(K)^T V + 1 (column sums of V)^T,
-            // S += psi(K)^T 1 + nv (every wave: no branch in the loop; wave 0's
-            // S is the one used), and wave 0 writes the S operands of the next
-            // chunk
+            // state update: Z += psi(K)^T V + 1 (column sums of V)^T; the
+            // wave's S tiles += psi(K)^T 1 + nv, and their share of the S
+            // operands of the next chunk
             f32x4 cv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int sg = 0; sg < 2; ++sg) cv = mma8(cv, ones8, va[sg]);
@@ -1781,12 +1804,14 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
 #pragma unroll
             for (int jt = 0; jt < JT; ++jt) {
 #pragma unroll
-                for (int sg = 0; sg < 2; ++sg) {
-                    Z[jt] = mma8(Z[jt], kt[jt][sg], va[sg]);
-                    S[jt] = mma8(S[jt], kt[jt][sg], ones8);
-                }
+                for (int sg = 0; sg < 2; ++sg) Z[jt] = mma8(Z[jt], kt[jt][sg], va[sg]);
                 Z[jt] += cv;
-                S[jt] += (f32x4){fn, fn, fn, fn};
+            }
+#pragma unroll
+            for (int m = 0; m < SPW; ++m) {
+#pragma unroll
+                for (int sg = 0; sg < 2; ++sg) S[m] = mma8(S[m], cs_ktr8<D>(Kb, 32 * sg, w + NWAVE * m, r, g), ones8);
+                S[m] += (f32x4){fn, fn, fn, fn};
             }
             // the next chunk's stage (its buffer's readers finished before
             // this chunk's first barrier; chunks past the group stage zeros,
@@ -1800,25 +1825,18 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
             }
-            if (w == 0 && c + 1 < nch) put_sops(S, buf ^ 1);
+            if (c + 1 < nch) put_sops(S, buf ^ 1);
         }
     });
 
-    // ---- publish the group's partial state (all but the last group).  When
-    // every workgroup of the head runs on this XCD (the usual case), the slot
-    // stays in the XCD's L2; otherwise it is written through for every XCD.
+    // ---- publish the group's partial state (all but the last group)
     const unsigned my_xcc = xcc_id();
     if (!last) {
         const rsrc_t sr = make_rsrc((const char *)a.part + (size_t)(hp * a.G + grp) * FS::BYTES, FS::BYTES);
-        auto put = [&](auto cpol) {
-            constexpr int CP = decltype(cpol)::value;
 #pragma unroll
-            for (int jt = 0; jt < JT; ++jt) cstore16<CP>(sr, FS::zoff(w, jt, lane), Z[jt]);
+        for (int jt = 0; jt < JT; ++jt) dstore16(sr, FS::zoff(w, jt, lane), Z[jt]);
 #pragma unroll
-            for (int jt = 0; jt < JT; ++jt) cstore16<CP>(sr, (w == 0 && r == 0) ? FS::soff(jt, g) : OFF_NONE, S[jt]);
-        };
-        if (ids_on_one_xcd(bh * a.G * a.P, a.G * a.P, gridDim.x)) put(IC<CPOL_XCD>{});
-        else put(IC<CPOL_DEVICE>{});
+        for (int m = 0; m < SPW; ++m) dstore16(sr, r == 0 ? FS::soff(w + NWAVE * m, g) : OFF_NONE, S[m]);
     }
     // the flag: this workgroup's memory accesses (slot stores; group 0: its
     // reads of the carried-in state) are complete.  A last group 0 sets it
@@ -1839,34 +1857,35 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
         const bool local = wait_flags(a.flags + (int64_t)hp * a.G, 1, grp, a.epoch, my_xcc, lane);
         constexpr int LB = 4;   // slots in flight
         const char *base = (const char *)a.part + (size_t)hp * a.G * FS::BYTES;
-        // x[jt] += the tiles at offset off(jt) of slots 0 .. grp - 1
-        auto sum_tiles = [&](auto cpol, f32x4 *x, auto off) {
+        // Ze += the wave's Z tiles and Se += its S tiles of slots 0 .. grp - 1
+        auto sum = [&](auto cpol) {
             constexpr int CP = decltype(cpol)::value;
             for (int g0 = 0; g0 < grp; g0 += LB) {
-                f32x4 t[LB][JT];
+                f32x4 tz[LB][JT], ts[LB][SPW];
 #pragma unroll
                 for (int u = 0; u < LB; ++u) {
                     const bool live = g0 + u < grp;
                     const rsrc_t sr = make_rsrc(base + (size_t)(live ? g0 + u : 0) * FS::BYTES, live ? FS::BYTES : 0);
 #pragma unroll
-                    for (int jt = 0; jt < JT; ++jt) t[u][jt] = dload16<CP>(sr, off(jt));
+                    for (int jt = 0; jt < JT; ++jt) tz[u][jt] = dload16<CP>(sr, FS::zoff(w, jt, lane));
+#pragma unroll
+                    for (int m = 0; m < SPW; ++m) ts[u][m] = dload16<CP>(sr, FS::soff(w + NWAVE * m, g));
                 }
 #pragma unroll
-                for (int u = 0; u < LB; ++u)
+                for (int u = 0; u < LB; ++u) {
 #pragma unroll
-                    for (int jt = 0; jt < JT; ++jt) x[jt] += t[u][jt];
+                    for (int jt = 0; jt < JT; ++jt) Ze[jt] += tz[u][jt];
+#pragma unroll
+                    for (int m = 0; m < SPW; ++m) Se[m] += ts[u][m];
+                }
             }
-        };
-        auto sum = [&](auto cpol) {
-            sum_tiles(cpol, Ze, [&](int jt) { return FS::zoff(w, jt, lane); });
-            if (w == 0) sum_tiles(cpol, Se, [&](int jt) { return FS::soff(jt, g); });
         };
         if (local) sum(IC<CPOL_XCD>{});
         else sum(IC<CPOL_DEVICE>{});
         // S operands of the state before the group, into the S buffer the
         // last chunk did not read
         const int eb = nch & 1;
-        if (w == 0) put_sops(Se, eb);
+        put_sops(Se, eb);
         __syncthreads();
 
         // ================= C: add the state before the group to every chunk:
@@ -1917,16 +1936,20 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
     if (last) {
         if (a.wait_s && s_writer) (void)wait_flags(a.flags + (int64_t)bh * a.P * a.G, a.G, a.P, a.epoch, my_xcc, lane);
         float *zo = a.z_out ? a.z_out + (int64_t)bh * D * D + p * DV + 16 * w + r : nullptr;
-        float *so = (a.s_out && s_writer && w == 0 && r == 0) ? a.s_out + (int64_t)bh * D : nullptr;
+        float *so = (a.s_out && s_writer && r == 0) ? a.s_out + (int64_t)bh * D : nullptr;
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int dim = cs_dim(jt, 4 * g + i);
                 const float zf = grp > 0 ? Z[jt][i] + Ze[jt][i] : Z[jt][i];
-                const float sf = grp > 0 ? S[jt][i] + Se[jt][i] : S[jt][i];
-                if (zo) zo[(int64_t)dim * D] = zf;
-                if (so) so[dim] = sf;
+                if (zo) zo[(int64_t)cs_dim(jt, 4 * g + i) * D] = zf;
+            }
+#pragma unroll
+        for (int m = 0; m < SPW; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float sf = grp > 0 ? S[m][i] + Se[m][i] : S[m][i];
+                if (so) so[cs_dim(w + NWAVE * m, 4 * g + i)] = sf;
             }
     }
 }
