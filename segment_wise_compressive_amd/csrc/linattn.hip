@@ -2191,6 +2191,15 @@ __global__ void __launch_bounds__(256) k_decode(const void *qp, const void *kp, 
         const uint16_t u = ((const uint16_t *)base)[i];
         return __uint_as_float((uint32_t)u << 16);
     };
+    // the state rows are requested first (they do not depend on phi), with
+    // non-temporal hints: each element is read and written once per step
+    float *zh = z + (int64_t)(active ? bh : 0) * D * D + 4 * cq;
+    f32x4 zr[RPT];
+    if (active) {
+#pragma unroll
+        for (int m = 0; m < RPT; ++m)
+            zr[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(zh + (int64_t)(m * RG + rg) * D));
+    }
     if (active) {
         for (int j = lt; j < D; j += TPH) {
             sphik[hl][j] = phi<F32>(ld(kp, (int64_t)bh * D + j));
@@ -2204,16 +2213,12 @@ __global__ void __launch_bounds__(256) k_decode(const void *qp, const void *kp, 
         f32x4 vv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) vv[e] = ld(vp, (int64_t)bh * D + 4 * cq + e);
-        float *zh = z + (int64_t)bh * D * D + 4 * cq;
-        f32x4 zr[RPT];
-#pragma unroll
-        for (int m = 0; m < RPT; ++m) zr[m] = *reinterpret_cast<const f32x4 *>(zh + (int64_t)(m * RG + rg) * D);
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
             const int j = m * RG + rg;
             const float fj = sphik[hl][j];
             zr[m] += fj * vv;
-            *reinterpret_cast<f32x4 *>(zh + (int64_t)j * D) = zr[m];
+            __builtin_nontemporal_store(zr[m], reinterpret_cast<f32x4 *>(zh + (int64_t)j * D));
             acc += sphiq[hl][j] * zr[m];
         }
         if (cq == 0) {
