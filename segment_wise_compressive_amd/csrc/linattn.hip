@@ -1414,13 +1414,13 @@ template <int D> struct CSGeo {
     static constexpr int VPR = D / 8;              // 16-byte vectors per q / k row
     static constexpr int NK = C * VPR / NTHR;      // k (and q) vectors per thread per chunk
     static constexpr int NV = C * (DV / 8) / NTHR; // v vectors per thread per chunk
-    // LDS, bf16 elements: two stage buffers of psi(K) [C][D] and of V [C][DV]
-    // (rows swizzled, swz); the score operands [6 pairs][hi, lo][64 lanes][8];
-    // the S operands [2][hi, lo][KS][4 lane groups][8]; psi(Q) of every chunk
-    // of the group [CPG][C][D] (swizzled); then fp32: the normalisers
-    // [CPG][C], the per-wave sums of S [2][4], the row sums of psi(q) and of
-    // psi(k) [2][C] each.
-    static constexpr int OK = 0, OV = 2 * C * D, OP = OV + 2 * C * DV, OSO = OP + 6 * 2 * 64 * 8;
+    // LDS, bf16 elements: the stage of psi(K) [C][D] and of V [C][DV] (rows
+    // swizzled, swz); the score operands [6 pairs][hi, lo][64 lanes][8]; the
+    // S operands [2][hi, lo][KS][4 lane groups][8]; psi(Q) of every chunk of
+    // the group [CPG][C][D] (swizzled); then fp32: the normalisers [CPG][C],
+    // the per-wave sums of S [2][4], the row sums of psi(q) and of psi(k)
+    // [2][C] each.
+    static constexpr int OK = 0, OV = C * D, OP = OV + C * DV, OSO = OP + 6 * 2 * 64 * 8;
     static constexpr int OQ = OSO + 2 * 2 * KS * 4 * 8;
     static constexpr int bf16_elems(int cpg) { return OQ + cpg * C * D; }
     static constexpr int lds_bytes(int cpg) { return bf16_elems(cpg) * 2 + (cpg * C + 8 + 4 * C) * 4; }
@@ -1502,8 +1502,8 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
     float *den_s = reinterpret_cast<float *>(smem_raw + T::bf16_elems(CPG) * 2);   // [CPG][C]
     float *ssum_s = den_s + CPG * C;                                                // [2][4]
     float *qsum_s = ssum_s + 8, *ksum_s = qsum_s + 2 * C;                           // [2][C] each
-    auto kbuf = [&](int buf) { return sm + T::OK + buf * C * D; };
-    auto vbuf = [&](int buf) { return sm + T::OV + buf * C * DV; };
+    auto kbuf = [&]() { return sm + T::OK; };
+    auto vbuf = [&]() { return sm + T::OV; };
     auto qslot = [&](int c) { return sm + T::OQ + c * C * D; };
 
     const int tid = threadIdx.x, lane = tid % WAVE, r = lane % 16, g = lane / 16;
@@ -1550,14 +1550,15 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
         for (int it = 0; it < NK; ++it) Qr[c][it] = bload16(qr, qo[it]);
     };
     auto nval_of = [&](int c) { return min(C, t_end - (t_begin + c * C)); };
-    // the stage of chunk c: psi(K) and V into buffer c % 2, psi(Q) into slot c.
+    // the stage of chunk c: psi(K) and V (one buffer each), psi(Q) into slot
+    // c, the row sums of psi(k) and psi(q) into their buffer c % 2.
     // Rows past the end of the sequence read as zeros (outside the buffer
     // resource), and psi(0) = 0, so they add nothing to the state; the scores
     // mask those keys.
     auto stage = [&](auto cc) {
         constexpr int c = decltype(cc)::value;
         const int buf = c & 1;
-        bf16 *Kb = kbuf(buf), *Qb = qslot(c), *Vb = vbuf(buf);
+        bf16 *Kb = kbuf(), *Qb = qslot(c), *Vb = vbuf();
 #pragma unroll
         for (int it = 0; it < NK; ++it) {
             const int item = tid + it * NTHR, row = item / VPR, vec = item % VPR;
@@ -1686,7 +1687,9 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
     // ================= A: every chunk of the group against the group-local
     // state: numerators in registers, normalisers (one query tile per wave)
     // in LDS; the local state runs through the chunks and ends as the
-    // group's partial state (group 0: including the carried-in state)
+    // group's partial state (group 0: including the carried-in state).
+    // Per chunk: barrier; scores, inter term, state update (every read of
+    // this chunk's psi(K) and V); barrier; P V, normaliser, next stage.
     f32x4 O[CPG][4];
     if (grp == 0) load_state(Z, S, a.z_in ? a.z_in + (int64_t)bh * D * D : nullptr, a.s_in ? a.s_in + (int64_t)bh * D : nullptr);
     else load_state(Z, S, nullptr, nullptr);
@@ -1699,9 +1702,9 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
         constexpr int c = decltype(cc)::value;
         if (c < nch) {
             const int buf = c & 1, nv = nval_of(c);
-            __syncthreads();   // the stage is visible; the previous chunk is done with the other buffer and the scores
+            __syncthreads();   // the stage is visible; the previous chunk's part B is done
             if constexpr (c + 2 < CPG) issue(IC<c + 2>{});
-            const bf16 *Kb = kbuf(buf), *Qb = qslot(c), *Vb = vbuf(buf);
+            const bf16 *Kb = kbuf(), *Qb = qslot(c), *Vb = vbuf();
             // this wave's score tiles: three table entries (sa, m) per wave,
             // 4 bits each; waves 2 and 3 repeat tile (0, 0), which writes the
             // same values as wave 0
@@ -1712,49 +1715,82 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
                                      (0x01u | 0x11u << 8 | 0x23u << 16) * (w == 1) +
                                      (0x02u | 0x12u << 8 | 0x00u << 16) * (w == 2) +
                                      (0x22u | 0x33u << 8 | 0x00u << 16) * (w == 3);
-                bf16x8 ka[3][KS], qa[3][KS];   // every operand read before the products
+                constexpr int TR = KS <= 2 ? 3 : 1;   // tiles whose operands are read together
 #pragma unroll
-                for (int i = 0; i < 3; ++i) {
-                    const int e = (tab >> (8 * i)) & 0xff;
+                for (int i0 = 0; i0 < 3; i0 += TR) {
+                    bf16x8 ka[TR][KS], qa[TR][KS];
 #pragma unroll
-                    for (int u = 0; u < KS; ++u) {
-                        ka[i][u] = nat8(Kb + swz<D>(16 * (e >> 4) + r, 32 * u + 8 * g));
-                        qa[i][u] = nat8(Qb + swz<D>(16 * (e & 15) + r, 32 * u + 8 * g));
+                    for (int i = 0; i < TR; ++i) {
+                        const int e = (tab >> (8 * (i0 + i))) & 0xff;
+#pragma unroll
+                        for (int u = 0; u < KS; ++u) {
+                            ka[i][u] = nat8(Kb + swz<D>(16 * (e >> 4) + r, 32 * u + 8 * g));
+                            qa[i][u] = nat8(Qb + swz<D>(16 * (e & 15) + r, 32 * u + 8 * g));
+                        }
                     }
-                }
-                __builtin_amdgcn_sched_barrier(0);
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int i = 0; i < 3; ++i) {
-                    const int e = (tab >> (8 * i)) & 0xff;
-                    score_tile(ka[i], qa[i], e >> 4, e & 15, nv, buf);
+                    for (int i = 0; i < TR; ++i) {
+                        const int e = (tab >> (8 * (i0 + i))) & 0xff;
+                        score_tile(ka[i], qa[i], e >> 4, e & 15, nv, buf);
+                    }
                 }
             }
             // inter-chunk term of every query tile: column sums of Z plus
             // Z^T psi(q)
-            bf16x8 zh[KS], zl[KS];
-            f32x4 cz;
-            state_ops(Z, zh, zl, cz);
             f32x4 o[4];
             {
-                bf16x8 qb[4][KS];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) q_ops(Qb, m, qb[m]);
-                __builtin_amdgcn_sched_barrier(0);
+                bf16x8 zh[KS], zl[KS];
+                f32x4 cz;
+                state_ops(Z, zh, zl, cz);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
+                    bf16x8 qb[KS];
+                    q_ops(Qb, m, qb);
                     o[m] = cz;
 #pragma unroll
                     for (int u = 0; u < KS; ++u) {
-                        o[m] = mma8(o[m], zh[u], qb[m][u]);
-                        o[m] = mma8(o[m], zl[u], qb[m][u]);
+                        o[m] = mma8(o[m], zh[u], qb[u]);
+                        o[m] = mma8(o[m], zl[u], qb[u]);
                     }
                 }
             }
-            __syncthreads();   // the score operands are visible
-            // intra-chunk term: V^T P^T over key tile pairs (2sg, 2sg + 1)
+            // state update: Z += psi(K)^T V + 1 (column sums of V)^T; the
+            // wave's S tiles += psi(K)^T 1 + nv, and their share of the S
+            // operands of the next chunk.  V stays in registers for P V.
             bf16x8 va[2];
 #pragma unroll
             for (int sg = 0; sg < 2; ++sg) va[sg] = tr8<64>(Vb, 32 * sg, 16 * w, r, g);
+            {
+                f32x4 cv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int sg = 0; sg < 2; ++sg) cv = mma8(cv, ones8, va[sg]);
+                const float fn = (float)nv;
+                constexpr int JR = JT <= 4 ? JT : 2;   // state tiles whose operands are read together
+#pragma unroll
+                for (int j0 = 0; j0 < JT; j0 += JR) {
+                    bf16x8 kt[JR][2];
+#pragma unroll
+                    for (int j = 0; j < JR; ++j)
+#pragma unroll
+                        for (int sg = 0; sg < 2; ++sg) kt[j][sg] = cs_ktr8<D>(Kb, 32 * sg, j0 + j, r, g);
+#pragma unroll
+                    for (int j = 0; j < JR; ++j) {
+#pragma unroll
+                        for (int sg = 0; sg < 2; ++sg) Z[j0 + j] = mma8(Z[j0 + j], kt[j][sg], va[sg]);
+                        Z[j0 + j] += cv;
+                    }
+                }
+#pragma unroll
+                for (int m = 0; m < SPW; ++m) {
+#pragma unroll
+                    for (int sg = 0; sg < 2; ++sg) S[m] = mma8(S[m], cs_ktr8<D>(Kb, 32 * sg, w + NWAVE * m, r, g), ones8);
+                    S[m] += (f32x4){fn, fn, fn, fn};
+                }
+            }
+            if (c + 1 < nch) put_sops(S, buf ^ 1);
+            __syncthreads();   // the score operands are visible; this chunk's psi(K) and V are read
+            // intra-chunk term: V^T P^T over key tile pairs (2sg, 2sg + 1)
             {
                 bf16x8 pp[6][2];   // the 6 score operand pairs, read before the products
 #pragma unroll
@@ -1789,43 +1825,9 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
                 dn += dp;
                 if (g == 0) den_s[c * C + 16 * w + r] = dn[0];
             }
-            // state update: Z += psi(K)^T V + 1 (column sums of V)^T; the
-            // wave's S tiles += psi(K)^T 1 + nv, and their share of the S
-            // operands of the next chunk
-            f32x4 cv = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int sg = 0; sg < 2; ++sg) cv = mma8(cv, ones8, va[sg]);
-            const float fn = (float)nv;
-            bf16x8 kt[JT][2];   // every operand read before the products
-#pragma unroll
-            for (int jt = 0; jt < JT; ++jt)
-#pragma unroll
-                for (int sg = 0; sg < 2; ++sg) kt[jt][sg] = cs_ktr8<D>(Kb, 32 * sg, jt, r, g);
-#pragma unroll
-            for (int jt = 0; jt < JT; ++jt) {
-#pragma unroll
-                for (int sg = 0; sg < 2; ++sg) Z[jt] = mma8(Z[jt], kt[jt][sg], va[sg]);
-                Z[jt] += cv;
-            }
-#pragma unroll
-            for (int m = 0; m < SPW; ++m) {
-#pragma unroll
-                for (int sg = 0; sg < 2; ++sg) S[m] = mma8(S[m], cs_ktr8<D>(Kb, 32 * sg, w + NWAVE * m, r, g), ones8);
-                S[m] += (f32x4){fn, fn, fn, fn};
-            }
-            // the next chunk's stage (its buffer's readers finished before
-            // this chunk's first barrier; chunks past the group stage zeros,
-            // never read).  It comes after this block's operand reads, so its
-            // VALU work can be scheduled between the products: the reads
-            // first, then one product per six VALU.
+            // the next chunk's stage (chunks past the group stage zeros, never
+            // read); its VALU work can be scheduled between the products above
             if constexpr (c + 1 < CPG) stage(IC<c + 1>{});
-            __builtin_amdgcn_sched_group_barrier(0x100, 32, 0);
-#pragma unroll
-            for (int i = 0; i < 44; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-            }
-            if (c + 1 < nch) put_sops(S, buf ^ 1);
         }
     });
 
@@ -1855,7 +1857,7 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
     if (grp > 0) {
         load_state(Ze, Se, nullptr, nullptr);
         const bool local = wait_flags(a.flags + (int64_t)hp * a.G, 1, grp, a.epoch, my_xcc, lane);
-        constexpr int LB = 4;   // slots in flight
+        constexpr int LB = JT <= 4 ? 4 : 2;   // slots in flight (register budget)
         const char *base = (const char *)a.part + (size_t)hp * a.G * FS::BYTES;
         // Ze += the wave's Z tiles and Se += its S tiles of slots 0 .. grp - 1
         auto sum = [&](auto cpol) {
@@ -2321,7 +2323,10 @@ Plan plan_causal(int B, int H, int N, int d, la_dtype dt, int chunk, bool want_o
     pl.P = d / pl.DV;
     const int64_t BH = (int64_t)B * H;
     pl.slot_floats = (size_t)pl.DV * d + d;
-    const int max_g = 1 + (int)(LA_LOOKBACK_BYTES / (pl.slot_floats * 4));
+    int max_g = 1 + (int)(LA_LOOKBACK_BYTES / (pl.slot_floats * 4));
+    // the column-split kernel at d = 128 holds 2 chunks per group: allow the
+    // 16 groups that give it a full grid
+    if (LA_COLUMN_SPLIT && want_out && dt == LA_BF16 && d == 128 && pl.C == 64 && max_g < 16) max_g = 16;
     pl.G = pick_groups(BH * pl.P, N, pl.C, want_out ? LA_CAUSAL_TARGET_WGS : 2 * LA_CAUSAL_TARGET_WGS,
                        max_g < LA_MAX_GROUPS ? max_g : LA_MAX_GROUPS);
     set_groups(pl, N);
@@ -2539,6 +2544,8 @@ la_status la_causal_fwd(const void *q, la_strides sq, const void *k, la_strides 
     const int nwg = (int)(BH * pl.P * pl.G);
     if (LA_COLUMN_SPLIT && want_out && resident && !f32 && d == 64)
         hipLaunchKernelGGL((k_cs_fwd<64, res_cpg(false, 64)>), dim3(nwg), dim3(NTHR), 0, stream, a);
+    else if (LA_COLUMN_SPLIT && want_out && resident && !f32 && d == 128)
+        hipLaunchKernelGGL((k_cs_fwd<128, res_cpg(false, 128)>), dim3(nwg), dim3(NTHR), 0, stream, a);
     else
         dispatch(f32, d, pl.C, want_out ? (resident ? 4 : 1) : 3, a, nwg, stream);
     return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
