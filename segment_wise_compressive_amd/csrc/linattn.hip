@@ -1423,7 +1423,7 @@ template <int D> struct CSGeo {
     static constexpr int OK = 0, OV = C * D, OP = OV + C * DV, OSO = OP + 6 * 2 * 64 * 8;
     static constexpr int OQ = OSO + 2 * 2 * KS * 4 * 8;
     static constexpr int bf16_elems(int cpg) { return OQ + cpg * C * D; }
-    static constexpr int lds_bytes(int cpg) { return bf16_elems(cpg) * 2 + (cpg * C + 8 + 4 * C) * 4; }
+    static constexpr int lds_bytes(int cpg) { return bf16_elems(cpg) * 2 + (2 * cpg * C + 8 + 2 * C) * 4; }
     static_assert(NK * NTHR == C * VPR && NV * NTHR == C * DV / 8, "whole vectors per thread");
 };
 __device__ __forceinline__ int cs_dim(int jt, int m) { return 32 * (jt >> 1) + 8 * (m >> 2) + 4 * (jt & 1) + (m & 3); }
@@ -1501,7 +1501,8 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
     bf16 *sm = reinterpret_cast<bf16 *>(smem_raw);
     float *den_s = reinterpret_cast<float *>(smem_raw + T::bf16_elems(CPG) * 2);   // [CPG][C]
     float *ssum_s = den_s + CPG * C;                                                // [2][4]
-    float *qsum_s = ssum_s + 8, *ksum_s = qsum_s + 2 * C;                           // [2][C] each
+    float *qsum_s = ssum_s + 8;                                                     // [2][C]
+    float *ksum_s = qsum_s + 2 * C;                                                 // [CPG][C]
     auto kbuf = [&]() { return sm + T::OK; };
     auto vbuf = [&]() { return sm + T::OV; };
     auto qslot = [&](int c) { return sm + T::OQ + c * C * D; };
@@ -1538,48 +1539,71 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
         vo[it] = (uint32_t)((item / 8) * vv.rs + (item % 8) * 16);
     }
     u32x4 Kr[CPG][NK], Vr[CPG][NV], Qr[CPG][NK];
-    auto issue = [&](auto cc) {
+    auto issue_kv = [&](auto cc) __attribute__((always_inline)) {
         constexpr int c = decltype(cc)::value;
         const int t0 = t_begin + c * C;
-        const rsrc_t kr = kv.at(t0, c < nch), vr = vv.at(t0, c < nch), qr = qv.at(t0, c < nch);
+        const rsrc_t kr = kv.at(t0, c < nch), vr = vv.at(t0, c < nch);
 #pragma unroll
         for (int it = 0; it < NK; ++it) Kr[c][it] = bload16(kr, ko[it]);
 #pragma unroll
         for (int it = 0; it < NV; ++it) Vr[c][it] = bload16(vr, vo[it]);
+    };
+    auto issue_q = [&](auto cc) __attribute__((always_inline)) {
+        constexpr int c = decltype(cc)::value;
+        const rsrc_t qr = qv.at(t_begin + c * C, c < nch);
 #pragma unroll
         for (int it = 0; it < NK; ++it) Qr[c][it] = bload16(qr, qo[it]);
     };
     auto nval_of = [&](int c) { return min(C, t_end - (t_begin + c * C)); };
-    // the stage of chunk c: psi(K) and V (one buffer each), psi(Q) into slot
-    // c, the row sums of psi(k) and psi(q) into their buffer c % 2.
+    // the stage of chunk c in pass 2: psi(K) (already in registers) and V
+    // (one buffer each), psi(Q) into slot c, the row sums of psi(q) into
+    // buffer c % 2 (those of psi(k) are in place since pass 1).
     // Rows past the end of the sequence read as zeros (outside the buffer
     // resource), and psi(0) = 0, so they add nothing to the state; the scores
     // mask those keys.
-    auto stage = [&](auto cc) {
+    auto stage = [&](auto cc) __attribute__((always_inline)) {
         constexpr int c = decltype(cc)::value;
         const int buf = c & 1;
         bf16 *Kb = kbuf(), *Qb = qslot(c), *Vb = vbuf();
 #pragma unroll
         for (int it = 0; it < NK; ++it) {
             const int item = tid + it * NTHR, row = item / VPR, vec = item % VPR;
-            float ks = 0.f, qs = 0.f;
-            *reinterpret_cast<u32x4 *>(Kb + swz<D>(row, vec * 8)) = cs_psi8(Kr[c][it], ks);
+            float qs = 0.f;
+            *reinterpret_cast<u32x4 *>(Kb + swz<D>(row, vec * 8)) = Kr[c][it];
             *reinterpret_cast<u32x4 *>(Qb + swz<D>(row, vec * 8)) = cs_psi8(Qr[c][it], qs);
-            // row sums over the VPR consecutive lanes of the row
+            // row sum over the VPR consecutive lanes of the row
 #pragma unroll
-            for (int m = 1; m < VPR; m <<= 1) {
-                ks += __shfl_xor(ks, m);
-                qs += __shfl_xor(qs, m);
-            }
-            if (vec == 0) {
-                ksum_s[buf * C + row] = ks;
-                qsum_s[buf * C + row] = qs;
-            }
+            for (int m = 1; m < VPR; m <<= 1) qs += __shfl_xor(qs, m);
+            if (vec == 0) qsum_s[buf * C + row] = qs;
         }
 #pragma unroll
         for (int it = 0; it < NV; ++it) {
             const int item = tid + it * NTHR, row = item / 8, vec = item % 8;
             *reinterpret_cast<u32x4 *>(Vb + swz<64>(row, vec * 8)) = Vr[c][it];
+        }
+    };
+    // the stage of pass 1: k becomes psi(k) in its registers, its row sums
+    // go to ksum_s[c]; psi(K) and V are staged for the state update (the
+    // last group, which has no pass-1 state, stages nothing)
+    auto stage_kv = [&](auto cc) __attribute__((always_inline)) {
+        constexpr int c = decltype(cc)::value;
+        bf16 *Kb = kbuf(), *Vb = vbuf();
+#pragma unroll
+        for (int it = 0; it < NK; ++it) {
+            const int item = tid + it * NTHR, row = item / VPR, vec = item % VPR;
+            float ks = 0.f;
+            Kr[c][it] = cs_psi8(Kr[c][it], ks);
+#pragma unroll
+            for (int m = 1; m < VPR; m <<= 1) ks += __shfl_xor(ks, m);
+            if (vec == 0) ksum_s[c * C + row] = ks;
+            if (!last) *reinterpret_cast<u32x4 *>(Kb + swz<D>(row, vec * 8)) = Kr[c][it];
+        }
+        if (!last) {
+#pragma unroll
+            for (int it = 0; it < NV; ++it) {
+                const int item = tid + it * NTHR, row = item / 8, vec = item % 8;
+                *reinterpret_cast<u32x4 *>(Vb + swz<64>(row, vec * 8)) = Vr[c][it];
+            }
         }
     };
 
@@ -1593,7 +1617,7 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
     constexpr int SPW = JT / NWAVE;
     static_assert(JT % NWAVE == 0, "S tiles split evenly over the waves");
     f32x4 Z[JT], S[SPW], Ze[JT], Se[SPW];
-    auto load_state = [&](f32x4 *z4, f32x4 *s4, const float *z, const float *s) {
+    auto load_state = [&](f32x4 *z4, f32x4 *s4, const float *z, const float *s) __attribute__((always_inline)) {
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
@@ -1605,7 +1629,7 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
     };
     // hi + lo operands of a state, and its sums over the key dims (every row
     // of the result: sum_i z[i][column])
-    auto state_ops = [&](const f32x4 *z4, bf16x8 *zh, bf16x8 *zl, f32x4 &zsum) {
+    auto state_ops = [&](const f32x4 *z4, bf16x8 *zh, bf16x8 *zl, f32x4 &zsum) __attribute__((always_inline)) {
         zsum = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < KS; ++u) {
@@ -1618,7 +1642,7 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
     // of a lane depends only on its lane group g): [2][hi, lo][KS][g][8];
     // every wave writes the halves of its S tiles and the sum of their values
     auto sops_at = [&](int buf, int hl, int u, int gg) { return sm + T::OSO + (((buf * 2 + hl) * KS + u) * 4 + gg) * 8; };
-    auto put_sops = [&](const f32x4 *s4, int buf) {
+    auto put_sops = [&](const f32x4 *s4, int buf) __attribute__((always_inline)) {
         float part = 0.f;
 #pragma unroll
         for (int m = 0; m < SPW; ++m) {
@@ -1637,7 +1661,7 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
         if (lane == 0) ssum_s[buf * 4 + w] = part;
     };
     // the normaliser of query tile m: sum S + S . psi(q) + (intra, by the caller)
-    auto sdot = [&](int buf, const bf16x8 *qb) {
+    auto sdot = [&](int buf, const bf16x8 *qb) __attribute__((always_inline)) {
         f32x4 dn;
         const f32x4 s4 = *reinterpret_cast<const f32x4 *>(ssum_s + buf * 4);
         const float s0 = (s4[0] + s4[1]) + (s4[2] + s4[3]);
@@ -1649,7 +1673,7 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
         }
         return dn;
     };
-    auto q_ops = [&](const bf16 *Qb, int m, bf16x8 *qb) {
+    auto q_ops = [&](const bf16 *Qb, int m, bf16x8 *qb) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < KS; ++u) qb[u] = nat8(Qb + swz<D>(16 * m + r, 32 * u + 8 * g));
     };
@@ -1664,10 +1688,10 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
         const int which = tid / WAVE, ln = tid % WAVE;   // (pair 0 | pair 3) x (hi | lo)
         *reinterpret_cast<uint2 *>(pop_at(which < 2 ? 0 : 3, which & 1, ln) + 4) = make_uint2(0u, 0u);
     }
-    auto score_tile = [&](const bf16x8 *ka, const bf16x8 *qb, int sa, int m, int nv, int buf) {
+    auto score_tile = [&](const bf16x8 *ka, const bf16x8 *qb, int sa, int m, int nv, int buf, int kc) __attribute__((always_inline)) {
         // d + sum psi(q_t) + sum psi(k_s) (row sums from the stage), then
         // + psi(k_s) . psi(q_t)
-        f32x4 pt = *reinterpret_cast<const f32x4 *>(ksum_s + buf * C + 16 * sa + 4 * g) +
+        f32x4 pt = *reinterpret_cast<const f32x4 *>(ksum_s + kc * C + 16 * sa + 4 * g) +
                    ((float)D + qsum_s[buf * C + 16 * m + r]);
 #pragma unroll
         for (int u = 0; u < KS; ++u) pt = mma8(pt, ka[u], qb[u]);
@@ -1684,26 +1708,180 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
         *reinterpret_cast<uint2 *>(pop_at(pair, 1, lane) + 4 * half) = lo;
     };
 
-    // ================= A: every chunk of the group against the group-local
-    // state: numerators in registers, normalisers (one query tile per wave)
-    // in LDS; the local state runs through the chunks and ends as the
-    // group's partial state (group 0: including the carried-in state).
+    // state update from the stage of one chunk: Z += psi(K)^T V + 1 (column
+    // sums of V)^T, the wave's S tiles += psi(K)^T 1 + nv (va: V operands)
+    auto update_state = [&](const bf16 *Kb, const bf16x8 *va, int nv) __attribute__((always_inline)) {
+        f32x4 cv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sg = 0; sg < 2; ++sg) cv = mma8(cv, ones8, va[sg]);
+        const float fn = (float)nv;
+        constexpr int JR = JT <= 4 ? JT : 2;   // state tiles whose operands are read together
+#pragma unroll
+        for (int j0 = 0; j0 < JT; j0 += JR) {
+            bf16x8 kt[JR][2];
+#pragma unroll
+            for (int j = 0; j < JR; ++j)
+#pragma unroll
+                for (int sg = 0; sg < 2; ++sg) kt[j][sg] = cs_ktr8<D>(Kb, 32 * sg, j0 + j, r, g);
+#pragma unroll
+            for (int j = 0; j < JR; ++j) {
+#pragma unroll
+                for (int sg = 0; sg < 2; ++sg) Z[j0 + j] = mma8(Z[j0 + j], kt[j][sg], va[sg]);
+                Z[j0 + j] += cv;
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < SPW; ++m) {
+#pragma unroll
+            for (int sg = 0; sg < 2; ++sg) S[m] = mma8(S[m], cs_ktr8<D>(Kb, 32 * sg, w + NWAVE * m, r, g), ones8);
+            S[m] += (f32x4){fn, fn, fn, fn};
+        }
+    };
+    auto load_start = [&]() __attribute__((always_inline)) {   // the state at the start of the group (group 0: carried in)
+        if (grp == 0) load_state(Z, S, a.z_in ? a.z_in + (int64_t)bh * D * D : nullptr, a.s_in ? a.s_in + (int64_t)bh * D : nullptr);
+        else load_state(Z, S, nullptr, nullptr);
+    };
+
+    // ================= pass 1: k and v of every chunk are requested at once
+    // and stay in registers for pass 2, k turned into psi(k).  Every group
+    // but the last also forms its partial state from them (group 0:
+    // including the carried-in state) and publishes it as early as the loads
+    // allow.  q of the first two chunks is requested meanwhile.
+    const unsigned my_xcc = xcc_id();
+    if (!last) load_start();
+    static_for<CPG>([&](auto cc) { issue_kv(cc); });
+    static_for<CPG>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        if (c < nch) {
+            stage_kv(cc);
+            if constexpr (c == 0) {
+                issue_q(IC<0>{});
+                if constexpr (CPG > 1) issue_q(IC<1>{});
+            }
+            if (!last) {
+                __syncthreads();   // the stage is visible
+                bf16x8 va[2];
+#pragma unroll
+                for (int sg = 0; sg < 2; ++sg) va[sg] = tr8<64>(vbuf(), 32 * sg, 16 * w, r, g);
+                update_state(kbuf(), va, nval_of(c));
+                __syncthreads();   // the stage is read
+            }
+        }
+    });
+    if (!last) {
+        const rsrc_t sr = make_rsrc((const char *)a.part + (size_t)(hp * a.G + grp) * FS::BYTES, FS::BYTES);
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) dstore16(sr, FS::zoff(w, jt, lane), Z[jt]);
+#pragma unroll
+        for (int m = 0; m < SPW; ++m) dstore16(sr, r == 0 ? FS::soff(w + NWAVE * m, g) : OFF_NONE, S[m]);
+    }
+    // the start state of pass 2, read again (group 0) before the flag, so
+    // that a last group writing the final state in place never overtakes it
+    load_start();
+    // the flag: this workgroup's memory accesses (slot stores; group 0: both
+    // reads of the carried-in state) are complete.  A last group 0 sets it
+    // only to signal that s_in has been read.
+    if (!last || (grp == 0 && a.wait_s)) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_store(a.flags + (int64_t)hp * a.G + grp, a.epoch | my_xcc, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // ================= pass 2: every chunk against the running state,
+    // numerators in registers, normalisers (one query tile per wave) in LDS.
+    // The running state starts as the group-local one; after chunk 0 the
+    // state before the group (sum of the earlier groups' published states,
+    // their flags set by now) is added to it, and chunk 0's numerators and
+    // normalisers are corrected, so later chunks see the full prefix.
     // Per chunk: barrier; scores, inter term, state update (every read of
     // this chunk's psi(K) and V); barrier; P V, normaliser, next stage.
     f32x4 O[CPG][4];
-    if (grp == 0) load_state(Z, S, a.z_in ? a.z_in + (int64_t)bh * D * D : nullptr, a.s_in ? a.s_in + (int64_t)bh * D : nullptr);
-    else load_state(Z, S, nullptr, nullptr);
+    // the state before the group: wait for the earlier groups' flags, sum
+    // their published states (each wave its columns' Z tiles and its S
+    // tiles), correct chunk 0 (numerators += column sums of Ze + Ze^T psi(q),
+    // own normaliser += sum Se + Se . psi(q)), then add it to the running
+    // state and to the next chunk's S operands
+    auto look_back = [&]() __attribute__((always_inline)) {
+        __syncthreads();   // every wave is done with chunk 0's S operands (buffer 0)
+        load_state(Ze, Se, nullptr, nullptr);
+        const bool local = wait_flags(a.flags + (int64_t)hp * a.G, 1, grp, a.epoch, my_xcc, lane);
+        constexpr int LB = JT <= 4 ? 4 : 2;   // slots in flight (register budget)
+        const char *base = (const char *)a.part + (size_t)hp * a.G * FS::BYTES;
+        auto sum = [&](auto cpol) __attribute__((always_inline)) {
+            constexpr int CP = decltype(cpol)::value;
+            for (int g0 = 0; g0 < grp; g0 += LB) {
+                f32x4 tz[LB][JT], ts[LB][SPW];
+#pragma unroll
+                for (int u = 0; u < LB; ++u) {
+                    const bool live = g0 + u < grp;
+                    const rsrc_t sr = make_rsrc(base + (size_t)(live ? g0 + u : 0) * FS::BYTES, live ? FS::BYTES : 0);
+#pragma unroll
+                    for (int jt = 0; jt < JT; ++jt) tz[u][jt] = dload16<CP>(sr, FS::zoff(w, jt, lane));
+#pragma unroll
+                    for (int m = 0; m < SPW; ++m) ts[u][m] = dload16<CP>(sr, FS::soff(w + NWAVE * m, g));
+                }
+#pragma unroll
+                for (int u = 0; u < LB; ++u) {
+#pragma unroll
+                    for (int jt = 0; jt < JT; ++jt) Ze[jt] += tz[u][jt];
+#pragma unroll
+                    for (int m = 0; m < SPW; ++m) Se[m] += ts[u][m];
+                }
+            }
+        };
+        if (local) sum(IC<CPOL_XCD>{});
+        else sum(IC<CPOL_DEVICE>{});
+        put_sops(Se, 0);
+        __syncthreads();
+        bf16x8 zh[KS], zl[KS];
+        f32x4 cz;
+        state_ops(Ze, zh, zl, cz);
+        const bf16 *Qb = qslot(0);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            bf16x8 qb[KS];
+            q_ops(Qb, m, qb);
+            f32x4 o = O[0][m] + cz;
+#pragma unroll
+            for (int u = 0; u < KS; ++u) {
+                o = mma8(o, zh[u], qb[u]);
+                o = mma8(o, zl[u], qb[u]);
+            }
+            O[0][m] = o;
+            if (m == w) {
+                const f32x4 dn = sdot(0, qb);
+                if (g == 0) den_s[16 * m + r] += dn[0];
+            }
+        }
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) Z[jt] += Ze[jt];
+#pragma unroll
+        for (int m = 0; m < SPW; ++m) S[m] += Se[m];
+        if (nch > 1) put_sops(S, 1);
+    };
+    // the outputs of chunk c: numerators / normalisers (every normaliser of
+    // the chunk is complete after the next barrier)
+    auto store_out = [&](auto cc) __attribute__((always_inline)) {
+        constexpr int c = decltype(cc)::value;
+        const int t0 = t_begin + c * C, nv = nval_of(c);
+        const rsrc_t orr = ov.at(t0);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int t = 16 * m + r;
+            const float inv = __builtin_amdgcn_rcpf(den_s[c * C + t] + a.eps);
+            bstore16(orr, t < nv ? (uint32_t)(t * ov.rs + (16 * w + 4 * g) * 4) : OFF_NONE, O[c][m] * inv);
+        }
+    };
     put_sops(S, 0);
-    // chunk 0 first for every workgroup (it gates the start), then chunk 1
-    issue(IC<0>{});
     stage(IC<0>{});
-    if constexpr (CPG > 1) issue(IC<1>{});
     static_for<CPG>([&](auto cc) {
         constexpr int c = decltype(cc)::value;
         if (c < nch) {
             const int buf = c & 1, nv = nval_of(c);
             __syncthreads();   // the stage is visible; the previous chunk's part B is done
-            if constexpr (c + 2 < CPG) issue(IC<c + 2>{});
+            if constexpr (c + 2 < CPG) issue_q(IC<c + 2>{});
             const bf16 *Kb = kbuf(), *Qb = qslot(c), *Vb = vbuf();
             // this wave's score tiles: three table entries (sa, m) per wave,
             // 4 bits each; waves 2 and 3 repeat tile (0, 0), which writes the
@@ -1732,10 +1910,11 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
 #pragma unroll
                     for (int i = 0; i < TR; ++i) {
                         const int e = (tab >> (8 * (i0 + i))) & 0xff;
-                        score_tile(ka[i], qa[i], e >> 4, e & 15, nv, buf);
+                        score_tile(ka[i], qa[i], e >> 4, e & 15, nv, buf, c);
                     }
                 }
             }
+            if constexpr (c > 0) store_out(IC<c - 1>{});   // the previous chunk is complete
             // inter-chunk term of every query tile: column sums of Z plus
             // Z^T psi(q)
             f32x4 o[4];
@@ -1755,39 +1934,12 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
                     }
                 }
             }
-            // state update: Z += psi(K)^T V + 1 (column sums of V)^T; the
-            // wave's S tiles += psi(K)^T 1 + nv, and their share of the S
-            // operands of the next chunk.  V stays in registers for P V.
+            // state update (V stays in registers for P V), and this wave's
+            // share of the S operands of the next chunk
             bf16x8 va[2];
 #pragma unroll
             for (int sg = 0; sg < 2; ++sg) va[sg] = tr8<64>(Vb, 32 * sg, 16 * w, r, g);
-            {
-                f32x4 cv = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int sg = 0; sg < 2; ++sg) cv = mma8(cv, ones8, va[sg]);
-                const float fn = (float)nv;
-                constexpr int JR = JT <= 4 ? JT : 2;   // state tiles whose operands are read together
-#pragma unroll
-                for (int j0 = 0; j0 < JT; j0 += JR) {
-                    bf16x8 kt[JR][2];
-#pragma unroll
-                    for (int j = 0; j < JR; ++j)
-#pragma unroll
-                        for (int sg = 0; sg < 2; ++sg) kt[j][sg] = cs_ktr8<D>(Kb, 32 * sg, j0 + j, r, g);
-#pragma unroll
-                    for (int j = 0; j < JR; ++j) {
-#pragma unroll
-                        for (int sg = 0; sg < 2; ++sg) Z[j0 + j] = mma8(Z[j0 + j], kt[j][sg], va[sg]);
-                        Z[j0 + j] += cv;
-                    }
-                }
-#pragma unroll
-                for (int m = 0; m < SPW; ++m) {
-#pragma unroll
-                    for (int sg = 0; sg < 2; ++sg) S[m] = mma8(S[m], cs_ktr8<D>(Kb, 32 * sg, w + NWAVE * m, r, g), ones8);
-                    S[m] += (f32x4){fn, fn, fn, fn};
-                }
-            }
+            update_state(Kb, va, nv);
             if (c + 1 < nch) put_sops(S, buf ^ 1);
             __syncthreads();   // the score operands are visible; this chunk's psi(K) and V are read
             // intra-chunk term: V^T P^T over key tile pairs (2sg, 2sg + 1)
@@ -1828,113 +1980,16 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
             // the next chunk's stage (chunks past the group stage zeros, never
             // read); its VALU work can be scheduled between the products above
             if constexpr (c + 1 < CPG) stage(IC<c + 1>{});
+            if constexpr (c == 0) {
+                if (grp > 0) look_back();
+            }
         }
     });
-
-    // ---- publish the group's partial state (all but the last group)
-    const unsigned my_xcc = xcc_id();
-    if (!last) {
-        const rsrc_t sr = make_rsrc((const char *)a.part + (size_t)(hp * a.G + grp) * FS::BYTES, FS::BYTES);
-#pragma unroll
-        for (int jt = 0; jt < JT; ++jt) dstore16(sr, FS::zoff(w, jt, lane), Z[jt]);
-#pragma unroll
-        for (int m = 0; m < SPW; ++m) dstore16(sr, r == 0 ? FS::soff(w + NWAVE * m, g) : OFF_NONE, S[m]);
-    }
-    // the flag: this workgroup's memory accesses (slot stores; group 0: its
-    // reads of the carried-in state) are complete.  A last group 0 sets it
-    // only to signal that s_in has been read.
-    if (!last || (grp == 0 && a.wait_s)) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (tid == 0)
-            __hip_atomic_store(a.flags + (int64_t)hp * a.G + grp, a.epoch | my_xcc, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    }
-
-    // ================= B: the state before the group (groups after the
-    // first): the sum of the published partial states of all earlier groups
-    // (S by wave 0 only)
-    if (grp > 0) {
-        load_state(Ze, Se, nullptr, nullptr);
-        const bool local = wait_flags(a.flags + (int64_t)hp * a.G, 1, grp, a.epoch, my_xcc, lane);
-        constexpr int LB = JT <= 4 ? 4 : 2;   // slots in flight (register budget)
-        const char *base = (const char *)a.part + (size_t)hp * a.G * FS::BYTES;
-        // Ze += the wave's Z tiles and Se += its S tiles of slots 0 .. grp - 1
-        auto sum = [&](auto cpol) {
-            constexpr int CP = decltype(cpol)::value;
-            for (int g0 = 0; g0 < grp; g0 += LB) {
-                f32x4 tz[LB][JT], ts[LB][SPW];
-#pragma unroll
-                for (int u = 0; u < LB; ++u) {
-                    const bool live = g0 + u < grp;
-                    const rsrc_t sr = make_rsrc(base + (size_t)(live ? g0 + u : 0) * FS::BYTES, live ? FS::BYTES : 0);
-#pragma unroll
-                    for (int jt = 0; jt < JT; ++jt) tz[u][jt] = dload16<CP>(sr, FS::zoff(w, jt, lane));
-#pragma unroll
-                    for (int m = 0; m < SPW; ++m) ts[u][m] = dload16<CP>(sr, FS::soff(w + NWAVE * m, g));
-                }
-#pragma unroll
-                for (int u = 0; u < LB; ++u) {
-#pragma unroll
-                    for (int jt = 0; jt < JT; ++jt) Ze[jt] += tz[u][jt];
-#pragma unroll
-                    for (int m = 0; m < SPW; ++m) Se[m] += ts[u][m];
-                }
-            }
-        };
-        if (local) sum(IC<CPOL_XCD>{});
-        else sum(IC<CPOL_DEVICE>{});
-        // S operands of the state before the group, into the S buffer the
-        // last chunk did not read
-        const int eb = nch & 1;
-        put_sops(Se, eb);
-        __syncthreads();
-
-        // ================= C: add the state before the group to every chunk:
-        // numerators += column sums of Ze + Ze^T psi(q); normalisers (own
-        // query tile) += sum_i Se_i + Se . psi(q)
-        bf16x8 zh[KS], zl[KS];
-        f32x4 cz;
-        state_ops(Ze, zh, zl, cz);
-        static_for<CPG>([&](auto cc) {
-            constexpr int c = decltype(cc)::value;
-            if (c < nch) {
-                const bf16 *Qb = qslot(c);
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    bf16x8 qb[KS];
-                    q_ops(Qb, m, qb);
-                    f32x4 o = O[c][m] + cz;
-#pragma unroll
-                    for (int u = 0; u < KS; ++u) {
-                        o = mma8(o, zh[u], qb[u]);
-                        o = mma8(o, zl[u], qb[u]);
-                    }
-                    O[c][m] = o;
-                    if (m == w) {
-                        const f32x4 dn = sdot(eb, qb);
-                        if (g == 0) den_s[c * C + 16 * m + r] += dn[0];
-                    }
-                }
-            }
-        });
-    }
-    __syncthreads();   // every normaliser is complete
-    // ---- the outputs
+    __syncthreads();   // the last chunk's normalisers are complete
     static_for<CPG>([&](auto cc) {
-        constexpr int c = decltype(cc)::value;
-        if (c < nch) {
-            const int t0 = t_begin + c * C, nv = nval_of(c);
-            const rsrc_t orr = ov.at(t0);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int t = 16 * m + r;
-                const float inv = __builtin_amdgcn_rcpf(den_s[c * C + t] + a.eps);
-                bstore16(orr, t < nv ? (uint32_t)(t * ov.rs + (16 * w + 4 * g) * 4) : OFF_NONE, O[c][m] * inv);
-            }
-        }
+        if (cc.value == nch - 1) store_out(cc);
     });
-    // ---- the final state (last group): local state + state before the group
+    // ---- the final state (last group): the running state after the last chunk
     if (last) {
         if (a.wait_s && s_writer) (void)wait_flags(a.flags + (int64_t)bh * a.P * a.G, a.G, a.P, a.epoch, my_xcc, lane);
         float *zo = a.z_out ? a.z_out + (int64_t)bh * D * D + p * DV + 16 * w + r : nullptr;
@@ -1943,15 +1998,13 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
         for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float zf = grp > 0 ? Z[jt][i] + Ze[jt][i] : Z[jt][i];
-                if (zo) zo[(int64_t)cs_dim(jt, 4 * g + i) * D] = zf;
+                if (zo) zo[(int64_t)cs_dim(jt, 4 * g + i) * D] = Z[jt][i];
             }
 #pragma unroll
         for (int m = 0; m < SPW; ++m)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float sf = grp > 0 ? S[m][i] + Se[m][i] : S[m][i];
-                if (so) so[cs_dim(w + NWAVE * m, 4 * g + i)] = sf;
+                if (so) so[cs_dim(w + NWAVE * m, 4 * g + i)] = S[m][i];
             }
     }
 }
