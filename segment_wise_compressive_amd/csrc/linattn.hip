@@ -1748,6 +1748,12 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
     // including the carried-in state) and publishes it as early as the loads
     // allow.  q of the first two chunks is requested meanwhile.
     const unsigned my_xcc = xcc_id();
+    // Wave priorities follow progress: the two workgroups that share a CU
+    // would otherwise run oldest-first, and the younger one would finish its
+    // last chunks alone on the CU.  Pass 1 runs at the top priority, chunk c
+    // of pass 2 at CPG - 1 - c, so a workgroup that is ahead yields.
+    static_assert(CPG >= 1 && CPG <= 4, "priorities 0..3 cover the chunks");
+    __builtin_amdgcn_s_setprio(3);
     if (!last) load_start();
     static_for<CPG>([&](auto cc) { issue_kv(cc); });
     static_for<CPG>([&](auto cc) {
@@ -1881,6 +1887,7 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
         if (c < nch) {
             const int buf = c & 1, nv = nval_of(c);
             __syncthreads();   // the stage is visible; the previous chunk's part B is done
+            __builtin_amdgcn_s_setprio(CPG - 1 - c);   // progress-based priority (see pass 1)
             if constexpr (c + 2 < CPG) issue_q(IC<c + 2>{});
             const bf16 *Kb = kbuf(), *Qb = qslot(c), *Vb = vbuf();
             // this wave's score tiles: three table entries (sa, m) per wave,
