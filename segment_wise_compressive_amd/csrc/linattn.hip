@@ -277,17 +277,24 @@ __device__ __forceinline__ bf16x8 nat8(const bf16 *p) { return *reinterpret_cast
 __device__ __forceinline__ f32x4 nat4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 
 // bf16 [row][W] arrays of phi(K) and V: the 16-byte piece p of a row is stored
-// at piece p ^ f(row).  Both ways these arrays are read then spread over all
-// 32 LDS banks: 16-byte reads of one piece from 8 consecutive rows (the
-// scores), and the transpose reads below, which take 32 bytes (two pieces)
-// from each of 4 consecutive rows per 16 lanes.  128-byte and longer rows:
-// f = 2 (row & 3) + ((row >> 2) & 1); 64-byte rows (two per 128 bytes):
-// f = 2 ((row >> 1) & 1) + ((row >> 2) & 1).
+// at piece p ^ f(row).  gfx950 LDS has 64 banks (256 bytes per clock): a
+// 16-byte read is served 16 lanes at a time, an 8-byte read 32 lanes at a
+// time.  f spreads both ways these arrays are read over all 64 banks:
+// 16-byte reads of one piece from 16 consecutive rows (scores, inter term),
+// and transpose reads of two pieces from each of 8 consecutive rows.
+//   256-byte rows: f = 2 (row & 7) + ((row >> 3) & 1)
+//   128-byte rows: f = 2 ((row >> 1) & 3) + ((row >> 3) & 1)   (rows of one
+//                  parity share a 256-byte bank cycle)
+//    64-byte rows: f = 2 ((row >> 2) & 1) + ((row >> 3) & 1)   (4 rows per
+//                  bank cycle)
+// The transpose read of four pieces per row (state update) stays 2-way.
 template <int W>
 __device__ __forceinline__ int swz_piece(int row, int piece)
 {
-    if constexpr (W == 32) return piece ^ (2 * ((row >> 1) & 1) + ((row >> 2) & 1));
-    else return piece ^ (2 * (row & 3) + ((row >> 2) & 1));
+    if constexpr (W == 32) return piece ^ (2 * ((row >> 2) & 1) + ((row >> 3) & 1));
+    else if constexpr (W == 64) return piece ^ (2 * ((row >> 1) & 3) + ((row >> 3) & 1));
+    else if constexpr (W == 128) return piece ^ (2 * (row & 7) + ((row >> 3) & 1));
+    else return piece;   // padded fp32 rows: not swizzled
 }
 // element offset of (row, col) in a swizzled bf16 [row][W] array (col % 4 == 0)
 template <int W>
@@ -1742,67 +1749,9 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
         else load_state(Z, S, nullptr, nullptr);
     };
 
-    // ================= pass 1: k and v of every chunk are requested at once
-    // and stay in registers for pass 2, k turned into psi(k).  Every group
-    // but the last also forms its partial state from them (group 0:
-    // including the carried-in state) and publishes it as early as the loads
-    // allow.  q of the first two chunks is requested meanwhile.
     const unsigned my_xcc = xcc_id();
-    // Wave priorities follow progress: the two workgroups that share a CU
-    // would otherwise run oldest-first, and the younger one would finish its
-    // last chunks alone on the CU.  Pass 1 runs at the top priority, chunk c
-    // of pass 2 at CPG - 1 - c, so a workgroup that is ahead yields.
-    static_assert(CPG >= 1 && CPG <= 4, "priorities 0..3 cover the chunks");
-    __builtin_amdgcn_s_setprio(3);
-    if (!last) load_start();
-    static_for<CPG>([&](auto cc) { issue_kv(cc); });
-    static_for<CPG>([&](auto cc) {
-        constexpr int c = decltype(cc)::value;
-        if (c < nch) {
-            stage_kv(cc);
-            if constexpr (c == 0) {
-                issue_q(IC<0>{});
-                if constexpr (CPG > 1) issue_q(IC<1>{});
-            }
-            if (!last) {
-                __syncthreads();   // the stage is visible
-                bf16x8 va[2];
-#pragma unroll
-                for (int sg = 0; sg < 2; ++sg) va[sg] = tr8<64>(vbuf(), 32 * sg, 16 * w, r, g);
-                update_state(kbuf(), va, nval_of(c));
-                __syncthreads();   // the stage is read
-            }
-        }
-    });
-    if (!last) {
-        const rsrc_t sr = make_rsrc((const char *)a.part + (size_t)(hp * a.G + grp) * FS::BYTES, FS::BYTES);
-#pragma unroll
-        for (int jt = 0; jt < JT; ++jt) dstore16(sr, FS::zoff(w, jt, lane), Z[jt]);
-#pragma unroll
-        for (int m = 0; m < SPW; ++m) dstore16(sr, r == 0 ? FS::soff(w + NWAVE * m, g) : OFF_NONE, S[m]);
-    }
-    // the start state of pass 2, read again (group 0) before the flag, so
-    // that a last group writing the final state in place never overtakes it
-    load_start();
-    // the flag: this workgroup's memory accesses (slot stores; group 0: both
-    // reads of the carried-in state) are complete.  A last group 0 sets it
-    // only to signal that s_in has been read.
-    if (!last || (grp == 0 && a.wait_s)) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (tid == 0)
-            __hip_atomic_store(a.flags + (int64_t)hp * a.G + grp, a.epoch | my_xcc, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    }
-
-    // ================= pass 2: every chunk against the running state,
-    // numerators in registers, normalisers (one query tile per wave) in LDS.
-    // The running state starts as the group-local one; after chunk 0 the
-    // state before the group (sum of the earlier groups' published states,
-    // their flags set by now) is added to it, and chunk 0's numerators and
-    // normalisers are corrected, so later chunks see the full prefix.
-    // Per chunk: barrier; scores, inter term, state update (every read of
-    // this chunk's psi(K) and V); barrier; P V, normaliser, next stage.
+    constexpr bool EARLY0 = JT <= 4;   // chunk 0 of pass 2 before the rest of pass 1
+    // numerators of every chunk of the group (registers), normalisers in LDS
     f32x4 O[CPG][4];
     // the state before the group: wait for the earlier groups' flags, sum
     // their published states (each wave its columns' Z tiles and its S
@@ -1880,115 +1829,230 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
             bstore16(orr, t < nv ? (uint32_t)(t * ov.rs + (16 * w + 4 * g) * 4) : OFF_NONE, O[c][m] * inv);
         }
     };
-    put_sops(S, 0);
-    stage(IC<0>{});
-    static_for<CPG>([&](auto cc) {
+    // one chunk of pass 2, everything but the next chunk's stage.  Per
+    // chunk: barrier; scores, inter term, state update (every read of this
+    // chunk's psi(K) and V); barrier; P V, normaliser.
+    auto chunk = [&](auto cc) __attribute__((always_inline)) {
         constexpr int c = decltype(cc)::value;
-        if (c < nch) {
-            const int buf = c & 1, nv = nval_of(c);
-            __syncthreads();   // the stage is visible; the previous chunk's part B is done
-            __builtin_amdgcn_s_setprio(CPG - 1 - c);   // progress-based priority (see pass 1)
-            if constexpr (c + 2 < CPG) issue_q(IC<c + 2>{});
-            const bf16 *Kb = kbuf(), *Qb = qslot(c), *Vb = vbuf();
-            // this wave's score tiles: three table entries (sa, m) per wave,
-            // 4 bits each; waves 2 and 3 repeat tile (0, 0), which writes the
-            // same values as wave 0
-            //   w0: (0,0) (0,3) (1,3)   w1: (0,1) (1,1) (2,3)
-            //   w2: (0,2) (1,2) (0,0)   w3: (2,2) (3,3) (0,0)
-            {
-                const uint32_t tab = (0x000000u | 0x03u << 8 | 0x13u << 16) * (w == 0) +
-                                     (0x01u | 0x11u << 8 | 0x23u << 16) * (w == 1) +
-                                     (0x02u | 0x12u << 8 | 0x00u << 16) * (w == 2) +
-                                     (0x22u | 0x33u << 8 | 0x00u << 16) * (w == 3);
-                constexpr int TR = KS <= 2 ? 3 : 1;   // tiles whose operands are read together
+        const int buf = c & 1, nv = nval_of(c);
+        __syncthreads();   // the stage is visible; the previous chunk's part B is done
+        __builtin_amdgcn_s_setprio(CPG - 1 - c);   // progress-based priority (see pass 1)
+        if constexpr (!EARLY0 && c + 2 < CPG) issue_q(IC<c + 2>{});
+        const bf16 *Kb = kbuf(), *Qb = qslot(c), *Vb = vbuf();
+        // this wave's score tiles: three table entries (sa, m) per wave,
+        // 4 bits each; waves 2 and 3 repeat tile (0, 0), which writes the
+        // same values as wave 0
+        //   w0: (0,0) (0,3) (1,3)   w1: (0,1) (1,1) (2,3)
+        //   w2: (0,2) (1,2) (0,0)   w3: (2,2) (3,3) (0,0)
+        {
+            const uint32_t tab = (0x000000u | 0x03u << 8 | 0x13u << 16) * (w == 0) +
+                                 (0x01u | 0x11u << 8 | 0x23u << 16) * (w == 1) +
+                                 (0x02u | 0x12u << 8 | 0x00u << 16) * (w == 2) +
+                                 (0x22u | 0x33u << 8 | 0x00u << 16) * (w == 3);
+            constexpr int TR = KS <= 2 ? 3 : 1;   // tiles whose operands are read together
 #pragma unroll
-                for (int i0 = 0; i0 < 3; i0 += TR) {
-                    bf16x8 ka[TR][KS], qa[TR][KS];
+            for (int i0 = 0; i0 < 3; i0 += TR) {
+                bf16x8 ka[TR][KS], qa[TR][KS];
 #pragma unroll
-                    for (int i = 0; i < TR; ++i) {
-                        const int e = (tab >> (8 * (i0 + i))) & 0xff;
-#pragma unroll
-                        for (int u = 0; u < KS; ++u) {
-                            ka[i][u] = nat8(Kb + swz<D>(16 * (e >> 4) + r, 32 * u + 8 * g));
-                            qa[i][u] = nat8(Qb + swz<D>(16 * (e & 15) + r, 32 * u + 8 * g));
-                        }
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int i = 0; i < TR; ++i) {
-                        const int e = (tab >> (8 * (i0 + i))) & 0xff;
-                        score_tile(ka[i], qa[i], e >> 4, e & 15, nv, buf, c);
-                    }
-                }
-            }
-            if constexpr (c > 0) store_out(IC<c - 1>{});   // the previous chunk is complete
-            // inter-chunk term of every query tile: column sums of Z plus
-            // Z^T psi(q)
-            f32x4 o[4];
-            {
-                bf16x8 zh[KS], zl[KS];
-                f32x4 cz;
-                state_ops(Z, zh, zl, cz);
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    bf16x8 qb[KS];
-                    q_ops(Qb, m, qb);
-                    o[m] = cz;
+                for (int i = 0; i < TR; ++i) {
+                    const int e = (tab >> (8 * (i0 + i))) & 0xff;
 #pragma unroll
                     for (int u = 0; u < KS; ++u) {
-                        o[m] = mma8(o[m], zh[u], qb[u]);
-                        o[m] = mma8(o[m], zl[u], qb[u]);
+                        ka[i][u] = nat8(Kb + swz<D>(16 * (e >> 4) + r, 32 * u + 8 * g));
+                        qa[i][u] = nat8(Qb + swz<D>(16 * (e & 15) + r, 32 * u + 8 * g));
                     }
                 }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < TR; ++i) {
+                    const int e = (tab >> (8 * (i0 + i))) & 0xff;
+                    score_tile(ka[i], qa[i], e >> 4, e & 15, nv, buf, c);
+                }
             }
-            // state update (V stays in registers for P V), and this wave's
-            // share of the S operands of the next chunk
+        }
+        if constexpr (c > 0) store_out(IC<c - 1>{});   // the previous chunk is complete
+        // inter-chunk term of every query tile: column sums of Z plus
+        // Z^T psi(q)
+        f32x4 o[4];
+        {
+            bf16x8 zh[KS], zl[KS];
+            f32x4 cz;
+            state_ops(Z, zh, zl, cz);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                bf16x8 qb[KS];
+                q_ops(Qb, m, qb);
+                o[m] = cz;
+#pragma unroll
+                for (int u = 0; u < KS; ++u) {
+                    o[m] = mma8(o[m], zh[u], qb[u]);
+                    o[m] = mma8(o[m], zl[u], qb[u]);
+                }
+            }
+        }
+        // state update (V stays in registers for P V), and this wave's
+        // share of the S operands of the next chunk
+        bf16x8 va[2];
+#pragma unroll
+        for (int sg = 0; sg < 2; ++sg) va[sg] = tr8<64>(Vb, 32 * sg, 16 * w, r, g);
+        update_state(Kb, va, nv);
+        if (c + 1 < nch) put_sops(S, buf ^ 1);
+        __syncthreads();   // the score operands are visible; this chunk's psi(K) and V are read
+        // intra-chunk term: V^T P^T over key tile pairs (2sg, 2sg + 1)
+        {
+            bf16x8 pp[6][2];   // the 6 score operand pairs, read before the products
+#pragma unroll
+            for (int pr = 0; pr < 6; ++pr) { pp[pr][0] = nat8(pop_at(pr, 0, lane)); pp[pr][1] = nat8(pop_at(pr, 1, lane)); }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+#pragma unroll
+                for (int sg = 0; 2 * sg <= m; ++sg) {
+                    o[m] = mma8(o[m], va[sg], pp[pbase(m) + sg][0]);
+                    o[m] = mma8(o[m], va[sg], pp[pbase(m) + sg][1]);
+                }
+                O[c][m] = o[m];
+            }
+        }
+        // normaliser of this wave's query tile w: sum_i S_i + S . psi(q) +
+        // sum_s P (the second key pair only for w >= 2: a zero operand
+        // otherwise)
+        {
+            bf16x8 qw[KS];
+            q_ops(Qb, w, qw);
+            f32x4 dn = sdot(buf, qw), dp = {0.f, 0.f, 0.f, 0.f};   // two independent chains
+            const int pw = pbase(w);
+            const bf16x8 z8 = {};
+            const bool two = w >= 2;
+#pragma unroll
+            for (int sg = 0; sg < 2; ++sg) {
+                bf16x8 ph = nat8(pop_at(pw + (sg & (int)two), 0, lane)), pl = nat8(pop_at(pw + (sg & (int)two), 1, lane));
+                if (sg == 1) { ph = two ? ph : z8; pl = two ? pl : z8; }
+                dp = mma8(dp, ones8, ph);
+                dp = mma8(dp, ones8, pl);
+            }
+            dn += dp;
+            if (g == 0) den_s[c * C + 16 * w + r] = dn[0];
+        }
+    };
+    // pass 1 for chunk c: k turned into psi(k) in its registers; every
+    // group but the last adds psi(K)^T V to its running state
+    auto pass1_chunk = [&](auto cc) __attribute__((always_inline)) {
+        constexpr int c = decltype(cc)::value;
+        stage_kv(cc);
+        if constexpr (EARLY0) {   // loads run two chunks ahead of their use
+            if constexpr (c + 2 < CPG) issue_kv(IC<c + 2>{});
+            issue_q(cc);
+        } else if constexpr (c == 0) {   // q of the first two chunks is requested meanwhile
+            issue_q(IC<0>{});
+            if constexpr (CPG > 1) issue_q(IC<1>{});
+        }
+        if (!last) {
+            __syncthreads();   // the stage is visible
             bf16x8 va[2];
 #pragma unroll
-            for (int sg = 0; sg < 2; ++sg) va[sg] = tr8<64>(Vb, 32 * sg, 16 * w, r, g);
-            update_state(Kb, va, nv);
-            if (c + 1 < nch) put_sops(S, buf ^ 1);
-            __syncthreads();   // the score operands are visible; this chunk's psi(K) and V are read
-            // intra-chunk term: V^T P^T over key tile pairs (2sg, 2sg + 1)
-            {
-                bf16x8 pp[6][2];   // the 6 score operand pairs, read before the products
+            for (int sg = 0; sg < 2; ++sg) va[sg] = tr8<64>(vbuf(), 32 * sg, 16 * w, r, g);
+            update_state(kbuf(), va, nval_of(c));
+            __syncthreads();   // the stage is read
+        }
+    };
+    // the group's partial state to its slot, then the flag: this
+    // workgroup's memory accesses (slot stores; group 0: its reads of the
+    // carried-in state) are complete.  A last group 0 sets it only to signal
+    // that s_in has been read.
+    auto publish = [&]() __attribute__((always_inline)) {
+        if (!last) {
+            const rsrc_t sr = make_rsrc((const char *)a.part + (size_t)(hp * a.G + grp) * FS::BYTES, FS::BYTES);
 #pragma unroll
-                for (int pr = 0; pr < 6; ++pr) { pp[pr][0] = nat8(pop_at(pr, 0, lane)); pp[pr][1] = nat8(pop_at(pr, 1, lane)); }
+            for (int jt = 0; jt < JT; ++jt) dstore16(sr, FS::zoff(w, jt, lane), Z[jt]);
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
+            for (int m = 0; m < SPW; ++m) dstore16(sr, r == 0 ? FS::soff(w + NWAVE * m, g) : OFF_NONE, S[m]);
+        }
+    };
+    auto set_flag = [&]() __attribute__((always_inline)) {
+        if (!last || (grp == 0 && a.wait_s)) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (tid == 0)
+                __hip_atomic_store(a.flags + (int64_t)hp * a.G + grp, a.epoch | my_xcc, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
+
+    // ================= the schedule.  Pass 1 (state only) publishes the
+    // group's partial state as early as the loads allow; pass 2 computes the
+    // outputs, chunk by chunk against the running state.  At d <= 64 chunk 0
+    // of pass 2 runs first, as soon as its inputs arrive (its state is the
+    // start state), and the state after it is kept while pass 1 advances
+    // over the remaining chunks; at larger d (register budget) pass 1 covers
+    // every chunk first and the start state is loaded again.  Then the state
+    // before the group is looked up (groups after the first) and chunk 0
+    // corrected, so chunks 1.. see the full prefix.
+    // Wave priorities follow progress: the two workgroups that share a CU
+    // would otherwise run oldest-first, and the younger one would finish its
+    // last chunks alone on the CU.  Pass 1 and chunk 0 run at the top
+    // priority, chunk c of pass 2 at CPG - 1 - c, so a workgroup that is
+    // ahead yields.
+    static_assert(CPG >= 1 && CPG <= 4, "priorities 0..3 cover the chunks");
+    __builtin_amdgcn_s_setprio(3);
+    if constexpr (EARLY0) {
+        // the loads are requested in the order of use, at most two chunks
+        // ahead, so that the first chunks of every workgroup arrive first
+        load_start();
+        issue_kv(IC<0>{});
+        issue_q(IC<0>{});
+        if constexpr (CPG > 1) issue_kv(IC<1>{});
+        put_sops(S, 0);
+        stage_kv(IC<0>{});   // psi(k) of chunk 0 (its state update is part of chunk 0 below)
+        stage(IC<0>{});
+        if constexpr (CPG > 2) issue_kv(IC<2>{});
+        if (nch > 0) chunk(IC<0>{});   // always; keeps chunk 0 a region of its own for the scheduler
+        __builtin_amdgcn_s_setprio(3);
+        f32x4 Zs[JT], Ss[SPW];   // the state after chunk 0
 #pragma unroll
-                    for (int sg = 0; 2 * sg <= m; ++sg) {
-                        o[m] = mma8(o[m], va[sg], pp[pbase(m) + sg][0]);
-                        o[m] = mma8(o[m], va[sg], pp[pbase(m) + sg][1]);
-                    }
-                    O[c][m] = o[m];
-                }
-            }
-            // normaliser of this wave's query tile w: sum_i S_i + S . psi(q) +
-            // sum_s P (the second key pair only for w >= 2: a zero operand
-            // otherwise)
-            {
-                bf16x8 qw[KS];
-                q_ops(Qb, w, qw);
-                f32x4 dn = sdot(buf, qw), dp = {0.f, 0.f, 0.f, 0.f};   // two independent chains
-                const int pw = pbase(w);
-                const bf16x8 z8 = {};
-                const bool two = w >= 2;
+        for (int jt = 0; jt < JT; ++jt) Zs[jt] = Z[jt];
 #pragma unroll
-                for (int sg = 0; sg < 2; ++sg) {
-                    bf16x8 ph = nat8(pop_at(pw + (sg & (int)two), 0, lane)), pl = nat8(pop_at(pw + (sg & (int)two), 1, lane));
-                    if (sg == 1) { ph = two ? ph : z8; pl = two ? pl : z8; }
-                    dp = mma8(dp, ones8, ph);
-                    dp = mma8(dp, ones8, pl);
-                }
-                dn += dp;
-                if (g == 0) den_s[c * C + 16 * w + r] = dn[0];
-            }
-            // the next chunk's stage (chunks past the group stage zeros, never
-            // read); its VALU work can be scheduled between the products above
-            if constexpr (c + 1 < CPG) stage(IC<c + 1>{});
-            if constexpr (c == 0) {
-                if (grp > 0) look_back();
+        for (int m = 0; m < SPW; ++m) Ss[m] = S[m];
+        static_for<CPG>([&](auto cc) {
+            if constexpr (cc.value > 0)
+                if (cc.value < nch) pass1_chunk(cc);
+        });
+        publish();
+        set_flag();
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) Z[jt] = Zs[jt];
+#pragma unroll
+        for (int m = 0; m < SPW; ++m) S[m] = Ss[m];
+        if constexpr (CPG > 1) stage(IC<1>{});
+        if (grp > 0) look_back();
+    } else {
+        if (!last) load_start();
+        static_for<CPG>([&](auto cc) { issue_kv(cc); });
+        static_for<CPG>([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            if (c < nch) pass1_chunk(cc);
+        });
+        publish();
+        // the start state of pass 2, read again (group 0) before the flag, so
+        // that a last group writing the final state in place never overtakes it
+        load_start();
+        set_flag();
+        put_sops(S, 0);
+        stage(IC<0>{});
+        if (nch > 0) {   // always; keeps chunk 0 a region of its own for the scheduler
+            chunk(IC<0>{});
+            if constexpr (CPG > 1) stage(IC<1>{});
+            if (grp > 0) look_back();
+        }
+    }
+    static_for<CPG>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        if constexpr (c > 0) {
+            if (c < nch) {
+                chunk(cc);
+                // the next chunk's stage (chunks past the group stage zeros,
+                // never read); its VALU work can be scheduled between the
+                // products above
+                if constexpr (c + 1 < CPG) stage(IC<c + 1>{});
             }
         }
     });
