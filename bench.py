@@ -259,7 +259,7 @@ def main():
                    "rotated_sets": args.rotate},
         "roofline": roofline(alg_bytes_causal(w), per_call, measured_traffic(w.name)),
     }
-    line["roofline"]["kernels"] = ("k_chunk_fwd (one launch per la_causal_fwd call); duration = HIP-event time "
+    line["roofline"]["kernels"] = ("k_cs_fwd (one launch per la_causal_fwd call); duration = HIP-event time "
                                    "of the timed back-to-back calls / calls")
     if not args.headline_only:
         log("segmented workload ...")
