@@ -22,13 +22,14 @@
 //    the published states of the earlier groups of its head (the state before
 //    the group).  Workgroups only wait for lower-indexed ones of the same XCD,
 //    which the hardware dispatches first.
-//  * bf16 inputs at d = 64 (k_cs_fwd): each of the 4 waves owns 16 value
-//    columns for the whole group, so its slice of the state never leaves its
-//    registers.  Every chunk is first computed against the group-local state
-//    while the loads stream in; once the earlier groups' state is known it is
-//    added to the held numerators and normalisers, and the outputs are stored
-//    once.  Only psi = phi - 1 (bf16) enters the MFMAs; the all-ones part of
-//    phi is carried in fp32 (see k_cs_fwd).
+//  * bf16 inputs at d = 64 and 128 (k_cs_fwd): each of the 4 waves owns 16
+//    value columns for the whole group, so its slice of the state never
+//    leaves its registers.  q, k and v stay in registers for two passes: a
+//    state-only pass publishes the group's partial state early, then the
+//    outputs are computed chunk by chunk; the earlier groups' state is summed
+//    after the first chunk, which is corrected, and later chunks run against
+//    the full prefix.  Only psi = phi - 1 (bf16) enters the MFMAs; the
+//    all-ones part of phi is carried in fp32 (see k_cs_fwd).
 //  * Other dtype / d pairs (k_chunk_fwd): the 4 waves share the state through
 //    LDS (Z^T as bf16 hi + lo parts, S as an extra row) and each wave owns one
 //    16-row query tile; the published state is summed before the chunk loop.
@@ -1405,9 +1406,9 @@ __global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F
 //   phi(q) . z     = sum_i z_i + psi(q) . z            (z a column of Z, or S)
 //   phi(q) . phi(k) = d + sum psi(q) + sum psi(k) + psi(q) . psi(k)
 //   Z += psi(K)^T V + 1 (column sums of V)^T,  S += psi(K)^T 1 + (tokens) 1,
-// where the sums over dims of psi come from the stage (fp32, of the rounded
-// values) and the sums over dims of Z and S are MFMA products with an all-ones
-// operand.  The fp32 values fed back as operands -- the scores P and the state
+// where the sums over dims of psi(k) (formed in pass 1) and psi(q) (formed in
+// the stage) are fp32 sums of the values before rounding, and the sums over
+// dims of Z and S are MFMA products with an all-ones operand.  The fp32 values fed back as operands -- the scores P and the state
 // (Z, S) -- are split into bf16 hi + lo.
 //
 // State tile layout: tile jt = 2u + hf, row m = 4g + i of the tile holds key
