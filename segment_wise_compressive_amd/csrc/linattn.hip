@@ -2001,10 +2001,10 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
         load_start();
         issue_kv(IC<0>{});
         issue_q(IC<0>{});
-        if constexpr (CPG > 1) issue_kv(IC<1>{});
         put_sops(S, 0);
         stage_kv(IC<0>{});   // psi(k) of chunk 0 (its state update is part of chunk 0 below)
         stage(IC<0>{});
+        if constexpr (CPG > 1) issue_kv(IC<1>{});
         if constexpr (CPG > 2) issue_kv(IC<2>{});
         if (nch > 0) chunk(IC<0>{});   // always; keeps chunk 0 a region of its own for the scheduler
         __builtin_amdgcn_s_setprio(3);
