@@ -254,9 +254,10 @@ def test_zero_length_passes_state_through():
     assert not z.cpu().any() and not s.cpu().any()
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [200, 3000])
-def test_inplace_state_matches_separate_buffers(N):
-    B, H, d = 1, 3, 128
+def test_inplace_state_matches_separate_buffers(N, d):
+    B, H = 1, 3
     q, k, v = (t.to(DEV) for t in inp.qkv((B, H, N, d), 45, torch.bfloat16, d ** -0.5))
     z0, s0 = (t.to(DEV) for t in rand_state(B, H, d, 10))
     o1, z1, s1 = run_causal(q, k, v, z_in=z0, s_in=s0)
