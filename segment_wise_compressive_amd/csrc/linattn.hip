@@ -1751,7 +1751,7 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
     };
 
     const unsigned my_xcc = xcc_id();
-    constexpr bool EARLY0 = JT <= 4;   // chunk 0 of pass 2 before the rest of pass 1
+    constexpr bool EARLY0 = CPG > 2;   // chunk 0 of pass 2 before the rest of pass 1
     // numerators of every chunk of the group (registers), normalisers in LDS
     f32x4 O[CPG][4];
     // the state before the group: wait for the earlier groups' flags, sum
@@ -1984,8 +1984,9 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
     // outputs, chunk by chunk against the running state.  At d <= 64 chunk 0
     // of pass 2 runs first, as soon as its inputs arrive (its state is the
     // start state), and the state after it is kept while pass 1 advances
-    // over the remaining chunks; at larger d (register budget) pass 1 covers
-    // every chunk first and the start state is loaded again.  Then the state
+    // over the remaining chunks.  At d = 128 (two chunks per group, so pass 1
+    // is short and publishing early matters more) pass 1 covers every chunk
+    // first and the start state is loaded again.  Then the state
     // before the group is looked up (groups after the first) and chunk 0
     // corrected, so chunks 1.. see the full prefix.
     // Wave priorities follow progress: the two workgroups that share a CU
