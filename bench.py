@@ -81,6 +81,48 @@ def roofline(bytes_per_call, ms_per_call, traffic=None):
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
 
 
+def step_spread(fn, steps, n_rot, blocks=10):
+    """Per-call time over `blocks` consecutive blocks of steps (HIP events
+    around each block): median, p10 and p90 in ms.  Runs after the timed
+    region, as a second look at the same calls."""
+    import torch
+    per = max(1, steps // blocks)
+    times = []
+    for b in range(blocks):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(per):
+            fn((b * per + i) % n_rot)
+        t1.record()
+        torch.cuda.synchronize()
+        times.append(t0.elapsed_time(t1) / per)
+    times.sort()
+    pick = lambda f: times[min(len(times) - 1, int(round(f * (len(times) - 1))))]
+    return {"blocks": blocks, "calls_per_block": per, "median_ms": round(pick(0.5), 5),
+            "p10_ms": round(pick(0.1), 5), "p90_ms": round(pick(0.9), 5)}
+
+
+def copy_bandwidth(torch, reps=5):
+    """Achievable HBM bandwidth of a plain 1 GiB device copy (read + write),
+    GB/s: the second denominator beside the 8 TB/s peak."""
+    n = 256 * 1024 * 1024
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty(n, device="cuda")
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    del src, dst
+    return round(2 * 4 * n / (ms * 1e-3) / 1e9, 1)
+
+
 def bench_headline(args, torch, la, inp):
     w = inp.WORKLOADS[inp.HEADLINE]
     dev = torch.device("cuda:0")
@@ -99,7 +141,8 @@ def bench_headline(args, torch, la, inp):
         calls[i]()
 
     total_ms = time_steps(step, args.steps, args.warmup, n_rot)
-    return w, total_ms, total_ms / args.steps, (q, k, v)
+    spread = step_spread(step, args.steps, n_rot)
+    return w, total_ms, total_ms / args.steps, (q, k, v), spread
 
 
 def bench_segmented(args, torch, la, inp):
@@ -164,6 +207,19 @@ def bench_decode(args, torch, la, inp):
         bpc = B * H * (2 * (d * d + d) * 4 + 3 * d * w.dtype.itemsize + d * 4)
         res[label] = {"ms_per_step": round(ms, 5), "value": round(B * H / (ms * 1e-3), 1),
                       "roofline": roofline(bpc, ms)}
+    # the prefix as a full causal call with outputs: a large B*H data point
+    # (not the decode target)
+    pw = inp.Workload("decode_prefix", "causal", w.dtype, B, H, int(pq.shape[2]), d, 0, 1.0)
+    pqd, pkd, pvd = pq.to(dev), pk.to(dev), pv.to(dev)
+    pout = torch.empty(B, H, pq.shape[2], d, dtype=torch.float32, device=dev)
+    pws = torch.empty(max(1, la.la_causal_fwd_workspace(B, H, pq.shape[2], d, w.dtype, 0)), dtype=torch.uint8,
+                      device=dev)
+    pcall = la.prepare_causal_fwd(pqd, pkd, pvd, pout, eps=w.eps, workspace=pws)
+    psteps = max(3, args.steps // 30)
+    pms = time_steps(lambda _: pcall(), psteps, 2, 1) / psteps
+    res["prefix_causal_with_outputs"] = {"shape": [B, H, int(pq.shape[2]), d], "ms_per_call": round(pms, 4),
+                                         "value": round(B * H * pq.shape[2] / (pms * 1e-3), 1),
+                                         "roofline": roofline(alg_bytes_causal(pw), pms)}
     return {"workload": w.name, "unit": "head-tokens/s", **res}
 
 
@@ -239,7 +295,7 @@ def main():
     la.load_library()
 
     log("headline workload ...")
-    w, total_ms, per_call, qkv = bench_headline(args, torch, la, inp)
+    w, total_ms, per_call, qkv, spread = bench_headline(args, torch, la, inp)
     ms_step = total_ms / args.steps
     line = {
         "metric": METRIC,
@@ -261,6 +317,10 @@ def main():
     }
     line["roofline"]["kernels"] = ("k_cs_fwd (one launch per la_causal_fwd call); duration = HIP-event time "
                                    "of the timed back-to-back calls / calls")
+    line["step_spread"] = spread
+    copy_gbs = copy_bandwidth(torch)
+    line["roofline"]["copy_1gib_gbs"] = copy_gbs
+    line["roofline"]["frac_of_copy"] = round(line["roofline"]["achieved"] / copy_gbs, 4)
     if not args.headline_only:
         log("segmented workload ...")
         line.setdefault("workloads", {})["segmented"] = bench_segmented(args, torch, la, inp)
@@ -271,6 +331,7 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline(w, qkv, args.cpu_seconds)
+        line["cpu_baseline"]["gpu_over_cpu"] = round(line["value"] / line["cpu_baseline"]["value"], 1)
     print(json.dumps(line), flush=True)
 
 
