@@ -175,7 +175,7 @@ def bench_segmented(args, torch, la, inp):
     b_call = alg_bytes_causal(seg_w, with_state_io=True)
     return {"workload": w.name, "value": round(w.head_tokens / (ms * 1e-3), 1), "unit": "head-tokens/s",
             "ms_per_step": round(ms, 4), "calls_per_step": nseg,
-            "roofline": roofline(b_call, ms / nseg)}
+            "roofline": roofline(b_call, ms / nseg, measured_traffic(w.name))}
 
 
 def bench_decode(args, torch, la, inp):
@@ -206,7 +206,7 @@ def bench_decode(args, torch, la, inp):
         ms = total_ms / nst
         bpc = B * H * (2 * (d * d + d) * 4 + 3 * d * w.dtype.itemsize + d * 4)
         res[label] = {"ms_per_step": round(ms, 5), "value": round(B * H / (ms * 1e-3), 1),
-                      "roofline": roofline(bpc, ms)}
+                      "roofline": roofline(bpc, ms, measured_traffic(w.name))}
     # the prefix as a full causal call with outputs: a large B*H data point
     # (not the decode target)
     pw = inp.Workload("decode_prefix", "causal", w.dtype, B, H, int(pq.shape[2]), d, 0, 1.0)
@@ -239,7 +239,8 @@ def bench_noncausal(args, torch, la, inp):
     total_ms = time_steps(step, steps, 2, 1)
     per_call = total_ms / steps
     return {"workload": w.name, "value": round(w.head_tokens / (per_call * 1e-3), 1), "unit": "head-tokens/s",
-            "ms_per_step": round(per_call, 4), "roofline": roofline(alg_bytes_causal(w), per_call)}
+            "ms_per_step": round(per_call, 4),
+            "roofline": roofline(alg_bytes_causal(w), per_call, measured_traffic(w.name))}
 
 
 def cpu_baseline(w, qkv, seconds):
