@@ -1394,11 +1394,13 @@ __global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F
 // bf16 inputs, 64-token chunks, a group of at most CPG chunks per workgroup
 // with every q, k, v load of the group held in registers.  Each of the 4 waves
 // owns 16 of the workgroup's 64 value columns for the whole group: its slice
-// of the state Z (all D key dims x 16 columns) and a copy of S stay in its
-// registers, so the chunk loop shares no state through LDS.  Per chunk a wave
-// computes the scores of all 64 queries (the same in every wave), the inter-
-// and intra-chunk terms of its 16 columns, and the normaliser of one 16-query
-// tile, which goes to the other waves through LDS with the chunk's barrier.
+// of the state Z (all D key dims x 16 columns) stays in its registers, and it
+// holds D / 64 of the S tiles (the S operands of the normalisers go through
+// LDS).  Per chunk the 10 causal 16x16 score tiles are split over the waves
+// and shared through LDS; each wave then forms the inter- and intra-chunk
+// terms of its 16 columns for all 64 queries and the normaliser of one
+// 16-query tile, which goes to the other waves through LDS with the next
+// barrier.
 //
 // Precision: phi = 1 + psi with psi = elu, and only psi(q), psi(k) are bf16
 // MFMA operands (exact for positive inputs; the all-ones part of phi is
@@ -1408,8 +1410,9 @@ __global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F
 //   Z += psi(K)^T V + 1 (column sums of V)^T,  S += psi(K)^T 1 + (tokens) 1,
 // where the sums over dims of psi(k) (formed in pass 1) and psi(q) (formed in
 // the stage) are fp32 sums of the values before rounding, and the sums over
-// dims of Z and S are MFMA products with an all-ones operand.  The fp32 values fed back as operands -- the scores P and the state
-// (Z, S) -- are split into bf16 hi + lo.
+// dims of Z and S are MFMA products with an all-ones operand.  The fp32
+// values fed back as operands -- the scores P and the state (Z, S) -- are
+// split into bf16 hi + lo.
 //
 // State tile layout: tile jt = 2u + hf, row m = 4g + i of the tile holds key
 // dim pi(jt, m) = 32u + 8g + 4hf + i.  Then tiles 2u and 2u + 1 of a lane hold
@@ -1426,8 +1429,8 @@ template <int D> struct CSGeo {
     // swizzled, swz); the score operands [6 pairs][hi, lo][64 lanes][8]; the
     // S operands [2][hi, lo][KS][4 lane groups][8]; psi(Q) of every chunk of
     // the group [CPG][C][D] (swizzled); then fp32: the normalisers [CPG][C],
-    // the per-wave sums of S [2][4], the row sums of psi(q) and of psi(k)
-    // [2][C] each.
+    // the per-wave sums of S [2][4], the row sums of psi(q) [2][C] and of
+    // psi(k) [CPG][C].
     static constexpr int OK = 0, OV = C * D, OP = OV + C * DV, OSO = OP + 6 * 2 * 64 * 8;
     static constexpr int OQ = OSO + 2 * 2 * KS * 4 * 8;
     static constexpr int bf16_elems(int cpg) { return OQ + cpg * C * D; }
@@ -1836,7 +1839,7 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
     auto chunk = [&](auto cc) __attribute__((always_inline)) {
         constexpr int c = decltype(cc)::value;
         const int buf = c & 1, nv = nval_of(c);
-        __syncthreads();   // the stage is visible; the previous chunk's part B is done
+        __syncthreads();   // the stage is visible; the previous chunk's second half is done
         __builtin_amdgcn_s_setprio(CPG - 1 - c);   // progress-based priority (see pass 1)
         if constexpr (!EARLY0 && c + 2 < CPG) issue_q(IC<c + 2>{});
         const bf16 *Kb = kbuf(), *Qb = qslot(c), *Vb = vbuf();
