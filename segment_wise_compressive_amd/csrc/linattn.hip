@@ -82,12 +82,6 @@ __device__ __forceinline__ float phi(float x)
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b)
-{
-    bf16x2 v = {(bf16)a, (bf16)b};  // round to nearest even (v_cvt_pk_bf16_f32)
-    return __builtin_bit_cast(uint32_t, v);
-}
-
 // Raw 16-byte vector of inputs -> floats.  bf16: 8 values, fp32: 4 values.
 template <bool F32> struct Vec;
 template <> struct Vec<false> {
@@ -115,15 +109,9 @@ template <> struct Vec<true> {
 //
 // bf16: v_mfma_f32_16x16x32_bf16 takes 8 values per lane, so two fragments
 // (two K-tiles) are concatenated; A and B are concatenated the same way, so
-// every product pairs matching contraction indices.
+// every product pairs matching contraction indices (mma8 below).
 // fp32: v_mfma_f32_16x16x4_f32 takes 1 value per lane; fragment entry i of all
 // lanes forms one K=4 step, four steps per K-tile.
-__device__ __forceinline__ f32x4 mma2(f32x4 c, bf16x4 a0, bf16x4 a1, bf16x4 b0, bf16x4 b1)
-{
-    bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-    bf16x8 b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 
 __device__ __forceinline__ f32x4 mma1(f32x4 c, f32x4 a, f32x4 b)
 {
@@ -132,33 +120,6 @@ __device__ __forceinline__ f32x4 mma1(f32x4 c, f32x4 a, f32x4 b)
     c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
     return c;
-}
-
-__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x)
-{
-    bf16x4 r = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
-    return r;
-}
-
-__device__ __forceinline__ f32x4 to_f32x4(bf16x4 x)
-{
-    f32x4 r = {(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
-    return r;
-}
-
-// hi + lo split of an fp32 fragment into two bf16 fragments.
-__device__ __forceinline__ void split_hi_lo(f32x4 x, bf16x4 &hi, bf16x4 &lo)
-{
-    hi = to_bf16x4(x);
-    lo = to_bf16x4(x - to_f32x4(hi));
-}
-
-__device__ __forceinline__ float reduce_lane_groups(float x)
-{
-    // sum over the 4 lane groups (lanes r, r+16, r+32, r+48)
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
 }
 
 // Workgroup index remapping: hardware hands consecutive workgroup ids to the
@@ -219,7 +180,7 @@ __host__ __device__ constexpr int lds_bytes(bool f32, int d, int dv, int c)
 }
 constexpr int LDS_LIMIT = 160 * 1024;  // per workgroup on gfx950
 // workgroups per CU the causal kernel's register budget is sized for
-__host__ __device__ constexpr int minwg_of(bool f32, int d, int c) { return (d <= 64 && c == 64) ? (d == 64 ? 2 : 3) : 1; }
+__host__ __device__ constexpr int minwg_of(bool /*f32*/, int d, int c) { return (d <= 64 && c == 64) ? (d == 64 ? 2 : 3) : 1; }
 // Register-resident groups (64-token chunks): chunks a workgroup keeps in
 // registers, and the workgroups per CU its register budget is sized for.
 __host__ __device__ constexpr int res_cpg(bool f32, int d) { return d == 128 ? (f32 ? 1 : 2) : (f32 && d == 64 ? 2 : 4); }
