@@ -1351,6 +1351,38 @@ __global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F
     }
 }
 
+// Logical (unit = head x column block, group) of a column-split workgroup
+// from its remapped index.  When the remap is active and every XCD holds
+// whole units, the first half of an XCD's workgroups (dispatched first, one
+// per CU) takes the first half of each unit's groups and the second half the
+// rest, so a CU pairs group g with group g + G/2 of one unit rather than two
+// groups g: the look-back reads, which grow with g, are spread over the CUs.
+// Every group still comes after all earlier groups of its unit in dispatch
+// order within the XCD.  Otherwise the plain order (column block fastest,
+// then group, then head).
+__device__ __forceinline__ void cs_unit_group(int wg, int n, int G, int P, int &unit, int &grp)
+{
+    const int nx = n >> 3;
+    if ((n & 7) == 0 && G >= 2 && nx % G == 0) {
+        const int x = wg / nx, i = wg % nx, ux = nx / G, gl = G / 2;
+        int u, gg;
+        if (i < ux * gl) {
+            u = i / gl;
+            gg = i % gl;
+        } else {
+            const int i2 = i - ux * gl;
+            u = i2 / (G - gl);
+            gg = gl + i2 % (G - gl);
+        }
+        unit = x * ux + u;
+        grp = gg;
+    } else {
+        const int p = wg % P, rest = wg / P;
+        grp = rest % G;
+        unit = (rest / G) * P + p;
+    }
+}
+
 // ================================================================ column-split causal kernel
 // bf16 inputs, 64-token chunks, a group of at most CPG chunks per workgroup
 // with every q, k, v load of the group held in registers.  Each of the 4 waves
@@ -1482,9 +1514,10 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
     const int tid = threadIdx.x, lane = tid % WAVE, r = lane % 16, g = lane / 16;
     const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);   // wave-uniform
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
-    const int p = wg % a.P, rest = wg / a.P, grp = rest % a.G, bh = rest / a.G;
+    int hp, grp;
+    cs_unit_group(wg, gridDim.x, a.G, a.P, hp, grp);
+    const int p = hp % a.P, bh = hp / a.P;
     const int b = bh / a.H, h = bh % a.H;
-    const int hp = bh * a.P + p;
     const int t_begin = grp * a.L, t_end = min(t_begin + a.L, a.N);
     const int nch = (t_end - t_begin + C - 1) / C;
     const bool last = grp == a.G - 1;
