@@ -73,6 +73,21 @@ def test_causal_small_all_elements(dtype, d, N):
     assert state_err(s.cpu(), torch.from_numpy(rs)) < tol
 
 
+@pytest.mark.parametrize("B,H,N,d", [(1, 8, 300, 64), (1, 8, 448, 64), (1, 4, 300, 128), (2, 8, 1000, 64)])
+def test_causal_group_orders(B, H, N, d):
+    # shapes whose workgroups fill whole XCDs with whole heads (the grid
+    # order that pairs early and late groups on a CU, odd group counts
+    # included) and one that does not; every element against the oracle
+    _log(f"causal group orders B={B} H={H} N={N} d={d}")
+    q, k, v = inp.qkv((B, H, N, d), 600 + N + d, torch.bfloat16, d ** -0.5)
+    z0, s0 = rand_state(B, H, d, 11, 0.5)
+    ro, rz, rs = oracle.causal(q, k, v, 1e-6, z0, s0)
+    out, z, s = run_causal(*(t.to(DEV) for t in (q, k, v)), z_in=z0.to(DEV), s_in=s0.to(DEV))
+    assert heads_err(out.cpu(), ro, d) < 2e-3
+    assert state_err(z.cpu(), torch.from_numpy(rz)) < 2e-3
+    assert state_err(s.cpu(), torch.from_numpy(rs)) < 2e-3
+
+
 @pytest.mark.parametrize("chunk", [16, 32, 64, 128])
 @pytest.mark.parametrize("d", [64, 128])
 def test_causal_chunk_sizes_and_groups(chunk, d):
