@@ -53,6 +53,8 @@ def _load():
         lib.oracle_decode_step.restype = None
         lib.oracle_noncausal.argtypes = [L, L, L, D, fp, fp, fp, dp, dp, dp]
         lib.oracle_noncausal.restype = None
+        lib.oracle_memory.argtypes = [L, L, L, D, fp, fp, fp, dp, dp, dp, dp, dp]
+        lib.oracle_memory.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -132,5 +134,24 @@ def noncausal(q, k, v, eps: float, want_out: bool = True):
     so = np.empty((BH, d), np.float64)
     _load().oracle_noncausal(BH, N, d, float(eps), _fptr(qa), _fptr(ka), _fptr(va),
                              _dptr(out), _dptr(zo), _dptr(so))
+    return (None if out is None else out.reshape(*lead, N, d),
+            zo.reshape(*lead, d, d), so.reshape(*lead, d))
+
+
+def memory(q, k, v, eps: float, z_in=None, s_in=None, want_out: bool = True):
+    """Compressive memory of one segment: every query reads (z_in, s_in), the
+    memory left by earlier segments; then the segment's keys and values are
+    added.  Returns (out [..., N, d] or None, z_out [..., d, d], s_out [..., d])
+    in float64."""
+    qa, ka, va = _f32(q), _f32(k), _f32(v)
+    lead, (N, d) = qa.shape[:-2], qa.shape[-2:]
+    BH = int(np.prod(lead)) if lead else 1
+    zi = None if z_in is None else _f64(z_in).reshape(BH, d, d)
+    si = None if s_in is None else _f64(s_in).reshape(BH, d)
+    out = np.empty((BH, N, d), np.float64) if want_out else None
+    zo = np.empty((BH, d, d), np.float64)
+    so = np.empty((BH, d), np.float64)
+    _load().oracle_memory(BH, N, d, float(eps), _fptr(qa), _fptr(ka), _fptr(va),
+                          _dptr(zi), _dptr(si), _dptr(out), _dptr(zo), _dptr(so))
     return (None if out is None else out.reshape(*lead, N, d),
             zo.reshape(*lead, d, d), so.reshape(*lead, d))

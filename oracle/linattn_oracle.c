@@ -186,3 +186,58 @@ void oracle_noncausal(long BH, long N, long d, double eps,
         free(Z); free(S); free(g);
     }
 }
+
+/*
+ * Compressive memory of one segment ("Segment-Wise Attention": the memory is
+ * an associative matrix, read and updated with the linear-attention rule of
+ * "Transformers are RNNs", and the thread's read divides the retrieved memory
+ * by the retrieved norm term).  Every query of the segment reads only what
+ * the earlier segments left in the memory:
+ *   out_t = phi(q_t)^T M / (phi(q_t) . n + eps)   with (M, n) = (z_in, s_in),
+ * and then the memory takes in the whole segment:
+ *   z_out = M + sum_t phi(k_t) v_t^T,  s_out = n + sum_t phi(k_t).
+ * z_in / s_in may be NULL (zeros: the first segment reads 0 / eps); out,
+ * z_out, s_out may be NULL (not written).
+ */
+void oracle_memory(long BH, long N, long d, double eps,
+                   const float *q, const float *k, const float *v,
+                   const double *z_in, const double *s_in,
+                   double *out, double *z_out, double *s_out)
+{
+    long h;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (h = 0; h < BH; ++h) {
+        double *mem = (double *)calloc((size_t)(d * d), sizeof(double));
+        double *norm = (double *)calloc((size_t)d, sizeof(double));
+        double *fq = (double *)malloc((size_t)d * sizeof(double));
+        long t, i, c;
+        if (z_in) memcpy(mem, z_in + h * d * d, (size_t)(d * d) * sizeof(double));
+        if (s_in) memcpy(norm, s_in + h * d, (size_t)d * sizeof(double));
+        /* the read, from the memory of the earlier segments */
+        for (t = 0; out && t < N; ++t) {
+            const float *qrow = q + (h * N + t) * d;
+            double *orow = out + (h * N + t) * d;
+            double retrieved_norm = eps;
+            for (i = 0; i < d; ++i) fq[i] = phi((double)qrow[i]);
+            for (i = 0; i < d; ++i) retrieved_norm += fq[i] * norm[i];
+            for (c = 0; c < d; ++c) {
+                double retrieved = 0.0;
+                for (i = 0; i < d; ++i) retrieved += fq[i] * mem[i * d + c];
+                orow[c] = retrieved / retrieved_norm;
+            }
+        }
+        /* the update, with every key and value of the segment */
+        for (t = 0; t < N; ++t) {
+            const float *krow = k + (h * N + t) * d;
+            const float *vrow = v + (h * N + t) * d;
+            for (i = 0; i < d; ++i) {
+                const double fk = phi((double)krow[i]);
+                for (c = 0; c < d; ++c) mem[i * d + c] += fk * (double)vrow[c];
+                norm[i] += fk;
+            }
+        }
+        if (z_out) memcpy(z_out + h * d * d, mem, (size_t)(d * d) * sizeof(double));
+        if (s_out) memcpy(s_out + h * d, norm, (size_t)d * sizeof(double));
+        free(mem); free(norm); free(fq);
+    }
+}

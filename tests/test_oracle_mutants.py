@@ -32,6 +32,13 @@ MUTANTS = {
     "decode_skips_key_sum": ("            Sh[j] += fj;", "            Sh[j] += 0.0 * fj;"),
     "noncausal_sum_stops_early": ("        for (t = 0; t < N; ++t) {\n            const float *kt = k + (h * N + t) * d;\n            const float *vt = v + (h * N + t) * d;\n            for (j = 0; j < d; ++j) {\n                double fj",
                                   "        for (t = 0; t + 1 < N; ++t) {\n            const float *kt = k + (h * N + t) * d;\n            const float *vt = v + (h * N + t) * d;\n            for (j = 0; j < d; ++j) {\n                double fj"),
+    "memory_read_without_norm_term": ("for (i = 0; i < d; ++i) retrieved_norm += fq[i] * norm[i];",
+                                      "for (i = 0; i < d; ++i) retrieved_norm += fq[i];"),
+    "memory_update_without_phi": ("const double fk = phi((double)krow[i]);", "const double fk = (double)krow[i];"),
+    "memory_read_map_is_x_plus_one": ("for (i = 0; i < d; ++i) fq[i] = phi((double)qrow[i]);",
+                                      "for (i = 0; i < d; ++i) fq[i] = (double)qrow[i] + 1.0;"),
+    "memory_in_ignored": ("if (z_in) memcpy(mem,", "if (0) memcpy(mem,"),
+    "memory_read_transposed": ("retrieved += fq[i] * mem[i * d + c];", "retrieved += fq[i] * mem[c * d + i];"),
 }
 
 

@@ -276,3 +276,85 @@ def test_zero_length_passes_state_through():
     assert out.shape == (2, 0, d)
     np.testing.assert_array_equal(z, zi)
     np.testing.assert_array_equal(s, si)
+
+
+# ---------------------------------------------------------------- compressive memory (retrieval, then update)
+def _block_masked(q, k, v, bounds, eps):
+    """Brute force over the attention matrix of the segment loop: token t of
+    the segment [a, b) sees every token i < a (all earlier segments), none of
+    its own segment; one head, q, k, v [N, d]."""
+    g, f = phi(q), phi(k)
+    N = q.shape[0]
+    seg_start = np.empty(N, np.int64)
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        seg_start[a:b] = a
+    mask = (np.arange(N)[None, :] < seg_start[:, None]).astype(np.float64)
+    W = (g @ f.T) * mask
+    return (W @ v.astype(np.float64)) / (W.sum(axis=1) + eps)[:, None]
+
+
+@pytest.mark.parametrize("cuts", [(5,), (1, 2, 30), (9, 9, 20), (16, 32, 48)])
+def test_memory_chain_matches_block_masked_brute_force(cuts):
+    N, d = 64, 6
+    q, k, v = (rnd((2, N, d), 140 + i, 0.7) for i in range(3))
+    bounds = [0, *cuts, N]
+    z = s = None
+    pieces = []
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        o, z, s = oracle.memory(q[:, a:b], k[:, a:b], v[:, a:b], 1e-6, z, s)
+        pieces.append(o)
+    out = np.concatenate(pieces, axis=1)
+    first = bounds[1]
+    # the first segment has an empty memory: 0 / eps
+    assert np.array_equal(out[:, :first], np.zeros_like(out[:, :first]))
+    for h in range(2):
+        ref = _block_masked(q[h], k[h], v[h], bounds, 1e-6)
+        assert rowwise_rel_err(out[h, first:], ref[first:]) < TIGHT
+    # the memory after the last segment is the state of the whole sequence
+    _, zf, sf = oracle.causal(q, k, v, 1e-6)
+    np.testing.assert_allclose(z, zf, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(s, sf, rtol=1e-13)
+
+
+def test_memory_zero_q_k_reads_scaled_mean_of_earlier_values():
+    N0, N1, d = 11, 5, 4
+    z0 = np.zeros((1, N0, d), np.float32)
+    v0 = rnd((1, N0, d), 150)
+    _, zm, sm = oracle.memory(z0, z0, v0, 1e-6)
+    q1 = np.zeros((1, N1, d), np.float32)
+    out, _, _ = oracle.memory(q1, q1, rnd((1, N1, d), 151), 1e-6, zm, sm)
+    # phi(0) = 1: every read is d * sum(v) / (d * N0 + eps), the same for all queries
+    ref = d * v0[0].astype(np.float64).sum(axis=0) / (d * N0 + 1e-6)
+    for t in range(N1):
+        assert rowwise_rel_err(out[0, t], ref) < TIGHT
+
+
+def test_memory_of_one_token_is_its_value_scaled():
+    d = 5
+    q0, k0, v0 = (rnd((1, 1, d), 160 + i) for i in range(3))
+    _, zm, sm = oracle.memory(q0, k0, v0, 1e-6)
+    q1 = rnd((1, 3, d), 163)
+    out, _, _ = oracle.memory(q1, rnd((1, 3, d), 164), rnd((1, 3, d), 165), 1e-6, zm, sm)
+    for t in range(3):
+        w = float(phi(q1[0, t]) @ phi(k0[0, 0]))
+        assert rowwise_rel_err(out[0, t], w * v0[0, 0].astype(np.float64) / (w + 1e-6)) < TIGHT
+
+
+def test_memory_empty_memory_reads_zero_or_nan():
+    d = 4
+    q, k, v = (rnd((2, 3, d), 170 + i) for i in range(3))
+    out, _, _ = oracle.memory(q, k, v, 1e-6)
+    assert np.array_equal(out, np.zeros_like(out))
+    out0, _, _ = oracle.memory(q, k, v, 0.0)   # 0 / 0
+    assert np.isnan(out0).all()
+
+
+def test_memory_zero_length_passes_state_through():
+    d = 4
+    e = np.zeros((2, 0, d), np.float32)
+    zi = rnd((2, d, d), 180).astype(np.float64)
+    si = rnd((2, d), 181).astype(np.float64)
+    out, z, s = oracle.memory(e, e, e, 1e-6, zi, si)
+    assert out.shape == (2, 0, d)
+    np.testing.assert_array_equal(z, zi)
+    np.testing.assert_array_equal(s, si)
