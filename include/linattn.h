@@ -141,6 +141,36 @@ la_status la_noncausal_fwd(const void *q, la_strides sq, const void *k, la_strid
                            int B, int H, int N, int d, float eps,
                            void *workspace, size_t ws_bytes, void *hip_stream);
 
+/*
+ * Compressive memory of one segment, Infini-attention style ("Segment-Wise
+ * Attention": the memory is an associative matrix, read and updated with the
+ * linear-attention rule of "Transformers are RNNs", and a read is the
+ * retrieved memory divided by the retrieved norm term).  Every query of the
+ * segment reads only the memory that earlier segments left, then the
+ * segment's keys and values are added to it:
+ *   out_t = phi(q_t)^T Z_in / (phi(q_t) . S_in + eps)   for every t,
+ *   Z_out = Z_in + sum_t phi(k_t) v_t^T,  S_out = S_in + sum_t phi(k_t).
+ * q, k, v, out, strides, B, H, N, d, eps, dt: as for la_noncausal_fwd.
+ * z_in / s_in: [B, H, d, d] / [B, H, d] float32, the memory before the
+ * segment; NULL means zeros (the first segment: every read is 0 / eps).
+ * z_out / s_out: the memory after the segment; NULL means not written.  They
+ * may equal z_in / s_in exactly (in place); any other overlap is
+ * LA_ERR_ALIAS.  out: NULL computes only the update; then z_out and s_out
+ * must not both be NULL (LA_ERR_NULL).
+ * N = 0 copies the input memory (or zeros) to the output.
+ * The sum over the segment is split across workgroups and reduced in a fixed
+ * order (deterministic).
+ * Workspace: at least la_memory_workspace(...) bytes, any contents.
+ */
+size_t la_memory_workspace(int B, int H, int N, int d, la_dtype dt);
+la_status la_memory_fwd(const void *q, la_strides sq, const void *k, la_strides sk,
+                        const void *v, la_strides sv, la_dtype dt,
+                        float *out, la_strides so,
+                        int B, int H, int N, int d, float eps,
+                        const float *z_in, const float *s_in,
+                        float *z_out, float *s_out,
+                        void *workspace, size_t ws_bytes, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

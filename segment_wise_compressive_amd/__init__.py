@@ -26,8 +26,9 @@ __all__ = [
     "la_causal_fwd_workspace", "la_causal_fwd",
     "la_decode_step",
     "la_noncausal_workspace", "la_noncausal_fwd",
-    "causal_fwd", "noncausal_fwd", "decode_step",
-    "Prepared", "prepare_causal_fwd", "prepare_noncausal_fwd", "prepare_decode_step",
+    "la_memory_workspace", "la_memory_fwd",
+    "causal_fwd", "noncausal_fwd", "decode_step", "memory_fwd",
+    "Prepared", "prepare_causal_fwd", "prepare_noncausal_fwd", "prepare_decode_step", "prepare_memory_fwd",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -77,6 +78,11 @@ def load_library():
     lib.la_noncausal_workspace.restype = sz
     lib.la_noncausal_fwd.argtypes = [vp, S, vp, S, vp, S, i32, vp, S, i32, i32, i32, i32, f32, vp, sz, vp]
     lib.la_noncausal_fwd.restype = i32
+    lib.la_memory_workspace.argtypes = [i32, i32, i32, i32, i32]
+    lib.la_memory_workspace.restype = sz
+    lib.la_memory_fwd.argtypes = [vp, S, vp, S, vp, S, i32, vp, S, i32, i32, i32, i32, f32,
+                                  vp, vp, vp, vp, vp, sz, vp]
+    lib.la_memory_fwd.restype = i32
     _lib = lib
     return lib
 
@@ -130,6 +136,11 @@ def _causal_ws(B, H, N, d, code, chunk, flags) -> int:
 @functools.lru_cache(maxsize=4096)
 def _noncausal_ws(B, H, N, d, code) -> int:
     return int(load_library().la_noncausal_workspace(B, H, N, d, code))
+
+
+@functools.lru_cache(maxsize=4096)
+def _memory_ws(B, H, N, d, code) -> int:
+    return int(load_library().la_memory_workspace(B, H, N, d, code))
 
 
 def la_causal_fwd_workspace(B: int, H: int, N: int, d: int, dtype: torch.dtype,
@@ -262,6 +273,52 @@ def la_noncausal_fwd(q, k, v, out, *, eps: float = 1e-6,
     prepare_noncausal_fwd(q, k, v, out, eps=eps, workspace=workspace, stream=stream)()
 
 
+def la_memory_workspace(B: int, H: int, N: int, d: int, dtype: torch.dtype) -> int:
+    code = LA_F32 if dtype == torch.float32 else LA_BF16
+    return _memory_ws(B, H, N, d, code)
+
+
+def prepare_memory_fwd(q, k, v, out=None, *, eps: float = 1e-6,
+                       z_in=None, s_in=None, z_out=None, s_out=None,
+                       workspace: Optional[torch.Tensor] = None, stream=None) -> Prepared:
+    """Check and marshal a la_memory_fwd call (nothing runs until it is called).
+
+    q, k, v: [B, H, N, d] bf16 or fp32 CUDA tensors (unit d stride); out:
+    float32 [B, H, N, d] or None (update only).  Memory: float32 contiguous
+    [B, H, d, d] / [B, H, d]; z_out/s_out may be the z_in/s_in tensors themselves.
+    """
+    B, H, N, d = q.shape
+    if tuple(k.shape) != (B, H, N, d) or tuple(v.shape) != (B, H, N, d):
+        raise ValueError("q, k, v must have the same shape")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must have the same dtype")
+    if out is not None and (out.dtype != torch.float32 or tuple(out.shape) != (B, H, N, d)):
+        raise ValueError("out must be float32 [B, H, N, d]")
+    for t, shp, nm in ((z_in, (B, H, d, d), "z_in"), (z_out, (B, H, d, d), "z_out"),
+                       (s_in, (B, H, d), "s_in"), (s_out, (B, H, d), "s_out")):
+        _state_check(t, shp, nm)
+    ws_bytes = la_memory_workspace(B, H, N, d, q.dtype)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    so = _strides(out) if out is not None else la_strides(0, 0, 0)
+    args = [_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v), _dtype_code(q),
+            _ptr(out), so, B, H, N, d, ctypes.c_float(eps),
+            _ptr(z_in), _ptr(s_in), _ptr(z_out), _ptr(s_out), _ptr(workspace), ctypes.c_size_t(have),
+            _opt_stream(stream, q.device)]
+    return Prepared(load_library().la_memory_fwd, args, q.device, "la_memory_fwd",
+                    (q, k, v, out, z_in, s_in, z_out, s_out, workspace))
+
+
+def la_memory_fwd(q, k, v, out=None, *, eps: float = 1e-6,
+                  z_in=None, s_in=None, z_out=None, s_out=None,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Compressive memory of one segment (la_memory_fwd in linattn.h); arguments
+    as for prepare_memory_fwd."""
+    prepare_memory_fwd(q, k, v, out, eps=eps, z_in=z_in, s_in=s_in, z_out=z_out, s_out=s_out,
+                       workspace=workspace, stream=stream)()
+
+
 # ---------------------------------------------------------------- conveniences
 def causal_fwd(q, k, v, *, eps: float = 1e-6, chunk: int = 0,
                state: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
@@ -290,6 +347,18 @@ def decode_step(q, k, v, z, s, *, eps: float = 1e-6):
     out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     la_decode_step(q, k, v, z, s, out, eps=eps)
     return out
+
+
+def memory_fwd(q, k, v, memory: Optional[Tuple[torch.Tensor, torch.Tensor]] = None, *, eps: float = 1e-6):
+    """Reads of one segment from the memory of earlier segments, and the
+    memory after the segment: returns (out, (z, s))."""
+    B, H, N, d = q.shape
+    out = torch.empty(B, H, N, d, dtype=torch.float32, device=q.device)
+    z_in, s_in = memory if memory is not None else (None, None)
+    z_out = torch.empty(B, H, d, d, dtype=torch.float32, device=q.device)
+    s_out = torch.empty(B, H, d, dtype=torch.float32, device=q.device)
+    la_memory_fwd(q, k, v, out, eps=eps, z_in=z_in, s_in=s_in, z_out=z_out, s_out=s_out)
+    return out, (z_out, s_out)
 
 
 def declared_entry_points(header: Optional[str] = None):

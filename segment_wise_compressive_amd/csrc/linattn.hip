@@ -723,7 +723,12 @@ __global__ void __launch_bounds__(NTHR) k_group_state(const Args a)
 //                  for i < nslots: the starting states of the token groups.
 //  mode 1 (total): z_out/s_out <- carried-in state + sum of the nslots slots.
 //  mode 2 (fin):   fin <- sum of the nslots slots.
-// Each element is read and written by one thread, so z_out may be z_in.
+//  mode 3 (memory): fin <- carried-in state (or 0), the memory that every
+//                  query reads; z_out/s_out <- carried-in state + sum of the
+//                  nslots slots.
+// Each element is read and written by one thread, so z_out may be z_in (the
+// S elements: by the thread of column block 0 only, which in mode 3 also
+// writes fin's copy of S for every column block).
 template <int D, int DV>
 __global__ void __launch_bounds__(256) k_slots(const Args a, int nslots, int mode)
 {
@@ -733,7 +738,7 @@ __global__ void __launch_bounds__(256) k_slots(const Args a, int nslots, int mod
     const int kk = blockIdx.x * 256 + threadIdx.x;
     if (kk >= SL) return;
     const bool is_s = kk >= SZ;
-    if (is_s && p != 0 && mode == 1) return;  // S is identical in every column block
+    if (is_s && p != 0 && (mode == 1 || mode == 3)) return;  // S is identical in every column block
     int64_t gidx;
     if (!is_s) {
         const int j = kk / DV, c = kk % DV;
@@ -765,6 +770,13 @@ __global__ void __launch_bounds__(256) k_slots(const Args a, int nslots, int mod
         }
         return;
     }
+    if (mode == 3 && a.fin) {
+        if (is_s) {
+            for (int pp = 0; pp < a.P; ++pp) a.fin[((int64_t)bh * a.P + pp) * SL + kk] = acc;
+        } else {
+            a.fin[(int64_t)hp * SL + kk] = acc;
+        }
+    }
     float vals[8];
     int i = 0;
     for (; i + 8 <= nslots; i += 8) {
@@ -774,7 +786,7 @@ __global__ void __launch_bounds__(256) k_slots(const Args a, int nslots, int mod
         for (int u = 0; u < 8; ++u) acc += vals[u];
     }
     for (; i < nslots; ++i) acc += src[(int64_t)i * SL];
-    if (mode == 1) {
+    if (mode == 1 || mode == 3) {
         float *dst = is_s ? a.s_out : a.z_out;
         if (dst) dst[gidx] = acc;
     } else {
@@ -2549,7 +2561,7 @@ void dispatch(bool f32, int d, int C, int what, const Args &a, int nwg, hipStrea
 }
 
 // mode: 0 = scan into group starting states, 1 = total into z_out/s_out,
-// 2 = total into fin.
+// 2 = total into fin, 3 = carried-in state into fin and total into z_out/s_out.
 void launch_slots(int d, const Args &a, int64_t BH, int P, int nslots, int mode, hipStream_t st)
 {
     const int sl = cols_per_wg(d) * d + d;
@@ -2757,6 +2769,75 @@ la_status la_noncausal_fwd(const void *q, la_strides sq, const void *k, la_strid
     a.G = (N + la - 1) / la;
     if (cs) hipLaunchKernelGGL((k_cs_apply<64>), dim3((unsigned)(BH * pl.P * a.G)), dim3(NTHR), 0, stream, a);
     else dispatch(f32, d, pl.C, 2, a, (int)(BH * pl.P * a.G), stream);
+    return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
+}
+
+size_t la_memory_workspace(int B, int H, int N, int d, la_dtype dt)
+{
+    if (check_common(B, H, N, d, dt, 0.f) != LA_OK) return 0;
+    return plan_noncausal(B, H, N, d, dt).total;
+}
+
+// The non-causal kernels with the carried-in memory as the state that the
+// queries read: 1) partial states of the segment's token groups, 2) the
+// memory copied for the readout and the updated memory written out, 3) every
+// query against the memory before the segment.
+la_status la_memory_fwd(const void *q, la_strides sq, const void *k, la_strides sk,
+                        const void *v, la_strides sv, la_dtype dt,
+                        float *out, la_strides so,
+                        int B, int H, int N, int d, float eps,
+                        const float *z_in, const float *s_in,
+                        float *z_out, float *s_out,
+                        void *workspace, size_t ws_bytes, void *hip_stream)
+{
+    la_status st = check_common(B, H, N, d, dt, eps);
+    if (st != LA_OK) return st;
+    const size_t es = dt == LA_F32 ? 4 : 2;
+    const bool want_out = out != nullptr;
+    if (!want_out && !z_out && !s_out) return LA_ERR_NULL;
+    if (N > 0) {
+        if ((st = check_tensor(q, sq, es)) != LA_OK) return st;
+        if ((st = check_tensor(k, sk, es)) != LA_OK) return st;
+        if ((st = check_tensor(v, sv, es)) != LA_OK) return st;
+        if (want_out && (st = check_tensor(out, so, 4)) != LA_OK) return st;
+    }
+    for (const void *p : {(const void *)z_in, (const void *)s_in, (const void *)z_out, (const void *)s_out})
+        if (p && !aligned16(p)) return LA_ERR_ALIGN;
+    const int64_t BH = (int64_t)B * H;
+    const size_t zb = (size_t)BH * d * d * 4, sb = (size_t)BH * d * 4;
+    if (z_out && z_in && z_out != (float *)z_in && overlaps(z_out, zb, z_in, zb)) return LA_ERR_ALIAS;
+    if (s_out && s_in && s_out != (float *)s_in && overlaps(s_out, sb, s_in, sb)) return LA_ERR_ALIAS;
+    if (overlaps(z_out, zb, s_in, sb) || overlaps(s_out, sb, z_in, zb) || overlaps(z_out, zb, s_out, sb))
+        return LA_ERR_ALIAS;
+    Plan pl = plan_noncausal(B, H, N, d, dt);
+    if (ws_bytes < pl.total || (pl.total > 0 && !workspace)) return LA_ERR_WORKSPACE;
+    if (BH == 0) return LA_OK;
+    hipStream_t stream = (hipStream_t)hip_stream;
+    (void)hipGetLastError();
+    char *ws = (char *)workspace;
+    Args a = make_args(q, sq, k, sk, v, sv, out, so, B, H, N, eps);
+    a.z_in = z_in; a.s_in = s_in; a.z_out = z_out; a.s_out = s_out;
+    a.P = pl.P; a.NS = pl.NS;
+    if (N == 0) {
+        // the carried-in memory (or zeros) passes through
+        launch_slots(d, a, BH, pl.P, 0, 1, stream);
+        return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
+    }
+    a.part = (float *)ws;
+    a.fin = want_out ? (float *)(ws + pl.fin_off) : nullptr;
+    const bool f32 = dt == LA_F32;
+    a.G = pl.G; a.L = pl.L; a.slot0 = 0;
+    const bool cs = LA_COLUMN_SPLIT && !f32 && d == 64 && pl.C == 64;
+    if (cs) hipLaunchKernelGGL((k_cs_state<64>), dim3((unsigned)(BH * pl.P * pl.G)), dim3(NTHR), 0, stream, a);
+    else dispatch(f32, d, pl.C, 0, a, (int)(BH * pl.P * pl.G), stream);
+    launch_slots(d, a, BH, pl.P, pl.G, 3, stream);
+    if (want_out) {
+        const int la = pl.C * 4;
+        a.L = la;
+        a.G = (N + la - 1) / la;
+        if (cs) hipLaunchKernelGGL((k_cs_apply<64>), dim3((unsigned)(BH * pl.P * a.G)), dim3(NTHR), 0, stream, a);
+        else dispatch(f32, d, pl.C, 2, a, (int)(BH * pl.P * a.G), stream);
+    }
     return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }
 

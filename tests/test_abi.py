@@ -27,7 +27,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = la.declared_entry_points()
     assert set(names) == {"la_status_str", "la_version", "la_causal_fwd_workspace", "la_causal_fwd",
-                          "la_decode_step", "la_noncausal_workspace", "la_noncausal_fwd"}
+                          "la_decode_step", "la_noncausal_workspace", "la_noncausal_fwd",
+                          "la_memory_workspace", "la_memory_fwd"}
     raw = ctypes.CDLL(la.library_path())
     for n in names:
         assert hasattr(raw, n), n
@@ -118,6 +119,41 @@ def test_noncausal_validation(lib):
     assert lib.la_noncausal_fwd(*bad) == 7
     bad = list(base); bad[2] = vp(FAKE + 0x100002)
     assert lib.la_noncausal_fwd(*bad) == 4
+
+
+def _memory(lib, **kw):
+    B, H, N, d = kw.get("B", 1), kw.get("H", 2), kw.get("N", 128), kw.get("d", 64)
+    st = la_strides(H * N * d, N * d, d)
+    args = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, dt=la.LA_BF16, out=FAKE + 0x300000,
+                so=st, eps=1e-6, z_in=None, s_in=None, z_out=None, s_out=None,
+                ws=FAKE + 0x400000, ws_bytes=1 << 30, sq=st, sk=st, sv=st)
+    args.update(kw)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.la_memory_fwd(vp(args["q"]), args["sq"], vp(args["k"]), args["sk"], vp(args["v"]), args["sv"],
+                             args["dt"], vp(args["out"]), args["so"], B, H, N, d, args["eps"],
+                             vp(args["z_in"]), vp(args["s_in"]), vp(args["z_out"]), vp(args["s_out"]),
+                             vp(args["ws"]), args["ws_bytes"], None)
+
+
+@no_device
+@pytest.mark.parametrize("kw, status", [
+    (dict(d=48), 5), (dict(dt=7), 3), (dict(eps=-1.0), 6), (dict(eps=float("nan")), 6),
+    (dict(N=-1), 2), (dict(q=None), 1), (dict(v=None), 1),
+    (dict(out=None), 1),                                 # update only needs z_out or s_out
+    (dict(k=FAKE + 0x100002), 4), (dict(out=FAKE + 0x300004), 4),
+    (dict(ws=None), 7), (dict(ws_bytes=16), 7),
+    (dict(z_in=FAKE + 0x500000, z_out=FAKE + 0x500000 + 64), 8),
+    (dict(s_in=FAKE + 0x500000, z_out=FAKE + 0x500000 - 256), 8),
+    (dict(s_out=FAKE + 0x500008), 4),
+])
+def test_memory_validation(lib, kw, status):
+    assert _memory(lib, **kw) == status
+
+
+def test_memory_workspace_query(lib):
+    assert la.la_memory_workspace(1, 16, 2048, 128, torch.bfloat16) > 0
+    assert la.la_memory_workspace(1, 16, 0, 128, torch.bfloat16) == 0
+    assert la.la_memory_workspace(1, 16, 2048, 96, torch.bfloat16) == 0
 
 
 def test_binding_rejects_bad_tensors():
