@@ -9,8 +9,8 @@ twice the 256 MB Infinity Cache) are rotated so every step reads HBM.
 Prints ONE JSON line: value = B*H*N head-tokens per second over the timed
 steps; `roofline` = algorithmic bytes of one call / its average duration
 (HIP events on the launch stream) against 8 TB/s; `cpu_baseline` = the fp64
-oracle on the host cores; `workloads` = the segment-carried, decode and
-non-causal workloads timed the same way.
+oracle on the host cores; `workloads` = the segment-carried, decode,
+non-causal and compressive-memory workloads timed the same way.
 """
 import argparse
 import json
@@ -243,6 +243,39 @@ def bench_noncausal(args, torch, la, inp):
             "roofline": roofline(alg_bytes_causal(w), per_call, measured_traffic(w.name))}
 
 
+def bench_memory(args, torch, la, inp):
+    """The compressive-memory loop: 32 la_memory_fwd calls of 2048 tokens,
+    each reading the memory of the earlier segments and adding its own."""
+    w = inp.WORKLOADS[inp.MEMORY]
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in inp.workload_inputs(w))
+    B, H, N, d = q.shape
+    out = torch.empty(B, H, N, d, dtype=torch.float32, device=dev)
+    zs = [torch.zeros(B, H, d, d, device=dev) for _ in range(2)]
+    ss = [torch.zeros(B, H, d, device=dev) for _ in range(2)]
+    ws = torch.empty(max(1, la.la_memory_workspace(B, H, w.segment, d, w.dtype)), dtype=torch.uint8, device=dev)
+    nseg = N // w.segment
+    calls = []
+    for i in range(nseg):
+        sl = slice(i * w.segment, (i + 1) * w.segment)
+        calls.append(la.prepare_memory_fwd(q[:, :, sl], k[:, :, sl], v[:, :, sl], out[:, :, sl], eps=w.eps,
+                                           z_in=zs[i & 1] if i else None, s_in=ss[i & 1] if i else None,
+                                           z_out=zs[(i + 1) & 1], s_out=ss[(i + 1) & 1], workspace=ws))
+
+    def step(_):
+        for c in calls:
+            c()
+
+    steps = max(3, args.steps // 4)
+    total_ms = time_steps(step, steps, max(1, args.warmup // 2), 1)
+    ms = total_ms / steps
+    seg_w = inp.Workload("segment", "memory", w.dtype, w.B, w.H, w.segment, w.d, 0, 1.0)
+    b_call = alg_bytes_causal(seg_w, with_state_io=True)
+    return {"workload": w.name, "value": round(w.head_tokens / (ms * 1e-3), 1), "unit": "head-tokens/s",
+            "ms_per_step": round(ms, 4), "calls_per_step": nseg,
+            "roofline": roofline(b_call, ms / nseg, measured_traffic(w.name))}
+
+
 def cpu_baseline(w, qkv, seconds):
     """The fp64 oracle, as it is, on the host cores: whole steps of the same
     workload repeated until `seconds` of wall time have passed (at least 2)."""
@@ -329,6 +362,8 @@ def main():
         line["workloads"]["decode"] = bench_decode(args, torch, la, inp)
         log("non-causal workload ...")
         line["workloads"]["noncausal"] = bench_noncausal(args, torch, la, inp)
+        log("memory workload ...")
+        line["workloads"]["memory"] = bench_memory(args, torch, la, inp)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline(w, qkv, args.cpu_seconds)

@@ -2504,14 +2504,14 @@ unsigned long long next_epoch()
     return z ? z : 16;
 }
 
-Plan plan_noncausal(int B, int H, int N, int d, la_dtype dt)
+Plan plan_noncausal(int B, int H, int N, int d, la_dtype dt, int target = 1024)
 {
     Plan pl;
     pl.C = pick_chunk(dt == LA_F32, d, 0);
     pl.DV = cols_per_wg(d);
     pl.P = d / pl.DV;
     const int64_t BH = (int64_t)B * H;
-    pl.G = pick_groups(BH * pl.P, N, pl.C, 1024);
+    pl.G = pick_groups(BH * pl.P, N, pl.C, target);
     set_groups(pl, N);
     pl.NS = pl.G;
     pl.slot_floats = (size_t)pl.DV * d + d;
@@ -2772,10 +2772,22 @@ la_status la_noncausal_fwd(const void *q, la_strides sq, const void *k, la_strid
     return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }
 
+// Memory calls run one segment at a time (a few thousand tokens per head):
+// fewer, longer token groups than the non-causal plan, so that a group's
+// published state does not outweigh its inputs, and shorter apply
+// workgroups, so that the readout still covers the chip.
+#ifndef LA_MEM_GROUP_TARGET
+#define LA_MEM_GROUP_TARGET 256
+#endif
+#ifndef LA_MEM_APPLY_CHUNKS
+#define LA_MEM_APPLY_CHUNKS 2
+#endif
+Plan plan_memory(int B, int H, int N, int d, la_dtype dt) { return plan_noncausal(B, H, N, d, dt, LA_MEM_GROUP_TARGET); }
+
 size_t la_memory_workspace(int B, int H, int N, int d, la_dtype dt)
 {
     if (check_common(B, H, N, d, dt, 0.f) != LA_OK) return 0;
-    return plan_noncausal(B, H, N, d, dt).total;
+    return plan_memory(B, H, N, d, dt).total;
 }
 
 // The non-causal kernels with the carried-in memory as the state that the
@@ -2809,7 +2821,7 @@ la_status la_memory_fwd(const void *q, la_strides sq, const void *k, la_strides 
     if (s_out && s_in && s_out != (float *)s_in && overlaps(s_out, sb, s_in, sb)) return LA_ERR_ALIAS;
     if (overlaps(z_out, zb, s_in, sb) || overlaps(s_out, sb, z_in, zb) || overlaps(z_out, zb, s_out, sb))
         return LA_ERR_ALIAS;
-    Plan pl = plan_noncausal(B, H, N, d, dt);
+    Plan pl = plan_memory(B, H, N, d, dt);
     if (ws_bytes < pl.total || (pl.total > 0 && !workspace)) return LA_ERR_WORKSPACE;
     if (BH == 0) return LA_OK;
     hipStream_t stream = (hipStream_t)hip_stream;
@@ -2832,7 +2844,7 @@ la_status la_memory_fwd(const void *q, la_strides sq, const void *k, la_strides 
     else dispatch(f32, d, pl.C, 0, a, (int)(BH * pl.P * pl.G), stream);
     launch_slots(d, a, BH, pl.P, pl.G, 3, stream);
     if (want_out) {
-        const int la = pl.C * 4;
+        const int la = pl.C * LA_MEM_APPLY_CHUNKS;
         a.L = la;
         a.G = (N + la - 1) / la;
         if (cs) hipLaunchKernelGGL((k_cs_apply<64>), dim3((unsigned)(BH * pl.P * a.G)), dim3(NTHR), 0, stream, a);

@@ -26,7 +26,7 @@ import torch
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "causal" | "segmented" | "decode" | "noncausal"
+    kind: str            # "causal" | "segmented" | "decode" | "noncausal" | "memory"
     dtype: torch.dtype   # input dtype of q, k, v
     B: int
     H: int
@@ -63,6 +63,10 @@ WORKLOADS = {
                  64, 32, 1024, 128, seed=1004, scale=_isqrt(128), prefix=1024),
         Workload("noncausal_bf16_b8h16n16384d64", "noncausal", torch.bfloat16,
                  8, 16, 16384, 64, seed=1005, scale=_isqrt(64)),
+        # compressive memory (retrieval, then update) over the segment stream
+        # of the segment-carried workload's shape
+        Workload("memory_bf16_b1h16n65536d128_seg2048", "memory", torch.bfloat16,
+                 1, 16, 65536, 128, seed=1006, scale=_isqrt(128), segment=2048),
     ]
 }
 SMALL = "causal_f32_b1h1n256d32"
@@ -70,6 +74,7 @@ HEADLINE = "causal_bf16_b4h8n4096d64"
 SEGMENTED = "segmented_bf16_b1h16n65536d128_seg2048"
 DECODE = "decode_bf16_b64h32d128_prefix1024_steps1024"
 NONCAUSAL = "noncausal_bf16_b8h16n16384d64"
+MEMORY = "memory_bf16_b1h16n65536d128_seg2048"
 
 
 def draw(shape, gen: torch.Generator, dtype: torch.dtype, scale: float,
@@ -96,7 +101,7 @@ def qkv(shape, seed: int, dtype: torch.dtype, scale: float, device: str = "cpu")
 def workload_inputs(w: Workload, device: str = "cpu"):
     """Inputs of a workload.
 
-    causal / segmented / noncausal: (q, k, v) each [B, H, N, d].
+    causal / segmented / noncausal / memory: (q, k, v) each [B, H, N, d].
     decode: (prefix (q, k, v) each [B, H, P, d], steps (q, k, v) each [T, B, H, d]).
     """
     g = make_generator(w.seed, device)
