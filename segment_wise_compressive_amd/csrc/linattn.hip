@@ -2117,7 +2117,7 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
 // of G takes the 64-token chunks grp, grp + G, grp + 2G, ... (the G
 // workgroups of a head read neighbouring chunks at any one time).
 template <int D>
-__global__ void __launch_bounds__(NTHR, 4) k_cs_state(const Args a)
+__global__ void __launch_bounds__(NTHR, D <= 64 ? 4 : 2) k_cs_state(const Args a)
 {
     typedef CSGeo<D> T;
     constexpr int C = T::C, DV = T::DV, JT = T::JT, VPR = T::VPR, NK = T::NK, NV = T::NV;
@@ -2223,7 +2223,7 @@ __global__ void __launch_bounds__(NTHR, 4) k_cs_state(const Args a)
 // S . psi(q_t), with Z and S as bf16 hi + lo operands.  Every wave computes
 // the normalisers of all queries (no exchange).
 template <int D>
-__global__ void __launch_bounds__(NTHR, 4) k_cs_apply(const Args a)
+__global__ void __launch_bounds__(NTHR, D <= 64 ? 4 : 2) k_cs_apply(const Args a)
 {
     typedef CSGeo<D> T;
     constexpr int C = T::C, DV = T::DV, JT = T::JT, KS = T::KS, VPR = T::VPR, NK = T::NK;
@@ -2571,6 +2571,18 @@ void launch_slots(int d, const Args &a, int64_t BH, int P, int nslots, int mode,
     else hipLaunchKernelGGL((k_slots<128, 64>), grid, dim3(256), 0, st, a, nslots, mode);
 }
 
+// column-split non-causal kernels (bf16, d = 64 or 128)
+void launch_cs_state(int d, const Args &a, unsigned nwg, hipStream_t st)
+{
+    if (d == 64) hipLaunchKernelGGL((k_cs_state<64>), dim3(nwg), dim3(NTHR), 0, st, a);
+    else hipLaunchKernelGGL((k_cs_state<128>), dim3(nwg), dim3(NTHR), 0, st, a);
+}
+void launch_cs_apply(int d, const Args &a, unsigned nwg, hipStream_t st)
+{
+    if (d == 64) hipLaunchKernelGGL((k_cs_apply<64>), dim3(nwg), dim3(NTHR), 0, st, a);
+    else hipLaunchKernelGGL((k_cs_apply<128>), dim3(nwg), dim3(NTHR), 0, st, a);
+}
+
 la_status check_common(int B, int H, int N, int d, la_dtype dt, float eps)
 {
     if (B < 0 || H < 0 || N < 0) return LA_ERR_SHAPE;
@@ -2760,14 +2772,14 @@ la_status la_noncausal_fwd(const void *q, la_strides sq, const void *k, la_strid
     // 1) partial states of the token groups, 2) their sum per head in group
     // order, 3) every query against the global state
     a.G = pl.G; a.L = pl.L; a.slot0 = 0;
-    const bool cs = LA_COLUMN_SPLIT && !f32 && d == 64 && pl.C == 64;
-    if (cs) hipLaunchKernelGGL((k_cs_state<64>), dim3((unsigned)(BH * pl.P * pl.G)), dim3(NTHR), 0, stream, a);
+    const bool cs = LA_COLUMN_SPLIT && !f32 && (d == 64 || d == 128) && pl.C == 64;
+    if (cs) launch_cs_state(d, a, (unsigned)(BH * pl.P * pl.G), stream);
     else dispatch(f32, d, pl.C, 0, a, (int)(BH * pl.P * pl.G), stream);
     launch_slots(d, a, BH, pl.P, pl.G, 2, stream);
     const int la = pl.C * 4;
     a.L = la;
     a.G = (N + la - 1) / la;
-    if (cs) hipLaunchKernelGGL((k_cs_apply<64>), dim3((unsigned)(BH * pl.P * a.G)), dim3(NTHR), 0, stream, a);
+    if (cs) launch_cs_apply(d, a, (unsigned)(BH * pl.P * a.G), stream);
     else dispatch(f32, d, pl.C, 2, a, (int)(BH * pl.P * a.G), stream);
     return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }
@@ -2839,15 +2851,15 @@ la_status la_memory_fwd(const void *q, la_strides sq, const void *k, la_strides 
     a.fin = want_out ? (float *)(ws + pl.fin_off) : nullptr;
     const bool f32 = dt == LA_F32;
     a.G = pl.G; a.L = pl.L; a.slot0 = 0;
-    const bool cs = LA_COLUMN_SPLIT && !f32 && d == 64 && pl.C == 64;
-    if (cs) hipLaunchKernelGGL((k_cs_state<64>), dim3((unsigned)(BH * pl.P * pl.G)), dim3(NTHR), 0, stream, a);
+    const bool cs = LA_COLUMN_SPLIT && !f32 && (d == 64 || d == 128) && pl.C == 64;
+    if (cs) launch_cs_state(d, a, (unsigned)(BH * pl.P * pl.G), stream);
     else dispatch(f32, d, pl.C, 0, a, (int)(BH * pl.P * pl.G), stream);
     launch_slots(d, a, BH, pl.P, pl.G, 3, stream);
     if (want_out) {
         const int la = pl.C * LA_MEM_APPLY_CHUNKS;
         a.L = la;
         a.G = (N + la - 1) / la;
-        if (cs) hipLaunchKernelGGL((k_cs_apply<64>), dim3((unsigned)(BH * pl.P * a.G)), dim3(NTHR), 0, stream, a);
+        if (cs) launch_cs_apply(d, a, (unsigned)(BH * pl.P * a.G), stream);
         else dispatch(f32, d, pl.C, 2, a, (int)(BH * pl.P * a.G), stream);
     }
     return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
