@@ -55,6 +55,8 @@ def _load():
         lib.oracle_noncausal.restype = None
         lib.oracle_memory.argtypes = [L, L, L, D, fp, fp, fp, dp, dp, dp, dp, dp]
         lib.oracle_memory.restype = None
+        lib.oracle_causal_unnormalized.argtypes = [L, L, L, fp, fp, fp, dp, dp]
+        lib.oracle_causal_unnormalized.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -155,3 +157,16 @@ def memory(q, k, v, eps: float, z_in=None, s_in=None, want_out: bool = True):
                           _dptr(zi), _dptr(si), _dptr(out), _dptr(zo), _dptr(so))
     return (None if out is None else out.reshape(*lead, N, d),
             zo.reshape(*lead, d, d), so.reshape(*lead, d))
+
+
+def causal_unnormalized(q, k, v, z_in=None):
+    """Causal linear attention without the normaliser: out_t = phi(q_t)^T Z_t
+    with Z_t = z_in + sum_{i<=t} phi(k_i) v_i^T.  Returns out [..., N, d] in
+    float64 (the carried state is the same as oracle.causal's)."""
+    qa, ka, va = _f32(q), _f32(k), _f32(v)
+    lead, (N, d) = qa.shape[:-2], qa.shape[-2:]
+    BH = int(np.prod(lead)) if lead else 1
+    zi = None if z_in is None else _f64(z_in).reshape(BH, d, d)
+    out = np.empty((BH, N, d), np.float64)
+    _load().oracle_causal_unnormalized(BH, N, d, _fptr(qa), _fptr(ka), _fptr(va), _dptr(zi), _dptr(out))
+    return out.reshape(*lead, N, d)

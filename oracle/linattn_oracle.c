@@ -241,3 +241,41 @@ void oracle_memory(long BH, long N, long d, double eps,
         free(mem); free(norm); free(fq);
     }
 }
+
+/*
+ * Unnormalised causal linear attention: the chunk formulas of "Attention
+ * Kernel Mask" (section "How to accelerate causal linear attention", the
+ * chunk-sequential and materialised modes) as printed, with no denominator.
+ * Per head, with phi on q and k:
+ *   W = W_in + sum_{i<=t} phi(k_i) v_i^T,   out_t = phi(q_t)^T W.
+ * w_in (may be NULL = zeros) is the carried-in context.  The key sums of the
+ * normalised form do not enter; the carried state is the same Z.
+ */
+void oracle_causal_unnormalized(long BH, long N, long d,
+                                const float *q, const float *k, const float *v,
+                                const double *w_in, double *out)
+{
+    long h;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (h = 0; h < BH; ++h) {
+        double *W = (double *)calloc((size_t)(d * d), sizeof(double));
+        double *phik = (double *)malloc((size_t)d * sizeof(double));
+        double *phiq = (double *)malloc((size_t)d * sizeof(double));
+        long t, a, b;
+        if (w_in) memcpy(W, w_in + h * d * d, (size_t)(d * d) * sizeof(double));
+        for (t = 0; t < N; ++t) {
+            const float *krow = k + (h * N + t) * d, *vrow = v + (h * N + t) * d, *qrow = q + (h * N + t) * d;
+            double *orow = out + (h * N + t) * d;
+            for (a = 0; a < d; ++a) phik[a] = phi((double)krow[a]);
+            for (a = 0; a < d; ++a)
+                for (b = 0; b < d; ++b) W[a * d + b] += phik[a] * (double)vrow[b];
+            for (a = 0; a < d; ++a) phiq[a] = phi((double)qrow[a]);
+            for (b = 0; b < d; ++b) {
+                double acc = 0.0;
+                for (a = 0; a < d; ++a) acc += phiq[a] * W[a * d + b];
+                orow[b] = acc;
+            }
+        }
+        free(W); free(phik); free(phiq);
+    }
+}

@@ -39,6 +39,10 @@ MUTANTS = {
                                       "for (i = 0; i < d; ++i) fq[i] = (double)qrow[i] + 1.0;"),
     "memory_in_ignored": ("if (z_in) memcpy(mem,", "if (0) memcpy(mem,"),
     "memory_read_transposed": ("retrieved += fq[i] * mem[i * d + c];", "retrieved += fq[i] * mem[c * d + i];"),
+    "unnormalized_update_without_phi": ("for (a = 0; a < d; ++a) phik[a] = phi((double)krow[a]);",
+                                        "for (a = 0; a < d; ++a) phik[a] = (double)krow[a];"),
+    "unnormalized_context_in_ignored": ("if (w_in) memcpy(W,", "if (0) memcpy(W,"),
+    "unnormalized_read_transposed": ("acc += phiq[a] * W[a * d + b];", "acc += phiq[a] * W[b * d + a];"),
 }
 
 

@@ -358,3 +358,45 @@ def test_memory_zero_length_passes_state_through():
     assert out.shape == (2, 0, d)
     np.testing.assert_array_equal(z, zi)
     np.testing.assert_array_equal(s, si)
+
+
+# ---------------------------------------------------------------- unnormalised form
+def test_unnormalized_matches_masked_numerator():
+    N, d = 37, 6
+    q, k, v = (rnd((2, N, d), 190 + i, 0.8) for i in range(3))
+    z0 = rnd((2, d, d), 193).astype(np.float64)
+    out = oracle.causal_unnormalized(q, k, v, z0)
+    for h in range(2):
+        g, f = phi(q[h]), phi(k[h])
+        W = (g @ f.T) * np.tril(np.ones((N, N)))
+        ref = W @ v[h].astype(np.float64) + g @ z0[h]
+        assert rowwise_rel_err(out[h], ref) < TIGHT
+
+
+def test_unnormalized_is_normalized_times_denominator():
+    N, d = 41, 5
+    q, k, v = (rnd((3, N, d), 200 + i, 0.6) for i in range(3))
+    eps = 1e-3
+    norm, _, _ = oracle.causal(q, k, v, eps)
+    un = oracle.causal_unnormalized(q, k, v)
+    den = np.einsum("htj,htj->ht", phi(q), np.cumsum(phi(k), axis=1)) + eps
+    assert rowwise_rel_err(un, norm * den[..., None]) < 1e-11
+
+
+def test_unnormalized_constant_v_and_zero_q_k():
+    N, d = 9, 4
+    z = np.zeros((1, N, d), np.float32)
+    v = np.full((1, N, d), 0.5, np.float32)
+    out = oracle.causal_unnormalized(z, z, v)
+    # phi(0) = 1: out_t = d * (t + 1) * 0.5 in every column
+    ref = (d * 0.5 * np.arange(1, N + 1))[:, None] * np.ones((1, d))
+    np.testing.assert_allclose(out[0], ref, rtol=1e-15)
+
+
+def test_unnormalized_segment_carry():
+    N, d = 50, 6
+    q, k, v = (rnd((2, N, d), 210 + i, 0.7) for i in range(3))
+    full = oracle.causal_unnormalized(q, k, v)
+    _, z, _ = oracle.causal(q[:, :17], k[:, :17], v[:, :17], 1e-6)
+    tail = oracle.causal_unnormalized(q[:, 17:], k[:, 17:], v[:, 17:], z)
+    assert rowwise_rel_err(tail, full[:, 17:]) < TIGHT
