@@ -115,6 +115,23 @@ la_status la_causal_fwd(const void *q, la_strides sq, const void *k, la_strides 
                         void *workspace, size_t ws_bytes, void *hip_stream);
 
 /*
+ * The unnormalised causal form: the chunk formulas of "Attention Kernel Mask"
+ * (section "How to accelerate causal linear attention", chunk-sequential and
+ * materialised modes) as printed, with no denominator:
+ *   out_t = phi(q_t)^T Z_t,  Z_t = Z_in + sum_{i<=t} phi(k_i) v_i^T.
+ * Arguments, workspace, state handling (S is carried and written exactly as
+ * by la_causal_fwd), aliasing and errors are those of la_causal_fwd; eps is
+ * validated but does not enter the outputs.
+ */
+la_status la_causal_fwd_unnormalized(const void *q, la_strides sq, const void *k, la_strides sk,
+                                     const void *v, la_strides sv, la_dtype dt,
+                                     float *out, la_strides so,
+                                     int B, int H, int N, int d, int chunk, float eps,
+                                     const float *z_in, const float *s_in,
+                                     float *z_out, float *s_out,
+                                     void *workspace, size_t ws_bytes, void *hip_stream);
+
+/*
  * One generation step per head ("Attention Kernel Mask", mode 2: recurrent
  * generation with a fixed-size state and no KV cache):
  *   Z += phi(k) v^T;  S += phi(k);  out = phi(q)^T Z / (phi(q) . S + eps).

@@ -23,7 +23,7 @@ __all__ = [
     "LinAttnError", "LA_F32", "LA_BF16", "LA_WS_INPLACE_STATE",
     "library_path", "load_library",
     "la_status_str", "la_version",
-    "la_causal_fwd_workspace", "la_causal_fwd",
+    "la_causal_fwd_workspace", "la_causal_fwd", "la_causal_fwd_unnormalized",
     "la_decode_step",
     "la_noncausal_workspace", "la_noncausal_fwd",
     "la_memory_workspace", "la_memory_fwd",
@@ -72,6 +72,8 @@ def load_library():
     lib.la_causal_fwd.argtypes = [vp, S, vp, S, vp, S, i32, vp, S, i32, i32, i32, i32, i32, f32,
                                   vp, vp, vp, vp, vp, sz, vp]
     lib.la_causal_fwd.restype = i32
+    lib.la_causal_fwd_unnormalized.argtypes = lib.la_causal_fwd.argtypes
+    lib.la_causal_fwd_unnormalized.restype = i32
     lib.la_decode_step.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, f32, vp]
     lib.la_decode_step.restype = i32
     lib.la_noncausal_workspace.argtypes = [i32, i32, i32, i32, i32]
@@ -177,8 +179,10 @@ def _opt_stream(stream, device):
 
 def prepare_causal_fwd(q, k, v, out=None, *, chunk: int = 0, eps: float = 1e-6,
                        z_in=None, s_in=None, z_out=None, s_out=None,
-                       workspace: Optional[torch.Tensor] = None, stream=None) -> Prepared:
+                       workspace: Optional[torch.Tensor] = None, stream=None,
+                       normalize: bool = True) -> Prepared:
     """Check and marshal a la_causal_fwd call (nothing runs until it is called).
+    normalize=False marshals la_causal_fwd_unnormalized instead (same arguments).
 
     q, k, v: [B, H, N, d] bf16 or fp32 CUDA tensors (any strides with unit d stride).
     out: float32 [B, H, N, d] or None (state only).  States: float32 contiguous
@@ -206,8 +210,10 @@ def prepare_causal_fwd(q, k, v, out=None, *, chunk: int = 0, eps: float = 1e-6,
             _ptr(out), so, B, H, N, d, int(chunk), ctypes.c_float(eps),
             _ptr(z_in), _ptr(s_in), _ptr(z_out), _ptr(s_out), _ptr(workspace), ctypes.c_size_t(have),
             _opt_stream(stream, q.device)]
-    return Prepared(load_library().la_causal_fwd, args, q.device, "la_causal_fwd",
-                    (q, k, v, out, z_in, s_in, z_out, s_out, workspace))
+    lib = load_library()
+    fn, name = (lib.la_causal_fwd, "la_causal_fwd") if normalize else \
+        (lib.la_causal_fwd_unnormalized, "la_causal_fwd_unnormalized")
+    return Prepared(fn, args, q.device, name, (q, k, v, out, z_in, s_in, z_out, s_out, workspace))
 
 
 def la_causal_fwd(q, k, v, out=None, *, chunk: int = 0, eps: float = 1e-6,
@@ -217,6 +223,15 @@ def la_causal_fwd(q, k, v, out=None, *, chunk: int = 0, eps: float = 1e-6,
     as for prepare_causal_fwd."""
     prepare_causal_fwd(q, k, v, out, chunk=chunk, eps=eps, z_in=z_in, s_in=s_in, z_out=z_out, s_out=s_out,
                        workspace=workspace, stream=stream)()
+
+
+def la_causal_fwd_unnormalized(q, k, v, out=None, *, chunk: int = 0, eps: float = 1e-6,
+                               z_in=None, s_in=None, z_out=None, s_out=None,
+                               workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Causal linear attention without the normaliser (la_causal_fwd_unnormalized
+    in linattn.h); arguments as for prepare_causal_fwd."""
+    prepare_causal_fwd(q, k, v, out, chunk=chunk, eps=eps, z_in=z_in, s_in=s_in, z_out=z_out, s_out=s_out,
+                       workspace=workspace, stream=stream, normalize=False)()
 
 
 def prepare_decode_step(q, k, v, z, s, out, *, eps: float = 1e-6, stream=None) -> Prepared:

@@ -153,6 +153,7 @@ struct Args {
     unsigned long long *flags;
     unsigned long long epoch;
     int wait_s;   // s_out is s_in and shared by P > 1 column blocks
+    int unnorm;   // causal outputs without the normaliser (numerators only)
 };
 
 // A slot holds one (head, column block) state in the layout of the state
@@ -1186,7 +1187,7 @@ __global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F
         const int tq = 16 * tb + r;
         // normaliser of query r: row 0 of the extra tile, held by lane r
         const float den = __shfl(o[CT][0], r) + a.eps;
-        const float inv = __builtin_amdgcn_rcpf(den);   // within 1 ulp
+        const float inv = a.unnorm ? 1.f : __builtin_amdgcn_rcpf(den);   // within 1 ulp
         const rsrc_t orr = ov.at(t0);
         const uint32_t obase = tq < nval ? (uint32_t)(tq * ov.rs + 16 * g) : OFF_NONE;
 #pragma unroll
@@ -1521,7 +1522,7 @@ __device__ __forceinline__ u32x4 cs_psi8(u32x4 x)
     return y;
 }
 
-template <int D, int CPG>
+template <int D, int CPG, bool UNNORM>
 __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
 {
     typedef CSGeo<D> T;
@@ -1850,7 +1851,7 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int t = 16 * m + r;
-            const float inv = __builtin_amdgcn_rcpf(den_s[c * C + t] + a.eps);
+            const float inv = UNNORM ? 1.f : __builtin_amdgcn_rcpf(den_s[c * C + t] + a.eps);
             bstore16nt(orr, t < nv ? (uint32_t)(t * ov.rs + (16 * w + 4 * g) * 4) : OFF_NONE, O[c][m] * inv);
         }
     };
@@ -2653,13 +2654,16 @@ size_t la_causal_fwd_workspace(int B, int H, int N, int d, la_dtype dt, int chun
     return a.total > b.total ? a.total : b.total;
 }
 
-la_status la_causal_fwd(const void *q, la_strides sq, const void *k, la_strides sk,
-                        const void *v, la_strides sv, la_dtype dt,
-                        float *out, la_strides so,
-                        int B, int H, int N, int d, int chunk, float eps,
-                        const float *z_in, const float *s_in,
-                        float *z_out, float *s_out,
-                        void *workspace, size_t ws_bytes, void *hip_stream)
+}  // extern "C"
+
+namespace {
+la_status causal_impl(const void *q, la_strides sq, const void *k, la_strides sk,
+                      const void *v, la_strides sv, la_dtype dt,
+                      float *out, la_strides so,
+                      int B, int H, int N, int d, int chunk, float eps,
+                      const float *z_in, const float *s_in,
+                      float *z_out, float *s_out,
+                      void *workspace, size_t ws_bytes, void *hip_stream, int unnorm)
 {
     la_status st = check_common(B, H, N, d, dt, eps);
     if (st != LA_OK) return st;
@@ -2690,6 +2694,7 @@ la_status la_causal_fwd(const void *q, la_strides sq, const void *k, la_strides 
     (void)hipGetLastError();
     Args a = make_args(q, sq, k, sk, v, sv, out, so, B, H, N, eps);
     a.z_in = z_in; a.s_in = s_in; a.z_out = z_out; a.s_out = s_out;
+    a.unnorm = unnorm;
     a.P = pl.P; a.L = pl.L; a.NS = pl.NS; a.G = pl.G;
     a.part = (float *)workspace;
     const bool f32 = dt == LA_F32;
@@ -2704,13 +2709,43 @@ la_status la_causal_fwd(const void *q, la_strides sq, const void *k, la_strides 
     a.wait_s = (s_out && s_out == s_in && pl.P > 1) ? 1 : 0;
     const bool resident = pl.C == 64 && pl.L <= res_cpg(f32, d) * pl.C;
     const int nwg = (int)(BH * pl.P * pl.G);
-    if (LA_COLUMN_SPLIT && want_out && resident && !f32 && d == 64)
-        hipLaunchKernelGGL((k_cs_fwd<64, res_cpg(false, 64)>), dim3(nwg), dim3(NTHR), 0, stream, a);
-    else if (LA_COLUMN_SPLIT && want_out && resident && !f32 && d == 128)
-        hipLaunchKernelGGL((k_cs_fwd<128, res_cpg(false, 128)>), dim3(nwg), dim3(NTHR), 0, stream, a);
+#define LA_CS(DD, UN) hipLaunchKernelGGL((k_cs_fwd<DD, res_cpg(false, DD), UN>), dim3(nwg), dim3(NTHR), 0, stream, a)
+    if (LA_COLUMN_SPLIT && want_out && resident && !f32 && d == 64) {
+        if (unnorm) LA_CS(64, true); else LA_CS(64, false);
+    } else if (LA_COLUMN_SPLIT && want_out && resident && !f32 && d == 128) {
+        if (unnorm) LA_CS(128, true); else LA_CS(128, false);
+    }
+#undef LA_CS
     else
         dispatch(f32, d, pl.C, want_out ? (resident ? 4 : 1) : 3, a, nwg, stream);
     return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
+}
+}  // namespace
+
+extern "C" {
+
+la_status la_causal_fwd(const void *q, la_strides sq, const void *k, la_strides sk,
+                        const void *v, la_strides sv, la_dtype dt,
+                        float *out, la_strides so,
+                        int B, int H, int N, int d, int chunk, float eps,
+                        const float *z_in, const float *s_in,
+                        float *z_out, float *s_out,
+                        void *workspace, size_t ws_bytes, void *hip_stream)
+{
+    return causal_impl(q, sq, k, sk, v, sv, dt, out, so, B, H, N, d, chunk, eps, z_in, s_in, z_out, s_out,
+                       workspace, ws_bytes, hip_stream, 0);
+}
+
+la_status la_causal_fwd_unnormalized(const void *q, la_strides sq, const void *k, la_strides sk,
+                                     const void *v, la_strides sv, la_dtype dt,
+                                     float *out, la_strides so,
+                                     int B, int H, int N, int d, int chunk, float eps,
+                                     const float *z_in, const float *s_in,
+                                     float *z_out, float *s_out,
+                                     void *workspace, size_t ws_bytes, void *hip_stream)
+{
+    return causal_impl(q, sq, k, sk, v, sv, dt, out, so, B, H, N, d, chunk, eps, z_in, s_in, z_out, s_out,
+                       workspace, ws_bytes, hip_stream, 1);
 }
 
 la_status la_decode_step(const void *q, const void *k, const void *v, la_dtype dt,

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(lib):
     names = la.declared_entry_points()
     assert set(names) == {"la_status_str", "la_version", "la_causal_fwd_workspace", "la_causal_fwd",
                           "la_decode_step", "la_noncausal_workspace", "la_noncausal_fwd",
-                          "la_memory_workspace", "la_memory_fwd"}
+                          "la_memory_workspace", "la_memory_fwd", "la_causal_fwd_unnormalized"}
     raw = ctypes.CDLL(la.library_path())
     for n in names:
         assert hasattr(raw, n), n
@@ -119,6 +119,23 @@ def test_noncausal_validation(lib):
     assert lib.la_noncausal_fwd(*bad) == 7
     bad = list(base); bad[2] = vp(FAKE + 0x100002)
     assert lib.la_noncausal_fwd(*bad) == 4
+
+
+@no_device
+def test_unnormalized_validation(lib):
+    # the unnormalised entry point shares la_causal_fwd's checks
+    st = la_strides(2 * 128 * 64, 128 * 64, 64)
+    vp = ctypes.c_void_p
+    base = [vp(FAKE), st, vp(FAKE + 0x100000), st, vp(FAKE + 0x200000), st, 1, vp(FAKE + 0x300000), st,
+            1, 2, 128, 64, 0, 1e-6, None, None, None, None, vp(FAKE + 0x400000), 1 << 30, None]
+    bad = list(base); bad[12] = 48
+    assert lib.la_causal_fwd_unnormalized(*bad) == 5
+    bad = list(base); bad[13] = 24
+    assert lib.la_causal_fwd_unnormalized(*bad) == 5
+    bad = list(base); bad[7] = None
+    assert lib.la_causal_fwd_unnormalized(*bad) == 1
+    bad = list(base); bad[20] = 16
+    assert lib.la_causal_fwd_unnormalized(*bad) == 7
 
 
 def _memory(lib, **kw):
