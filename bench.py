@@ -10,7 +10,8 @@ Prints ONE JSON line: value = B*H*N head-tokens per second over the timed
 steps; `roofline` = algorithmic bytes of one call / its average duration
 (HIP events on the launch stream) against 8 TB/s; `cpu_baseline` = the fp64
 oracle on the host cores; `workloads` = the segment-carried, decode,
-non-causal and compressive-memory workloads timed the same way.
+non-causal and compressive-memory workloads and the unnormalised causal form
+of the headline workload, timed the same way.
 """
 import argparse
 import json
@@ -143,6 +144,31 @@ def bench_headline(args, torch, la, inp):
     total_ms = time_steps(step, args.steps, args.warmup, n_rot)
     spread = step_spread(step, args.steps, n_rot)
     return w, total_ms, total_ms / args.steps, (q, k, v), spread
+
+
+def bench_unnormalized(args, torch, la, inp):
+    """The headline workload through la_causal_fwd_unnormalized (numerators
+    only), timed the same way with the same rotated input sets."""
+    w = inp.WORKLOADS[inp.HEADLINE]
+    dev = torch.device("cuda:0")
+    q, k, v = inp.workload_inputs(w)
+    n_rot = args.rotate
+    sets = [(q.to(dev), k.to(dev), v.to(dev), torch.empty(w.B, w.H, w.N, w.d, dtype=torch.float32, device=dev))
+            for _ in range(n_rot)]
+    ws = torch.empty(max(1, la.la_causal_fwd_workspace(w.B, w.H, w.N, w.d, w.dtype, w.chunk)),
+                     dtype=torch.uint8, device=dev)
+    calls = [la.prepare_causal_fwd(a[0], a[1], a[2], a[3], chunk=w.chunk, eps=w.eps, workspace=ws, normalize=False)
+             for a in sets]
+
+    def step(i):
+        calls[i]()
+
+    steps = max(3, args.steps // 2)
+    total_ms = time_steps(step, steps, max(1, args.warmup // 2), n_rot)
+    per_call = total_ms / steps
+    return {"workload": w.name + "_unnormalized", "value": round(w.head_tokens / (per_call * 1e-3), 1),
+            "unit": "head-tokens/s", "ms_per_step": round(per_call, 5),
+            "roofline": roofline(alg_bytes_causal(w), per_call, None)}
 
 
 def bench_segmented(args, torch, la, inp):
@@ -364,6 +390,8 @@ def main():
         line["workloads"]["noncausal"] = bench_noncausal(args, torch, la, inp)
         log("memory workload ...")
         line["workloads"]["memory"] = bench_memory(args, torch, la, inp)
+        log("unnormalised causal workload ...")
+        line["workloads"]["unnormalized"] = bench_unnormalized(args, torch, la, inp)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline(w, qkv, args.cpu_seconds)
