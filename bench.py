@@ -163,9 +163,8 @@ def bench_unnormalized(args, torch, la, inp):
     def step(i):
         calls[i]()
 
-    steps = max(3, args.steps // 2)
-    total_ms = time_steps(step, steps, max(1, args.warmup // 2), n_rot)
-    per_call = total_ms / steps
+    total_ms = time_steps(step, args.steps, args.warmup, n_rot)
+    per_call = total_ms / args.steps
     return {"workload": w.name + "_unnormalized", "value": round(w.head_tokens / (per_call * 1e-3), 1),
             "unit": "head-tokens/s", "ms_per_step": round(per_call, 5),
             "roofline": roofline(alg_bytes_causal(w), per_call, None)}
