@@ -2318,6 +2318,202 @@ __global__ void __launch_bounds__(NTHR, D <= 64 ? 4 : 2) k_cs_apply(const Args a
     }
 }
 
+// k_cs_memory: one token share of a compressive-memory call in one launch.
+// Share grp of G takes the 64-token chunks grp, grp + G, ...  First its
+// partial state, Z = sum psi(k) v^T + 1 (sum v)^T and S = sum psi(k) + tokens
+// (as k_cs_state; each wave forms only its S tiles w, w + 4, ...), goes to its
+// slot; then every query of the share reads the carried-in memory,
+// out_t = phi(q_t)^T Z_in / (phi(q_t) . S_in + eps) (as k_cs_apply, with Z_in
+// and S_in read from the state tensors).  The two phases share the LDS, and
+// their registers are never live together.  k_slots then adds the slots to
+// the memory.
+template <int D>
+__global__ void __launch_bounds__(NTHR, 2) k_cs_memory(const Args a)
+{
+    typedef CSGeo<D> T;
+    constexpr int C = T::C, DV = T::DV, JT = T::JT, KS = T::KS, VPR = T::VPR, NK = T::NK, NV = T::NV;
+    constexpr int SL = Slot<D, DV>::SIZE;
+    constexpr int SPW = JT / NWAVE;
+    static_assert(JT % NWAVE == 0, "S tiles split evenly over the waves");
+    // phase 1: psi(K) [2][C][D], V [2][C][DV]; phase 2: psi(Q) [2][C][D]
+    __shared__ __attribute__((aligned(16))) bf16 sm[2 * C * D + 2 * C * DV];
+    const int tid = threadIdx.x, lane = tid % WAVE, r = lane % 16, g = lane / 16;
+    const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    const int p = wg % a.P, rest = wg / a.P, grp = rest % a.G, bh = rest / a.G;
+    const int b = bh / a.H, h = bh % a.H;
+    const int hp = bh * a.P + p;
+    const int nall = (a.N + C - 1) / C;
+    const int nch = grp < nall ? (nall - grp + a.G - 1) / a.G : 0;
+    auto t0_of = [&](int ch) { return (grp + ch * a.G) * C; };
+    const RowView qv{(const char *)a.q + (b * a.sqb + h * a.sqh) * 2, a.sqn * 2, (a.N - 1) * a.sqn * 2 + D * 2};
+    const RowView kv{(const char *)a.k + (b * a.skb + h * a.skh) * 2, a.skn * 2, (a.N - 1) * a.skn * 2 + D * 2};
+    const RowView vv{(const char *)a.v + (b * a.svb + h * a.svh + p * DV) * 2, a.svn * 2,
+                     (a.N - 1) * a.svn * 2 + DV * 2};
+    const RowView ov{(const char *)(a.out + b * a.sob + h * a.soh + p * DV), a.son * 4, (a.N - 1) * a.son * 4 + DV * 4};
+    uint32_t qo[NK], ko[NK], vo[NV];
+#pragma unroll
+    for (int it = 0; it < NK; ++it) {
+        const int item = tid + it * NTHR;
+        qo[it] = (uint32_t)((item / VPR) * qv.rs + (item % VPR) * 16);
+        ko[it] = (uint32_t)((item / VPR) * kv.rs + (item % VPR) * 16);
+    }
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+        const int item = tid + it * NTHR;
+        vo[it] = (uint32_t)((item / 8) * vv.rs + (item % 8) * 16);
+    }
+    bf16x8 ones8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones8[e] = (bf16)1.f;
+    u32x4 Qr[2][NK];   // q of chunks ch + 1 and ch + 2 in flight (phase 2)
+    auto issue_q = [&](int ch, int slot) {
+        const rsrc_t qr = qv.at(ch < nch ? t0_of(ch) : 0, ch < nch);
+#pragma unroll
+        for (int it = 0; it < NK; ++it) Qr[slot][it] = bload16nt(qr, qo[it]);
+    };
+
+    // ================= phase 1: the share's partial state
+    {
+        u32x4 Kr[2][NK], Vr[2][NV];   // chunks ch + 1 and ch + 2 in flight
+        auto issue_kv = [&](int ch, int slot) {
+            const int t0 = ch < nch ? t0_of(ch) : 0;
+            const rsrc_t kr = kv.at(t0, ch < nch), vr = vv.at(t0, ch < nch);
+#pragma unroll
+            for (int it = 0; it < NK; ++it) Kr[slot][it] = bload16nt(kr, ko[it]);
+#pragma unroll
+            for (int it = 0; it < NV; ++it) Vr[slot][it] = bload16nt(vr, vo[it]);
+        };
+        issue_kv(0, 0);
+        issue_kv(1, 1);
+        f32x4 Z[JT], S[SPW];
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) Z[jt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < SPW; ++m) S[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        float ntok = 0.f;
+        auto step = [&](int ch, int slot, int buf) {
+            bf16 *Kb = sm + buf * C * D, *Vb = sm + 2 * C * D + buf * C * DV;
+#pragma unroll
+            for (int it = 0; it < NK; ++it) {
+                const int item = tid + it * NTHR, row = item / VPR, vec = item % VPR;
+                *reinterpret_cast<u32x4 *>(Kb + swz<D>(row, vec * 8)) = cs_psi8(Kr[slot][it]);
+            }
+#pragma unroll
+            for (int it = 0; it < NV; ++it) {
+                const int item = tid + it * NTHR, row = item / 8, vec = item % 8;
+                *reinterpret_cast<u32x4 *>(Vb + swz<64>(row, vec * 8)) = Vr[slot][it];
+            }
+            issue_kv(ch + 2, slot);
+            __syncthreads();   // the stage is visible; the other buffer's readers are done
+            bf16x8 va[2];
+#pragma unroll
+            for (int sg = 0; sg < 2; ++sg) va[sg] = tr8<64>(Vb, 32 * sg, 16 * w, r, g);
+            f32x4 cv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int sg = 0; sg < 2; ++sg) cv = mma8(cv, ones8, va[sg]);
+            constexpr int JR = 2;   // state tiles whose operands are read together
+#pragma unroll
+            for (int j0 = 0; j0 < JT; j0 += JR) {
+                bf16x8 kt[JR][2];
+#pragma unroll
+                for (int j = 0; j < JR; ++j)
+#pragma unroll
+                    for (int sg = 0; sg < 2; ++sg) kt[j][sg] = cs_ktr8<D>(Kb, 32 * sg, j0 + j, r, g);
+#pragma unroll
+                for (int j = 0; j < JR; ++j) {
+#pragma unroll
+                    for (int sg = 0; sg < 2; ++sg) Z[j0 + j] = mma8(Z[j0 + j], kt[j][sg], va[sg]);
+                    Z[j0 + j] += cv;
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < SPW; ++m)
+#pragma unroll
+                for (int sg = 0; sg < 2; ++sg) S[m] = mma8(S[m], cs_ktr8<D>(Kb, 32 * sg, w + NWAVE * m, r, g), ones8);
+            ntok += ch < nch ? (float)min(C, a.N - t0_of(ch)) : 0.f;   // 0 for the empty step
+        };
+        for (int ch = 0; ch < nch; ch += 2) {   // an odd count runs one empty step (zeros)
+            step(ch, 0, 0);
+            if (ch + 2 >= nch) issue_q(0, 0);   // phase 2's first q during the last steps
+            step(ch + 1, 1, 1);
+            if (ch + 2 >= nch) issue_q(1, 1);
+        }
+        if (nch == 0) { issue_q(0, 0); issue_q(1, 1); }
+        float *slot = a.part + ((int64_t)hp * a.NS + grp) * SL;
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) slot[cs_dim(jt, 4 * g + i) * DV + 16 * w + r] = Z[jt][i];
+#pragma unroll
+        for (int m = 0; m < SPW; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (r == 0) slot[DV * D + cs_dim(w + NWAVE * m, 4 * g + i)] = S[m][i] + ntok;
+    }
+
+    // ================= phase 2: every query reads the carried-in memory
+    bf16x8 zh[KS], zl[KS], sh[KS], sl[KS];
+    f32x4 cz = {0.f, 0.f, 0.f, 0.f}, cs = cz;
+    {
+        const float *zin = a.z_in ? a.z_in + (int64_t)bh * D * D + p * DV + 16 * w + r : nullptr;
+        const float *sin = a.s_in ? a.s_in + (int64_t)bh * D : nullptr;
+        f32x4 Zm[JT], Sm[JT];
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int dim = cs_dim(jt, 4 * g + i);
+                Zm[jt][i] = zin ? zin[(int64_t)dim * D] : 0.f;
+                Sm[jt][i] = sin ? sin[dim] : 0.f;
+            }
+#pragma unroll
+        for (int u = 0; u < KS; ++u) {
+            cs_split(Zm[2 * u], Zm[2 * u + 1], zh[u], zl[u]);
+            cs_split(Sm[2 * u], Sm[2 * u + 1], sh[u], sl[u]);
+            cz = mma8(cz, zh[u], ones8);
+            cz = mma8(cz, zl[u], ones8);
+            cs = mma8(cs, sh[u], ones8);
+            cs = mma8(cs, sl[u], ones8);
+        }
+    }
+    __syncthreads();   // phase 1's stage buffers are read
+    auto read = [&](int ch, int slot, int buf) {
+        bf16 *Qb = sm + buf * C * D;
+#pragma unroll
+        for (int it = 0; it < NK; ++it) {
+            const int item = tid + it * NTHR, row = item / VPR, vec = item % VPR;
+            *reinterpret_cast<u32x4 *>(Qb + swz<D>(row, vec * 8)) = cs_psi8(Qr[slot][it]);
+        }
+        issue_q(ch + 2, slot);
+        __syncthreads();   // the stage is visible; the other buffer's readers are done
+        const int t0 = ch < nch ? t0_of(ch) : 0, nv = ch < nch ? min(C, a.N - t0) : 0;
+        const rsrc_t orr = ov.at(t0, nv > 0);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            bf16x8 qb[KS];
+#pragma unroll
+            for (int u = 0; u < KS; ++u) qb[u] = nat8(Qb + swz<D>(16 * m + r, 32 * u + 8 * g));
+            f32x4 o = cz, dn = cs;
+#pragma unroll
+            for (int u = 0; u < KS; ++u) {
+                o = mma8(o, zh[u], qb[u]);
+                o = mma8(o, zl[u], qb[u]);
+                dn = mma8(dn, sh[u], qb[u]);
+                dn = mma8(dn, sl[u], qb[u]);
+            }
+            // dn holds the normaliser of query r in every row
+            const float inv = __builtin_amdgcn_rcpf(dn[0] + a.eps);
+            const int t = 16 * m + r;
+            bstore16nt(orr, t < nv ? (uint32_t)(t * ov.rs + (16 * w + 4 * g) * 4) : OFF_NONE, o * inv);
+        }
+    };
+    for (int ch = 0; ch < nch; ch += 2) {
+        read(ch, 0, 0);
+        if (ch + 1 < nch) read(ch + 1, 1, 1);
+    }
+}
+
 // One recurrent step for every head: Z += phi(k) v^T, S += phi(k),
 // out = phi(q)^T Z / (phi(q) . S + eps).  Pure streaming over Z (read, update,
 // write back once); every state element is read and written by one thread.
@@ -2887,6 +3083,15 @@ la_status la_memory_fwd(const void *q, la_strides sq, const void *k, la_strides 
     const bool f32 = dt == LA_F32;
     a.G = pl.G; a.L = pl.L; a.slot0 = 0;
     const bool cs = LA_COLUMN_SPLIT && !f32 && (d == 64 || d == 128) && pl.C == 64;
+    if (cs && want_out) {
+        // one pass: the reads of the memory and the partial states, then the
+        // memory after the segment
+        const unsigned nwg = (unsigned)(BH * pl.P * pl.G);
+        if (d == 64) hipLaunchKernelGGL((k_cs_memory<64>), dim3(nwg), dim3(NTHR), 0, stream, a);
+        else hipLaunchKernelGGL((k_cs_memory<128>), dim3(nwg), dim3(NTHR), 0, stream, a);
+        launch_slots(d, a, BH, pl.P, pl.G, 1, stream);
+        return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
+    }
     if (cs) launch_cs_state(d, a, (unsigned)(BH * pl.P * pl.G), stream);
     else dispatch(f32, d, pl.C, 0, a, (int)(BH * pl.P * pl.G), stream);
     launch_slots(d, a, BH, pl.P, pl.G, 3, stream);
