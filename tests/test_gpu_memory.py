@@ -152,3 +152,22 @@ def test_memory_segmented_workload_sampled_heads():
                 assert heads_err(oc[0, h, sl], ro, d) < 2e-3, (h, i)
         assert block_err(zs[nseg & 1][0, h].cpu(), zr, d * d) < 2e-3
         assert block_err(ss[nseg & 1][0, h].cpu(), sr, d) < 2e-3
+
+
+def test_memory_strided_inputs_and_wide_output():
+    # [B, N, H, d] storage viewed as [B, H, N, d]; reads into a wider buffer
+    B, H, N, d = 2, 4, 777, 128
+    g = torch.Generator().manual_seed(1700)
+    base = [(torch.randn(B, N, H, d, generator=g) * d ** -0.5).to(torch.bfloat16) for _ in range(3)]
+    q, k, v = (t.permute(0, 2, 1, 3) for t in base)
+    z0, s0 = earlier_memory(B, H, d, 1701, torch.bfloat16)
+    ro, rz, rs = oracle.memory(q.contiguous(), k.contiguous(), v.contiguous(), 1e-6, z0, s0)
+    qd, kd, vd = (t.to(DEV).permute(0, 2, 1, 3) for t in base)
+    wide = torch.full((B, H, N, 2 * d), 7.0, device=DEV)
+    z = torch.empty(B, H, d, d, device=DEV)
+    s = torch.empty(B, H, d, device=DEV)
+    la.la_memory_fwd(qd, kd, vd, wide[..., :d], z_in=z0.to(DEV), s_in=s0.to(DEV), z_out=z, s_out=s)
+    torch.cuda.synchronize()
+    assert heads_err(wide[..., :d].cpu(), ro, d) < 2e-3
+    assert (wide[..., d:] == 7.0).all()
+    assert block_err(z.cpu(), rz, d * d) < 2e-3 and block_err(s.cpu(), rs, d) < 2e-3

@@ -81,3 +81,16 @@ def test_unnormalized_headline_workload_sampled_heads():
     for b, h in [(0, 0), (1, 5), (3, 7)]:
         ref = oracle.causal_unnormalized(q[b, h], k[b, h], v[b, h])
         assert heads_err(out[b, h], ref, w.d) < 2e-3, (b, h)
+
+
+def test_unnormalized_strided_inputs():
+    B, H, N, d = 2, 4, 777, 64
+    g = torch.Generator().manual_seed(2300)
+    base = [(torch.randn(B, N, H, d, generator=g) * 0.125).to(torch.bfloat16) for _ in range(3)]
+    q, k, v = (t.permute(0, 2, 1, 3) for t in base)
+    ref = oracle.causal_unnormalized(q.contiguous(), k.contiguous(), v.contiguous())
+    qd, kd, vd = (t.to(DEV).permute(0, 2, 1, 3) for t in base)
+    out = torch.empty(B, H, N, d, device=DEV)
+    la.la_causal_fwd_unnormalized(qd, kd, vd, out)
+    torch.cuda.synchronize()
+    assert heads_err(out.cpu(), ref, d) < 2e-3
