@@ -2318,15 +2318,16 @@ __global__ void __launch_bounds__(NTHR, D <= 64 ? 4 : 2) k_cs_apply(const Args a
     }
 }
 
-// k_cs_memory: one token share of a compressive-memory call in one launch.
-// Share grp of G takes the 64-token chunks grp, grp + G, ...  First its
+// k_cs_memory: a compressive-memory call in one launch of two workgroups per
+// token share (share grp of G takes the 64-token chunks grp, grp + G, ...).
+// The reads of the memory need only the carried-in state, not the segment's,
+// so the two jobs run side by side: an even workgroup forms the share's
 // partial state, Z = sum psi(k) v^T + 1 (sum v)^T and S = sum psi(k) + tokens
-// (as k_cs_state; each wave forms only its S tiles w, w + 4, ...), goes to its
-// slot; then every query of the share reads the carried-in memory,
-// out_t = phi(q_t)^T Z_in / (phi(q_t) . S_in + eps) (as k_cs_apply, with Z_in
-// and S_in read from the state tensors).  The two phases share the LDS, and
-// their registers are never live together.  k_slots then adds the slots to
-// the memory.
+// (as k_cs_state; each wave forms only its S tiles w, w + 4, ...), and writes
+// it to the share's slot; the odd one lets every query of the share read the
+// carried-in memory, out_t = phi(q_t)^T Z_in / (phi(q_t) . S_in + eps) (as
+// k_cs_apply, with Z_in and S_in read from the state tensors).  k_slots then
+// adds the slots to the memory.
 template <int D>
 __global__ void __launch_bounds__(NTHR, 2) k_cs_memory(const Args a)
 {
@@ -2335,11 +2336,13 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_memory(const Args a)
     constexpr int SL = Slot<D, DV>::SIZE;
     constexpr int SPW = JT / NWAVE;
     static_assert(JT % NWAVE == 0, "S tiles split evenly over the waves");
-    // phase 1: psi(K) [2][C][D], V [2][C][DV]; phase 2: psi(Q) [2][C][D]
+    // state: psi(K) [2][C][D], V [2][C][DV]; reads: psi(Q) [2][C][D]
     __shared__ __attribute__((aligned(16))) bf16 sm[2 * C * D + 2 * C * DV];
     const int tid = threadIdx.x, lane = tid % WAVE, r = lane % 16, g = lane / 16;
     const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
-    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    const int wg2 = xcd_remap(blockIdx.x, gridDim.x);
+    const bool reader = wg2 & 1;   // odd workgroups read the memory, even ones form the partial states
+    const int wg = wg2 >> 1;
     const int p = wg % a.P, rest = wg / a.P, grp = rest % a.G, bh = rest / a.G;
     const int b = bh / a.H, h = bh % a.H;
     const int hp = bh * a.P + p;
@@ -2366,15 +2369,15 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_memory(const Args a)
     bf16x8 ones8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones8[e] = (bf16)1.f;
-    u32x4 Qr[2][NK];   // q of chunks ch + 1 and ch + 2 in flight (phase 2)
+    u32x4 Qr[2][NK];   // q of chunks ch + 1 and ch + 2 in flight (reads)
     auto issue_q = [&](int ch, int slot) {
         const rsrc_t qr = qv.at(ch < nch ? t0_of(ch) : 0, ch < nch);
 #pragma unroll
         for (int it = 0; it < NK; ++it) Qr[slot][it] = bload16nt(qr, qo[it]);
     };
 
-    // ================= phase 1: the share's partial state
-    {
+    // ================= even workgroups: the share's partial state
+    if (!reader) {
         u32x4 Kr[2][NK], Vr[2][NV];   // chunks ch + 1 and ch + 2 in flight
         auto issue_kv = [&](int ch, int slot) {
             const int t0 = ch < nch ? t0_of(ch) : 0;
@@ -2435,11 +2438,8 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_memory(const Args a)
         };
         for (int ch = 0; ch < nch; ch += 2) {   // an odd count runs one empty step (zeros)
             step(ch, 0, 0);
-            if (ch + 2 >= nch) issue_q(0, 0);   // phase 2's first q during the last steps
             step(ch + 1, 1, 1);
-            if (ch + 2 >= nch) issue_q(1, 1);
         }
-        if (nch == 0) { issue_q(0, 0); issue_q(1, 1); }
         float *slot = a.part + ((int64_t)hp * a.NS + grp) * SL;
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt)
@@ -2450,9 +2450,12 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_memory(const Args a)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 if (r == 0) slot[DV * D + cs_dim(w + NWAVE * m, 4 * g + i)] = S[m][i] + ntok;
+        return;
     }
 
-    // ================= phase 2: every query reads the carried-in memory
+    // ================= odd workgroups: every query reads the carried-in memory
+    issue_q(0, 0);
+    issue_q(1, 1);
     bf16x8 zh[KS], zl[KS], sh[KS], sl[KS];
     f32x4 cz = {0.f, 0.f, 0.f, 0.f}, cs = cz;
     {
@@ -2477,7 +2480,6 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_memory(const Args a)
             cs = mma8(cs, sl[u], ones8);
         }
     }
-    __syncthreads();   // phase 1's stage buffers are read
     auto read = [&](int ch, int slot, int buf) {
         bf16 *Qb = sm + buf * C * D;
 #pragma unroll
@@ -3020,7 +3022,7 @@ la_status la_noncausal_fwd(const void *q, la_strides sq, const void *k, la_strid
 // published state does not outweigh its inputs, and shorter apply
 // workgroups, so that the readout still covers the chip.
 #ifndef LA_MEM_GROUP_TARGET
-#define LA_MEM_GROUP_TARGET 256
+#define LA_MEM_GROUP_TARGET 128
 #endif
 #ifndef LA_MEM_APPLY_CHUNKS
 #define LA_MEM_APPLY_CHUNKS 2
@@ -3084,9 +3086,9 @@ la_status la_memory_fwd(const void *q, la_strides sq, const void *k, la_strides 
     a.G = pl.G; a.L = pl.L; a.slot0 = 0;
     const bool cs = LA_COLUMN_SPLIT && !f32 && (d == 64 || d == 128) && pl.C == 64;
     if (cs && want_out) {
-        // one pass: the reads of the memory and the partial states, then the
-        // memory after the segment
-        const unsigned nwg = (unsigned)(BH * pl.P * pl.G);
+        // one launch: the partial states and the reads of the memory (two
+        // workgroups per share), then the memory after the segment
+        const unsigned nwg = (unsigned)(2 * BH * pl.P * pl.G);
         if (d == 64) hipLaunchKernelGGL((k_cs_memory<64>), dim3(nwg), dim3(NTHR), 0, stream, a);
         else hipLaunchKernelGGL((k_cs_memory<128>), dim3(nwg), dim3(NTHR), 0, stream, a);
         launch_slots(d, a, BH, pl.P, pl.G, 1, stream);
