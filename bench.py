@@ -82,19 +82,27 @@ def roofline(bytes_per_call, ms_per_call, traffic=None):
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
 
 
-def prewarm(fn, n_rot, seconds):
+def prewarm(fn, n_rot, seconds, batch=100):
     """Untimed calls for about `seconds` of wall time before the warm-up
     steps, so that the GPU clocks have ramped up when the timed region starts
     (a fresh process reaches steady clocks only after some tens of ms of
-    work).  Runs in batches of 100 calls with a synchronize after each."""
+    work).  Runs in batches of `batch` calls with a synchronize after each."""
     import torch
     t0 = time.perf_counter()
     i = 0
     while time.perf_counter() - t0 < seconds:
-        for _ in range(100):
+        for _ in range(batch):
             fn(i % n_rot)
             i += 1
         torch.cuda.synchronize()
+
+
+def leg_counts(args, steps, warmup):
+    """Timed and warm-up repetitions of a non-headline workload: fixed
+    counts (the headline's --steps / --warmup do not shrink them), or the
+    --leg-steps / --leg-warmup overrides (short profiled runs)."""
+    return (args.leg_steps if args.leg_steps is not None else steps,
+            args.leg_warmup if args.leg_warmup is not None else warmup)
 
 
 def step_spread(fn, steps, n_rot, blocks=10):
@@ -148,7 +156,7 @@ def bench_headline(args, torch, la, inp):
     for _ in range(n_rot):
         sets.append((q.to(dev), k.to(dev), v.to(dev),
                      torch.empty(w.B, w.H, w.N, w.d, dtype=torch.float32, device=dev)))
-    ws = torch.empty(max(1, la.la_causal_fwd_workspace(w.B, w.H, w.N, w.d, w.dtype, w.chunk)),
+    ws = torch.empty(max(1, la.la_causal_fwd_workspace(w.B, w.H, w.N, w.d, w.chunk)),
                      dtype=torch.uint8, device=dev)
 
     calls = [la.prepare_causal_fwd(a[0], a[1], a[2], a[3], chunk=w.chunk, eps=w.eps, workspace=ws) for a in sets]
@@ -171,7 +179,7 @@ def bench_unnormalized(args, torch, la, inp):
     n_rot = args.rotate
     sets = [(q.to(dev), k.to(dev), v.to(dev), torch.empty(w.B, w.H, w.N, w.d, dtype=torch.float32, device=dev))
             for _ in range(n_rot)]
-    ws = torch.empty(max(1, la.la_causal_fwd_workspace(w.B, w.H, w.N, w.d, w.dtype, w.chunk)),
+    ws = torch.empty(max(1, la.la_causal_fwd_workspace(w.B, w.H, w.N, w.d, w.chunk)),
                      dtype=torch.uint8, device=dev)
     calls = [la.prepare_causal_fwd(a[0], a[1], a[2], a[3], chunk=w.chunk, eps=w.eps, workspace=ws, normalize=False)
              for a in sets]
@@ -195,7 +203,7 @@ def bench_segmented(args, torch, la, inp):
     out = torch.empty(B, H, N, d, dtype=torch.float32, device=dev)
     zs = [torch.zeros(B, H, d, d, device=dev) for _ in range(2)]
     ss = [torch.zeros(B, H, d, device=dev) for _ in range(2)]
-    ws = torch.empty(max(1, la.la_causal_fwd_workspace(B, H, w.segment, d, w.dtype, 0)), dtype=torch.uint8,
+    ws = torch.empty(max(1, la.la_causal_fwd_workspace(B, H, w.segment, d)), dtype=torch.uint8,
                      device=dev)
     nseg = N // w.segment
 
@@ -210,8 +218,9 @@ def bench_segmented(args, torch, la, inp):
         for c in calls:
             c()
 
-    steps = max(3, args.steps // 4)
-    total_ms = time_steps(step, steps, max(1, args.warmup // 2), 1)
+    steps, warm = leg_counts(args, 20, 5)
+    prewarm(step, 1, args.prewarm_s, batch=4)
+    total_ms = time_steps(step, steps, warm, 1)
     ms = total_ms / steps
     seg_w = inp.Workload("segment", "causal", w.dtype, w.B, w.H, w.segment, w.d, 0, 1.0)
     b_call = alg_bytes_causal(seg_w, with_state_io=True)
@@ -232,7 +241,7 @@ def bench_decode(args, torch, la, inp):
         for _ in range(nstate):
             z = torch.empty(B, H, d, d, device=dev)
             s = torch.empty(B, H, d, device=dev)
-            la.la_causal_fwd(pq.to(dev), pk.to(dev), pv.to(dev), None, eps=w.eps, z_out=z, s_out=s)
+            la.la_causal_fwd(None, pk.to(dev), pv.to(dev), None, eps=w.eps, z_out=z, s_out=s)
             zs.append(z)
             ss.append(s)
         out = torch.empty(B, H, d, device=dev)
@@ -244,21 +253,23 @@ def bench_decode(args, torch, la, inp):
         def step(i):
             calls[i % nst]()
 
+        prewarm(step, 10 ** 9, args.prewarm_s)
         total_ms = time_steps(step, nst, 16, 10 ** 9)
         ms = total_ms / nst
         bpc = B * H * (2 * (d * d + d) * 4 + 3 * d * w.dtype.itemsize + d * 4)
         res[label] = {"ms_per_step": round(ms, 5), "value": round(B * H / (ms * 1e-3), 1),
                       "roofline": roofline(bpc, ms, measured_traffic(w.name))}
     # the prefix as a full causal call with outputs: a large B*H data point
-    # (not the decode target)
+    # (not the decode target; the prefix state itself comes from a state-only
+    # call, timed in the prefill workload)
     pw = inp.Workload("decode_prefix", "causal", w.dtype, B, H, int(pq.shape[2]), d, 0, 1.0)
     pqd, pkd, pvd = pq.to(dev), pk.to(dev), pv.to(dev)
     pout = torch.empty(B, H, pq.shape[2], d, dtype=torch.float32, device=dev)
-    pws = torch.empty(max(1, la.la_causal_fwd_workspace(B, H, pq.shape[2], d, w.dtype, 0)), dtype=torch.uint8,
+    pws = torch.empty(max(1, la.la_causal_fwd_workspace(B, H, pq.shape[2], d)), dtype=torch.uint8,
                       device=dev)
     pcall = la.prepare_causal_fwd(pqd, pkd, pvd, pout, eps=w.eps, workspace=pws)
-    psteps = max(3, args.steps // 30)
-    pms = time_steps(lambda _: pcall(), psteps, 2, 1) / psteps
+    psteps, pwarm = leg_counts(args, 10, 2)
+    pms = time_steps(lambda _: pcall(), psteps, pwarm, 1) / psteps
     res["prefix_causal_with_outputs"] = {"shape": [B, H, int(pq.shape[2]), d], "ms_per_call": round(pms, 4),
                                          "value": round(B * H * pq.shape[2] / (pms * 1e-3), 1),
                                          "roofline": roofline(alg_bytes_causal(pw), pms)}
@@ -270,15 +281,16 @@ def bench_noncausal(args, torch, la, inp):
     dev = torch.device("cuda:0")
     q, k, v = (t.to(dev) for t in inp.workload_inputs(w))
     out = torch.empty(w.B, w.H, w.N, w.d, dtype=torch.float32, device=dev)
-    ws = torch.empty(max(1, la.la_noncausal_workspace(w.B, w.H, w.N, w.d, w.dtype)), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(1, la.la_noncausal_workspace(w.B, w.H, w.N, w.d)), dtype=torch.uint8, device=dev)
 
     call = la.prepare_noncausal_fwd(q, k, v, out, eps=w.eps, workspace=ws)
 
     def step(_):
         call()
 
-    steps = max(3, args.steps // 2)
-    total_ms = time_steps(step, steps, 2, 1)
+    steps, warm = leg_counts(args, 20, 5)
+    prewarm(step, 1, args.prewarm_s, batch=2)
+    total_ms = time_steps(step, steps, warm, 1)
     per_call = total_ms / steps
     return {"workload": w.name, "value": round(w.head_tokens / (per_call * 1e-3), 1), "unit": "head-tokens/s",
             "ms_per_step": round(per_call, 4),
@@ -295,7 +307,7 @@ def bench_memory(args, torch, la, inp):
     out = torch.empty(B, H, N, d, dtype=torch.float32, device=dev)
     zs = [torch.zeros(B, H, d, d, device=dev) for _ in range(2)]
     ss = [torch.zeros(B, H, d, device=dev) for _ in range(2)]
-    ws = torch.empty(max(1, la.la_memory_workspace(B, H, w.segment, d, w.dtype)), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(1, la.la_memory_workspace(B, H, w.segment, d)), dtype=torch.uint8, device=dev)
     nseg = N // w.segment
     calls = []
     for i in range(nseg):
@@ -308,14 +320,40 @@ def bench_memory(args, torch, la, inp):
         for c in calls:
             c()
 
-    steps = max(3, args.steps // 4)
-    total_ms = time_steps(step, steps, max(1, args.warmup // 2), 1)
+    steps, warm = leg_counts(args, 20, 5)
+    prewarm(step, 1, args.prewarm_s, batch=4)
+    total_ms = time_steps(step, steps, warm, 1)
     ms = total_ms / steps
     seg_w = inp.Workload("segment", "memory", w.dtype, w.B, w.H, w.segment, w.d, 0, 1.0)
     b_call = alg_bytes_causal(seg_w, with_state_io=True)
     return {"workload": w.name, "value": round(w.head_tokens / (ms * 1e-3), 1), "unit": "head-tokens/s",
             "ms_per_step": round(ms, 4), "calls_per_step": nseg,
             "roofline": roofline(b_call, ms / nseg, measured_traffic(w.name))}
+
+
+def bench_prefill(args, torch, la, inp):
+    """State-only calls (out = NULL, no q): the prefill, which needs only the
+    state after the prompt.  On the headline shape (B4 H8 N4096 d64) and on
+    the decode workload's prefix (B64 H32 N1024 d128).  Algorithmic bytes:
+    k and v once (bf16) plus the fp32 state written."""
+    dev = torch.device("cuda:0")
+    res = {}
+    for label, w in (("headline_shape", inp.WORKLOADS[inp.HEADLINE]), ("decode_prefix", inp.WORKLOADS[inp.DECODE])):
+        N = w.prefix if w.kind == "decode" else w.N
+        g = inp.make_generator(w.seed + 100)
+        k, v = (inp.draw((w.B, w.H, N, w.d), g, w.dtype, w.scale).to(dev) for _ in range(2))
+        z = torch.empty(w.B, w.H, w.d, w.d, device=dev)
+        s = torch.empty(w.B, w.H, w.d, device=dev)
+        ws = torch.empty(max(1, la.la_causal_fwd_workspace(w.B, w.H, N, w.d)), dtype=torch.uint8, device=dev)
+        call = la.prepare_causal_fwd(None, k, v, None, eps=w.eps, z_out=z, s_out=s, workspace=ws)
+        steps, warm = leg_counts(args, 50, 10)
+        prewarm(lambda _: call(), 1, args.prewarm_s)
+        ms = time_steps(lambda _: call(), steps, warm, 1) / steps
+        b = w.B * w.H * (N * 2 * w.d * w.dtype.itemsize + (w.d * w.d + w.d) * 4)
+        res[label] = {"shape": [w.B, w.H, N, w.d], "ms_per_call": round(ms, 5),
+                      "value": round(w.B * w.H * N / (ms * 1e-3), 1), "unit": "head-tokens/s",
+                      "alg_bytes_per_call": b, "roofline": roofline(b, ms, None)}
+    return res
 
 
 def cpu_baseline(w, qkv, seconds):
@@ -335,6 +373,11 @@ def cpu_baseline(w, qkv, seconds):
                       f"fp64 recurrent form, run back to back for about {seconds:g} s"}
 
 
+LEGS = ("headline", "segmented", "decode", "noncausal", "memory", "unnormalized", "prefill")
+LEG_FNS = {"segmented": bench_segmented, "decode": bench_decode, "noncausal": bench_noncausal,
+           "memory": bench_memory, "unnormalized": bench_unnormalized, "prefill": bench_prefill}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -344,6 +387,11 @@ def main():
     ap.add_argument("--prewarm-s", type=float, default=0.25,
                     help="seconds of untimed headline calls before the warm-up steps (GPU clock ramp)")
     ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
+    ap.add_argument("--only", default=None,
+                    help="comma-separated workloads to run, of " + ",".join(LEGS) + " (profiling runs; "
+                         "without 'headline' the line carries only the workloads object)")
+    ap.add_argument("--leg-steps", type=int, default=None, help="timed repetitions of each non-headline workload")
+    ap.add_argument("--leg-warmup", type=int, default=None, help="warm-up repetitions of each non-headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="wall time given to the oracle baseline")
     ap.add_argument("--copy-probe", action="store_true",
@@ -371,6 +419,20 @@ def main():
         print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n, "launches": 3}))
         return
     la.load_library()
+    legs = LEGS if args.only is None else tuple(x.strip() for x in args.only.split(","))
+    unknown = [x for x in legs if x not in LEGS]
+    if unknown:
+        print(f"unknown workloads {unknown}; choose from {LEGS}", file=sys.stderr)
+        sys.exit(2)
+    if args.headline_only:
+        legs = ("headline",)
+    if "headline" not in legs:
+        line = {"workloads": {}}
+        for name in legs:
+            log(f"{name} workload ...")
+            line["workloads"][name] = LEG_FNS[name](args, torch, la, inp)
+        print(json.dumps(line), flush=True)
+        return
 
     log("headline workload ...")
     w, total_ms, per_call, qkv, spread = bench_headline(args, torch, la, inp)
@@ -400,17 +462,10 @@ def main():
     copy_gbs = copy_bandwidth(torch)
     line["roofline"]["copy_1gib_gbs"] = copy_gbs
     line["roofline"]["frac_of_copy"] = round(line["roofline"]["achieved"] / copy_gbs, 4)
-    if not args.headline_only:
-        log("segmented workload ...")
-        line.setdefault("workloads", {})["segmented"] = bench_segmented(args, torch, la, inp)
-        log("decode workload ...")
-        line["workloads"]["decode"] = bench_decode(args, torch, la, inp)
-        log("non-causal workload ...")
-        line["workloads"]["noncausal"] = bench_noncausal(args, torch, la, inp)
-        log("memory workload ...")
-        line["workloads"]["memory"] = bench_memory(args, torch, la, inp)
-        log("unnormalised causal workload ...")
-        line["workloads"]["unnormalized"] = bench_unnormalized(args, torch, la, inp)
+    for name in legs:
+        if name != "headline":
+            log(f"{name} workload ...")
+            line.setdefault("workloads", {})[name] = LEG_FNS[name](args, torch, la, inp)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline(w, qkv, args.cpu_seconds)

@@ -39,9 +39,16 @@
  *    null stream).
  *  - Results are deterministic: the same inputs, sizes and chunk give bitwise
  *    identical outputs (no floating-point atomics).
- *  - Non-finite inputs propagate to every later output of their head and to
- *    the carried state; in the causal kernels an infinite v may also turn the
- *    outputs of earlier tokens of the same chunk into NaN.
+ *  - Non-finite inputs: a NaN or infinite q, k or v reaches the outputs of its
+ *    own token and of every later token of its head and the carried state,
+ *    as in the recurrent form.  The causal calls evaluate each 64-token chunk
+ *    as the chunk formulas of "Attention Kernel Mask" print it, a masked
+ *    score matrix times V; in IEEE arithmetic a masked (zero) score times an
+ *    infinite value is NaN, so an infinite v_s may also turn column c of the
+ *    outputs of earlier tokens of its chunk into NaN (c: the column that holds
+ *    the infinity).  Outputs of tokens in earlier chunks, and other columns,
+ *    are unaffected.  (Non-causal and memory calls: every output of the head
+ *    reads the non-finite state.)
  */
 #ifndef LINATTN_H
 #define LINATTN_H
@@ -55,15 +62,16 @@ extern "C" {
 
 typedef enum {
     LA_OK = 0,
-    LA_ERR_NULL = 1,        /* a required pointer is NULL */
-    LA_ERR_SHAPE = 2,       /* a negative size, or sizes too large for 32-bit indexing */
-    LA_ERR_DTYPE = 3,       /* dtype is not LA_F32 or LA_BF16 */
-    LA_ERR_ALIGN = 4,       /* a pointer or a stride is not 16-byte aligned */
-    LA_ERR_UNSUPPORTED = 5, /* d not in {32,64,128}, or chunk not in {0,16,32,64,128} */
-    LA_ERR_VALUE = 6,       /* eps negative or not finite */
-    LA_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than the query returned */
-    LA_ERR_ALIAS = 8,       /* an output state overlaps an input state other than exactly */
-    LA_ERR_LAUNCH = 9       /* a HIP launch or copy failed */
+    LA_ERR_NULL = -1,        /* a required pointer is NULL */
+    LA_ERR_SHAPE = -2,       /* a negative size, or sizes too large for 32-bit indexing */
+    LA_ERR_DTYPE = -3,       /* dtype is not LA_F32 or LA_BF16 */
+    LA_ERR_ALIGN = -4,       /* a pointer or a stride is not 16-byte aligned */
+    LA_ERR_UNSUPPORTED = -5, /* d not in {32,64,128}, chunk not in {0,16,32,64,128}, or a
+                                causal call issued while its stream is being captured */
+    LA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the query returned */
+    LA_ERR_LAUNCH = -7,      /* a HIP launch failed */
+    LA_ERR_VALUE = -8,       /* eps negative or not finite */
+    LA_ERR_ALIAS = -9        /* an output state overlaps an input state other than exactly */
 } la_status;
 
 typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
@@ -72,9 +80,6 @@ typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
 typedef struct {
     int64_t b, h, n;
 } la_strides;
-
-/* Workspace flag: the causal call will pass z_out == z_in and/or s_out == s_in. */
-#define LA_WS_INPLACE_STATE 1
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *la_status_str(la_status s);
@@ -92,20 +97,34 @@ int la_version(void);
  * z_in / s_in: state carried in from earlier segments ("Segment-Wise
  * Attention"); NULL means zeros (each independently).
  * z_out / s_out: state after the last token; NULL means not written.  They may
- * equal z_in / s_in exactly (in place) if the workspace was sized with
- * LA_WS_INPLACE_STATE; any other overlap is LA_ERR_ALIAS.
- * out: NULL computes only the state (prefill / state-only use); then z_out
- * and s_out must not both be NULL.
+ * equal z_in / s_in exactly (in place); any other overlap is LA_ERR_ALIAS.
+ * out: NULL computes only the state from k and v (the prefill remark of
+ * "Attention Kernel Mask": only the final sums are needed, formed in
+ * parallel and summed); then q may be NULL and is not read, and z_out and
+ * s_out must not both be NULL.
  * chunk: 0 = default; otherwise 16, 32, 64 or 128 tokens.  It is a tuning
- * choice only: results agree for every chunk up to rounding.  A chunk too
- * large for the on-chip memory of a (dtype, d) pair is reduced to the largest
- * one that fits.
+ * choice only: results agree for every chunk up to rounding.  The kernels'
+ * MFMA tiles span 64 tokens, so 16 and 32 run as 64; 128 runs as 128 for
+ * bf16 inputs at d = 32 and 64 with out != NULL, and as 64 otherwise.
  * N = 0 copies the input state (or zeros) to the output state.
  * Workspace: at least la_causal_fwd_workspace(...) bytes of device memory,
  * any contents; 256-byte alignment recommended.  NULL is allowed when the
- * query returns 0.
+ * query returns 0.  The size covers both dtypes and both uses (with and
+ * without out).
+ * Look-back: workgroups of one call exchange partial states through the
+ * workspace, each tagged by the call, and a workgroup waits for the tags of
+ * the earlier token groups of its head.  The tag is chosen when the call is
+ * issued, so a call issued while `hip_stream` is being captured into a HIP
+ * graph (whose replays would reuse it) is refused with LA_ERR_UNSUPPORTED.
+ * Every wait is bounded (about 2^20 polls); a wait that gives up writes NaN
+ * into the state it was summing, so the outputs of its columns in that
+ * token group and the final state turn NaN instead of silently wrong, and
+ * it adds 1 to the 32-bit counter at byte offset 0 of the workspace.  The
+ * library never resets that counter: a caller that wants to check it sets it
+ * to zero once after allocating the workspace and reads it after
+ * synchronising.
  */
-size_t la_causal_fwd_workspace(int B, int H, int N, int d, la_dtype dt, int chunk, int flags);
+size_t la_causal_fwd_workspace(int B, int H, int N, int d, int chunk);
 la_status la_causal_fwd(const void *q, la_strides sq, const void *k, la_strides sk,
                         const void *v, la_strides sv, la_dtype dt,
                         float *out, la_strides so,
@@ -149,9 +168,10 @@ la_status la_decode_step(const void *q, const void *k, const void *v, la_dtype d
  *   Z = sum_t phi(k_t) v_t^T,  S = sum_t phi(k_t),
  *   out_t = phi(q_t)^T Z / (phi(q_t) . S + eps)   for every t.
  * The sums over t are split across workgroups and reduced in a fixed order.
- * Workspace: at least la_noncausal_workspace(...) bytes, any contents.
+ * Workspace: at least la_noncausal_workspace(...) bytes, any contents (the
+ * size covers both dtypes).
  */
-size_t la_noncausal_workspace(int B, int H, int N, int d, la_dtype dt);
+size_t la_noncausal_workspace(int B, int H, int N, int d);
 la_status la_noncausal_fwd(const void *q, la_strides sq, const void *k, la_strides sk,
                            const void *v, la_strides sv, la_dtype dt,
                            float *out, la_strides so,
@@ -177,9 +197,10 @@ la_status la_noncausal_fwd(const void *q, la_strides sq, const void *k, la_strid
  * N = 0 copies the input memory (or zeros) to the output.
  * The sum over the segment is split across workgroups and reduced in a fixed
  * order (deterministic).
- * Workspace: at least la_memory_workspace(...) bytes, any contents.
+ * Workspace: at least la_memory_workspace(...) bytes, any contents (the size
+ * covers both dtypes).
  */
-size_t la_memory_workspace(int B, int H, int N, int d, la_dtype dt);
+size_t la_memory_workspace(int B, int H, int N, int d);
 la_status la_memory_fwd(const void *q, la_strides sq, const void *k, la_strides sk,
                         const void *v, la_strides sv, la_dtype dt,
                         float *out, la_strides so,

@@ -57,6 +57,8 @@ def _load():
         lib.oracle_memory.restype = None
         lib.oracle_causal_unnormalized.argtypes = [L, L, L, fp, fp, fp, dp, dp]
         lib.oracle_causal_unnormalized.restype = None
+        lib.oracle_causal_bwd.argtypes = [L, L, L, D, fp, fp, fp, fp, dp, dp, dp, dp, dp, dp, dp, dp, dp]
+        lib.oracle_causal_bwd.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -170,3 +172,27 @@ def causal_unnormalized(q, k, v, z_in=None):
     out = np.empty((BH, N, d), np.float64)
     _load().oracle_causal_unnormalized(BH, N, d, _fptr(qa), _fptr(ka), _fptr(va), _dptr(zi), _dptr(out))
     return out.reshape(*lead, N, d)
+
+
+def causal_bwd(q, k, v, dout, eps: float, z_in=None, s_in=None, dz_out=None, ds_out=None):
+    """Gradients of oracle.causal: for the upstream gradient dout [..., N, d]
+    (and dz_out [..., d, d], ds_out [..., d] reaching the final state; None =
+    zeros), returns (dq, dk, dv [..., N, d], dz_in [..., d, d], ds_in [..., d])
+    in float64.  dout is read as float32 (the values a GPU call sees)."""
+    qa, ka, va, da = _f32(q), _f32(k), _f32(v), _f32(dout)
+    lead, (N, d) = qa.shape[:-2], qa.shape[-2:]
+    BH = int(np.prod(lead)) if lead else 1
+    zi = None if z_in is None else _f64(z_in).reshape(BH, d, d)
+    si = None if s_in is None else _f64(s_in).reshape(BH, d)
+    dzo = None if dz_out is None else _f64(dz_out).reshape(BH, d, d)
+    dso = None if ds_out is None else _f64(ds_out).reshape(BH, d)
+    dq = np.empty((BH, N, d), np.float64)
+    dk = np.empty((BH, N, d), np.float64)
+    dv = np.empty((BH, N, d), np.float64)
+    dzi = np.empty((BH, d, d), np.float64)
+    dsi = np.empty((BH, d), np.float64)
+    _load().oracle_causal_bwd(BH, N, d, float(eps), _fptr(qa), _fptr(ka), _fptr(va), _fptr(da),
+                              _dptr(zi), _dptr(si), _dptr(dzo), _dptr(dso),
+                              _dptr(dq), _dptr(dk), _dptr(dv), _dptr(dzi), _dptr(dsi))
+    sh = lambda a: a.reshape(*lead, N, d)
+    return sh(dq), sh(dk), sh(dv), dzi.reshape(*lead, d, d), dsi.reshape(*lead, d)

@@ -279,3 +279,104 @@ void oracle_causal_unnormalized(long BH, long N, long d,
         free(W); free(phik); free(phiq);
     }
 }
+
+/* Derivative of phi: 1 above zero, exp(x) at or below it (both sides give 1
+ * at x = 0, so phi is continuously differentiable). */
+static double dphi(double x) { return x > 0.0 ? 1.0 : exp(x); }
+
+/*
+ * Gradients of the causal form -- the backward pass of a training step,
+ * which "Attention Kernel Mask" names (the "Training-Backward" row of its
+ * table under "Causal Attention Training and Inferencing"; training needs
+ * every output, the cumsum problem of its "Causal linear attention" notes)
+ * but does not write out.  They are the exact derivatives of oracle_causal's
+ * definition.  With f_t = phi(k_t), g_t = phi(q_t), Z_t, S_t the running
+ * state (state_in included) and D_t = g_t . S_t + eps, out_t = Z_t^T g_t / D_t,
+ * for an upstream gradient dout_t (and dz_out, ds_out reaching the final
+ * state; NULL = zeros):
+ *   dn_t = dout_t / D_t,  dD_t = -(dout_t . out_t) / D_t
+ *   dq_t = (Z_t dn_t + S_t dD_t) * phi'(q_t)                 (forward sweep)
+ *   R_t = dz_out + sum_{u>=t} g_u dn_u^T,  r_t = ds_out + sum_{u>=t} g_u dD_u
+ *   dk_t = (R_t v_t + r_t) * phi'(k_t),  dv_t = R_t^T f_t     (reverse sweep)
+ *   dz_in = R_0,  ds_in = r_0
+ * (Segment-Wise Attention discusses detaching the carried memory from the
+ * graph: that is dz_out = ds_out = NULL and ignoring dz_in, ds_in.)
+ * dout, dq, dk, dv: [BH][N][d]; dz_* [BH][d][d]; ds_* [BH][d]; dz_in / ds_in
+ * may be NULL.
+ */
+void oracle_causal_bwd(long BH, long N, long d, double eps,
+                       const float *q, const float *k, const float *v, const float *dout,
+                       const double *z_in, const double *s_in,
+                       const double *dz_out, const double *ds_out,
+                       double *dq, double *dk, double *dv, double *dz_in, double *ds_in)
+{
+    long h;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (h = 0; h < BH; ++h) {
+        double *Z = (double *)calloc((size_t)(d * d), sizeof(double));
+        double *S = (double *)calloc((size_t)d, sizeof(double));
+        double *R = (double *)calloc((size_t)(d * d), sizeof(double));
+        double *r = (double *)calloc((size_t)d, sizeof(double));
+        double *dn = (double *)malloc((size_t)(N * d + 1) * sizeof(double));
+        double *dD = (double *)malloc((size_t)(N + 1) * sizeof(double));
+        double *f = (double *)malloc((size_t)d * sizeof(double));
+        double *g = (double *)malloc((size_t)d * sizeof(double));
+        double *o = (double *)malloc((size_t)d * sizeof(double));
+        long t, j, c;
+        if (z_in) memcpy(Z, z_in + h * d * d, (size_t)(d * d) * sizeof(double));
+        if (s_in) memcpy(S, s_in + h * d, (size_t)d * sizeof(double));
+        /* forward sweep: the state after token t, the output, dq_t */
+        for (t = 0; t < N; ++t) {
+            const float *kt = k + (h * N + t) * d, *vt = v + (h * N + t) * d;
+            const float *qt = q + (h * N + t) * d, *dot = dout + (h * N + t) * d;
+            double den = 0.0, dodo = 0.0;
+            for (j = 0; j < d; ++j) f[j] = phi((double)kt[j]);
+            for (j = 0; j < d; ++j) {
+                for (c = 0; c < d; ++c) Z[j * d + c] += f[j] * (double)vt[c];
+                S[j] += f[j];
+            }
+            for (j = 0; j < d; ++j) g[j] = phi((double)qt[j]);
+            for (j = 0; j < d; ++j) den += g[j] * S[j];
+            den += eps;
+            for (c = 0; c < d; ++c) {
+                double num = 0.0;
+                for (j = 0; j < d; ++j) num += g[j] * Z[j * d + c];
+                o[c] = num / den;
+                dodo += (double)dot[c] * o[c];
+            }
+            dD[t] = -dodo / den;
+            for (c = 0; c < d; ++c) dn[t * d + c] = (double)dot[c] / den;
+            for (j = 0; j < d; ++j) {
+                double acc = S[j] * dD[t];
+                for (c = 0; c < d; ++c) acc += Z[j * d + c] * dn[t * d + c];
+                dq[(h * N + t) * d + j] = acc * dphi((double)qt[j]);
+            }
+        }
+        /* reverse sweep: the adjoint state R_t, r_t (token t included), dk_t, dv_t */
+        if (dz_out) memcpy(R, dz_out + h * d * d, (size_t)(d * d) * sizeof(double));
+        if (ds_out) memcpy(r, ds_out + h * d, (size_t)d * sizeof(double));
+        for (t = N - 1; t >= 0; --t) {
+            const float *kt = k + (h * N + t) * d, *vt = v + (h * N + t) * d;
+            const float *qt = q + (h * N + t) * d;
+            for (j = 0; j < d; ++j) g[j] = phi((double)qt[j]);
+            for (j = 0; j < d; ++j) {
+                for (c = 0; c < d; ++c) R[j * d + c] += g[j] * dn[t * d + c];
+                r[j] += g[j] * dD[t];
+            }
+            for (j = 0; j < d; ++j) f[j] = phi((double)kt[j]);
+            for (j = 0; j < d; ++j) {
+                double acc = r[j];
+                for (c = 0; c < d; ++c) acc += R[j * d + c] * (double)vt[c];
+                dk[(h * N + t) * d + j] = acc * dphi((double)kt[j]);
+            }
+            for (c = 0; c < d; ++c) {
+                double acc = 0.0;
+                for (j = 0; j < d; ++j) acc += R[j * d + c] * f[j];
+                dv[(h * N + t) * d + c] = acc;
+            }
+        }
+        if (dz_in) memcpy(dz_in + h * d * d, R, (size_t)(d * d) * sizeof(double));
+        if (ds_in) memcpy(ds_in + h * d, r, (size_t)d * sizeof(double));
+        free(Z); free(S); free(R); free(r); free(dn); free(dD); free(f); free(g); free(o);
+    }
+}

@@ -20,7 +20,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = [
-    "LinAttnError", "LA_F32", "LA_BF16", "LA_WS_INPLACE_STATE",
+    "LinAttnError", "LA_F32", "LA_BF16", "STATUS",
     "library_path", "load_library",
     "la_status_str", "la_version",
     "la_causal_fwd_workspace", "la_causal_fwd", "la_causal_fwd_unnormalized",
@@ -36,7 +36,10 @@ _LIBPATH = os.path.join(_HERE, "liblinattn.so")
 _lib = None
 
 LA_F32, LA_BF16 = 0, 1
-LA_WS_INPLACE_STATE = 1
+# la_status values of linattn.h
+STATUS = {"LA_OK": 0, "LA_ERR_NULL": -1, "LA_ERR_SHAPE": -2, "LA_ERR_DTYPE": -3, "LA_ERR_ALIGN": -4,
+          "LA_ERR_UNSUPPORTED": -5, "LA_ERR_WORKSPACE": -6, "LA_ERR_LAUNCH": -7, "LA_ERR_VALUE": -8,
+          "LA_ERR_ALIAS": -9}
 
 
 class LinAttnError(RuntimeError):
@@ -67,7 +70,7 @@ def load_library():
     lib.la_status_str.restype = ctypes.c_char_p
     lib.la_version.argtypes = []
     lib.la_version.restype = i32
-    lib.la_causal_fwd_workspace.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.la_causal_fwd_workspace.argtypes = [i32, i32, i32, i32, i32]
     lib.la_causal_fwd_workspace.restype = sz
     lib.la_causal_fwd.argtypes = [vp, S, vp, S, vp, S, i32, vp, S, i32, i32, i32, i32, i32, f32,
                                   vp, vp, vp, vp, vp, sz, vp]
@@ -76,11 +79,11 @@ def load_library():
     lib.la_causal_fwd_unnormalized.restype = i32
     lib.la_decode_step.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, f32, vp]
     lib.la_decode_step.restype = i32
-    lib.la_noncausal_workspace.argtypes = [i32, i32, i32, i32, i32]
+    lib.la_noncausal_workspace.argtypes = [i32, i32, i32, i32]
     lib.la_noncausal_workspace.restype = sz
     lib.la_noncausal_fwd.argtypes = [vp, S, vp, S, vp, S, i32, vp, S, i32, i32, i32, i32, f32, vp, sz, vp]
     lib.la_noncausal_fwd.restype = i32
-    lib.la_memory_workspace.argtypes = [i32, i32, i32, i32, i32]
+    lib.la_memory_workspace.argtypes = [i32, i32, i32, i32]
     lib.la_memory_workspace.restype = sz
     lib.la_memory_fwd.argtypes = [vp, S, vp, S, vp, S, i32, vp, S, i32, i32, i32, i32, f32,
                                   vp, vp, vp, vp, vp, sz, vp]
@@ -131,24 +134,22 @@ def la_version() -> int:
 
 
 @functools.lru_cache(maxsize=4096)
-def _causal_ws(B, H, N, d, code, chunk, flags) -> int:
-    return int(load_library().la_causal_fwd_workspace(B, H, N, d, code, chunk, flags))
+def la_causal_fwd_workspace(B: int, H: int, N: int, d: int, chunk: int = 0) -> int:
+    """Workspace bytes of la_causal_fwd / la_causal_fwd_unnormalized (0 for
+    arguments the call would reject)."""
+    return int(load_library().la_causal_fwd_workspace(B, H, N, d, chunk))
 
 
 @functools.lru_cache(maxsize=4096)
-def _noncausal_ws(B, H, N, d, code) -> int:
-    return int(load_library().la_noncausal_workspace(B, H, N, d, code))
+def la_noncausal_workspace(B: int, H: int, N: int, d: int) -> int:
+    """Workspace bytes of la_noncausal_fwd."""
+    return int(load_library().la_noncausal_workspace(B, H, N, d))
 
 
 @functools.lru_cache(maxsize=4096)
-def _memory_ws(B, H, N, d, code) -> int:
-    return int(load_library().la_memory_workspace(B, H, N, d, code))
-
-
-def la_causal_fwd_workspace(B: int, H: int, N: int, d: int, dtype: torch.dtype,
-                            chunk: int = 0, inplace_state: bool = False) -> int:
-    code = LA_F32 if dtype == torch.float32 else LA_BF16
-    return _causal_ws(B, H, N, d, code, chunk, LA_WS_INPLACE_STATE if inplace_state else 0)
+def la_memory_workspace(B: int, H: int, N: int, d: int) -> int:
+    """Workspace bytes of la_memory_fwd."""
+    return int(load_library().la_memory_workspace(B, H, N, d))
 
 
 class Prepared:
@@ -185,35 +186,35 @@ def prepare_causal_fwd(q, k, v, out=None, *, chunk: int = 0, eps: float = 1e-6,
     normalize=False marshals la_causal_fwd_unnormalized instead (same arguments).
 
     q, k, v: [B, H, N, d] bf16 or fp32 CUDA tensors (any strides with unit d stride).
-    out: float32 [B, H, N, d] or None (state only).  States: float32 contiguous
-    [B, H, d, d] / [B, H, d]; z_out/s_out may be the z_in/s_in tensors themselves.
-    A workspace of la_causal_fwd_workspace() bytes is allocated if none is given.
+    out: float32 [B, H, N, d] or None (state only; then q may be None).  States:
+    float32 contiguous [B, H, d, d] / [B, H, d]; z_out/s_out may be the z_in/s_in
+    tensors themselves.  A workspace of la_causal_fwd_workspace() bytes is
+    allocated if none is given.
     """
-    B, H, N, d = q.shape
-    if tuple(k.shape) != (B, H, N, d) or tuple(v.shape) != (B, H, N, d):
+    B, H, N, d = k.shape
+    if (q is not None and tuple(q.shape) != (B, H, N, d)) or tuple(v.shape) != (B, H, N, d):
         raise ValueError("q, k, v must have the same shape")
-    if k.dtype != q.dtype or v.dtype != q.dtype:
+    if (q is not None and q.dtype != k.dtype) or v.dtype != k.dtype:
         raise TypeError("q, k, v must have the same dtype")
     if out is not None and (out.dtype != torch.float32 or tuple(out.shape) != (B, H, N, d)):
         raise ValueError("out must be float32 [B, H, N, d]")
     for t, shp, nm in ((z_in, (B, H, d, d), "z_in"), (z_out, (B, H, d, d), "z_out"),
                        (s_in, (B, H, d), "s_in"), (s_out, (B, H, d), "s_out")):
         _state_check(t, shp, nm)
-    inplace = (z_out is not None and z_in is not None and z_out.data_ptr() == z_in.data_ptr()) or \
-              (s_out is not None and s_in is not None and s_out.data_ptr() == s_in.data_ptr())
-    ws_bytes = la_causal_fwd_workspace(B, H, N, d, q.dtype, chunk, inplace)
+    ws_bytes = la_causal_fwd_workspace(B, H, N, d, chunk)
     if workspace is None and ws_bytes > 0:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=k.device)
     have = 0 if workspace is None else workspace.numel() * workspace.element_size()
     so = _strides(out) if out is not None else la_strides(0, 0, 0)
-    args = [_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v), _dtype_code(q),
+    sq = _strides(q) if q is not None else la_strides(0, 0, 0)
+    args = [_ptr(q), sq, _ptr(k), _strides(k), _ptr(v), _strides(v), _dtype_code(k),
             _ptr(out), so, B, H, N, d, int(chunk), ctypes.c_float(eps),
             _ptr(z_in), _ptr(s_in), _ptr(z_out), _ptr(s_out), _ptr(workspace), ctypes.c_size_t(have),
-            _opt_stream(stream, q.device)]
+            _opt_stream(stream, k.device)]
     lib = load_library()
     fn, name = (lib.la_causal_fwd, "la_causal_fwd") if normalize else \
         (lib.la_causal_fwd_unnormalized, "la_causal_fwd_unnormalized")
-    return Prepared(fn, args, q.device, name, (q, k, v, out, z_in, s_in, z_out, s_out, workspace))
+    return Prepared(fn, args, k.device, name, (q, k, v, out, z_in, s_in, z_out, s_out, workspace))
 
 
 def la_causal_fwd(q, k, v, out=None, *, chunk: int = 0, eps: float = 1e-6,
@@ -257,11 +258,6 @@ def la_decode_step(q, k, v, z, s, out, *, eps: float = 1e-6, stream=None) -> Non
     prepare_decode_step(q, k, v, z, s, out, eps=eps, stream=stream)()
 
 
-def la_noncausal_workspace(B: int, H: int, N: int, d: int, dtype: torch.dtype) -> int:
-    code = LA_F32 if dtype == torch.float32 else LA_BF16
-    return _noncausal_ws(B, H, N, d, code)
-
-
 def prepare_noncausal_fwd(q, k, v, out, *, eps: float = 1e-6,
                           workspace: Optional[torch.Tensor] = None, stream=None) -> Prepared:
     """Check and marshal a la_noncausal_fwd call (nothing runs until it is called)."""
@@ -272,7 +268,7 @@ def prepare_noncausal_fwd(q, k, v, out, *, eps: float = 1e-6,
         raise TypeError("q, k, v must have the same dtype")
     if out.dtype != torch.float32 or tuple(out.shape) != (B, H, N, d):
         raise ValueError("out must be float32 [B, H, N, d]")
-    ws_bytes = la_noncausal_workspace(B, H, N, d, q.dtype)
+    ws_bytes = la_noncausal_workspace(B, H, N, d)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     have = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -286,11 +282,6 @@ def la_noncausal_fwd(q, k, v, out, *, eps: float = 1e-6,
                      workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """Non-causal linear attention forward (la_noncausal_fwd in linattn.h)."""
     prepare_noncausal_fwd(q, k, v, out, eps=eps, workspace=workspace, stream=stream)()
-
-
-def la_memory_workspace(B: int, H: int, N: int, d: int, dtype: torch.dtype) -> int:
-    code = LA_F32 if dtype == torch.float32 else LA_BF16
-    return _memory_ws(B, H, N, d, code)
 
 
 def prepare_memory_fwd(q, k, v, out=None, *, eps: float = 1e-6,
@@ -312,7 +303,7 @@ def prepare_memory_fwd(q, k, v, out=None, *, eps: float = 1e-6,
     for t, shp, nm in ((z_in, (B, H, d, d), "z_in"), (z_out, (B, H, d, d), "z_out"),
                        (s_in, (B, H, d), "s_in"), (s_out, (B, H, d), "s_out")):
         _state_check(t, shp, nm)
-    ws_bytes = la_memory_workspace(B, H, N, d, q.dtype)
+    ws_bytes = la_memory_workspace(B, H, N, d)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     have = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -47,7 +47,9 @@
 #include <time.h>
 #include <unistd.h>
 
+#include <algorithm>
 #include <atomic>
+#include <stdlib.h>
 
 #include "linattn.h"
 
@@ -152,6 +154,9 @@ struct Args {
     // set to `epoch` (unique per call) when that group's slot is published
     unsigned long long *flags;
     unsigned long long epoch;
+    unsigned long long wait_tag;   // the tag waits look for (== epoch)
+    int spin_limit;                // polls before a wait gives up
+    unsigned *giveups;             // counter of waits that gave up (workspace offset 0)
     int wait_s;   // s_out is s_in and shared by P > 1 column blocks
     int unnorm;   // causal outputs without the normaliser (numerators only)
 };
@@ -829,43 +834,44 @@ template <int D, int DV> struct FSlot {
     __device__ static uint32_t soff(int jt, int g) { return (uint32_t)((ZF + 16 * jt + 4 * g) * 4); }
 };
 
-// chunks of a register-resident group whose phi(K) split is held from the
-// group's own-state step to the chunk loop (registers permitting)
-#ifndef LA_KEEP_SPLIT
-#define LA_KEEP_SPLIT 0
-#endif
-
-// bf16 causal calls with output and register-resident groups run the
-// column-split kernel (k_cs_fwd) where it is instantiated
-#ifndef LA_COLUMN_SPLIT
-#define LA_COLUMN_SPLIT 1
-#endif
-
 // Spin limit of a flag wait (a poll is a memory round trip plus a short
 // sleep): a call whose flags never arrive (a bug, or memory not meant for
 // this call) ends instead of hanging.
 constexpr int SPIN_LIMIT = 1 << 20;
 
 // A flag holds the call's tag (low 4 bits zero) plus the XCD index of the
-// workgroup that set it.  Wait until base[i * stride] carries `epoch` for
-// i < n (lane i watches entry i, in rounds of 64 entries); returns whether
-// all of them were set on XCD `xcc`.  Every lane of the wave runs this.
+// workgroup that set it.  Wait until base[i * stride] carries `tag` for
+// i < n (lane i watches entry i, in rounds of 64 entries), at most
+// `spin_limit` polls per round.  Returns whether all of them were set on XCD
+// `xcc`; `ok` is false if the wait gave up.  Every lane of the wave runs
+// this, and the results are wave-uniform.
 __device__ __forceinline__ bool wait_flags(const unsigned long long *base, int stride, int n,
-                                           unsigned long long epoch, unsigned xcc, int lane)
+                                           unsigned long long tag, unsigned xcc, int lane, int spin_limit,
+                                           bool &ok)
 {
     bool local = true;
+    ok = true;
     for (int i0 = 0; i0 < n; i0 += WAVE) {
         const int i = i0 + lane;
         const unsigned long long *f = base + (int64_t)(i < n ? i : 0) * stride;
         unsigned long long v = 0;
-        for (int spin = 0; spin < SPIN_LIMIT; ++spin) {
+        bool seen = false;
+        for (int spin = 0; spin < spin_limit; ++spin) {
             v = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (__all(i >= n || (v & ~0xfull) == epoch)) break;
+            if (__all(i >= n || (v & ~0xfull) == tag)) { seen = true; break; }
             __builtin_amdgcn_s_sleep(2);
         }
+        ok = ok && seen;
         local = local && __all(i >= n || (v & 0xfull) == xcc);
     }
     return local;
+}
+
+// A wait that gave up: one lane of the wave counts it in the workspace's
+// counter (a vector atomic), and the caller poisons what it was summing.
+__device__ __forceinline__ void count_giveup(unsigned *ctr, int lane)
+{
+    if (lane == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The causal forward of one token group in a single pass (modes 3 and 4 of
@@ -880,7 +886,6 @@ __device__ __forceinline__ bool wait_flags(const unsigned long long *base, int s
 //     P = phi(Q_c) phi(K_c)^T, then Z += phi(K_c)^T V_c, S += phi(K_c)^T 1 on
 //     the owned state tiles, published to LDS for the next chunk; the last
 //     group writes z_out/s_out.
-// MODE_STATE (no output) stops after A and B: the last group writes the sum.
 // MODE_APPLY (non-causal): out_t = phi(q_t) Z / (phi(q_t) . S + eps) with the
 // reduced global state.
 // Waiting in B is only on groups with lower workgroup indices of the same XCD
@@ -890,7 +895,7 @@ __device__ __forceinline__ bool wait_flags(const unsigned long long *base, int s
 // row of Z^T and an all-ones row is an extra row of V^T, so an extra 16-row
 // output tile (whose other rows are zero operands) accumulates
 // phi(q_t) . S_prev + sum_s P_ts in its first row.
-constexpr int MODE_OUT = 0, MODE_STATE = 1, MODE_APPLY = 2;
+constexpr int MODE_OUT = 0, MODE_APPLY = 2;
 
 // CPG > 0 (MODE_OUT only): the group has at most CPG chunks, and all of its
 // q, k, v loads are issued at the start into registers; steps A and C then
@@ -968,12 +973,13 @@ __global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F
     };
 
     // ---- slot helpers: add the published slots of groups 0..n-1 of this
-    // (head, column block); write z_out / s_out from (Zown + Zadd, Sown + Sadd)
+    // (head, column block); write z_out / s_out from (Zown, Sown)
     // (slots written on this workgroup's XCD are read from its L2; others
     // from memory)
     const unsigned my_xcc = xcc_id();
     auto add_slots = [&](int n) {
-        const bool local = wait_flags(a.flags + (int64_t)hp * a.G, 1, n, a.epoch, my_xcc, lane);
+        bool ok;
+        const bool local = wait_flags(a.flags + (int64_t)hp * a.G, 1, n, a.wait_tag, my_xcc, lane, a.spin_limit, ok);
         constexpr int LB = (G_::ZT + G_::SMAX) <= 5 ? 4 : 2;   // slots in flight
         const char *base = (const char *)a.part + (size_t)hp * a.G * FS::BYTES;
         auto sum = [&](auto cpol) {
@@ -1003,6 +1009,13 @@ __global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F
         };
         if (local) sum(IC<CPOL_XCD>{});
         else sum(IC<CPOL_DEVICE>{});
+        if (!ok) {   // the earlier groups' state is unknown: poison it
+            count_giveup(a.giveups, lane);
+#pragma unroll
+            for (int m = 0; m < G_::ZT; ++m) Zown[m] = (f32x4){NAN, NAN, NAN, NAN};
+#pragma unroll
+            for (int m = 0; m < G_::SMAX; ++m) Sown[m] = (f32x4){NAN, NAN, NAN, NAN};
+        }
     };
     // this group's slot <- (za, sa), plus (Zown, Sown) if `add`
     auto publish_slot = [&](const f32x4 *za, const f32x4 *sa, bool add) {
@@ -1023,19 +1036,22 @@ __global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F
             __hip_atomic_store(a.flags + (int64_t)hp * a.G + grp, a.epoch | my_xcc, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     };
-    auto store_final = [&](const f32x4 *Zadd, const f32x4 *Sadd) {
+    auto store_final = [&]() {
         // s_out is written by the last column block; with in-place states it
         // first waits until group 0 of every column block has read s_in
         const bool s_writer = p == a.P - 1;
-        if (a.wait_s && s_writer) (void)wait_flags(a.flags + (int64_t)bh * a.P * a.G, a.G, a.P, a.epoch, my_xcc, lane);
-        f32x4 zf[G_::ZT], sf[G_::SMAX];
+        bool s_ok = true;
+        if (a.wait_s && s_writer) {
+            (void)wait_flags(a.flags + (int64_t)bh * a.P * a.G, a.G, a.P, a.wait_tag, my_xcc, lane, a.spin_limit, s_ok);
+            if (!s_ok) count_giveup(a.giveups, lane);
+        }
+        if (!s_ok) {   // s_in may not have been read yet: poison s_out
 #pragma unroll
-        for (int m = 0; m < G_::ZT; ++m) zf[m] = Zadd ? Zown[m] + Zadd[m] : Zown[m];
-#pragma unroll
-        for (int m = 0; m < G_::SMAX; ++m) sf[m] = Sadd ? Sown[m] + Sadd[m] : Sown[m];
+            for (int m = 0; m < G_::SMAX; ++m) Sown[m] = (f32x4){NAN, NAN, NAN, NAN};
+        }
         store_owned<JT, CT, G_::ZT, G_::SMAX>(a.z_out ? a.z_out + (int64_t)bh * D * D + p * DV : nullptr, D,
                                               (a.s_out && s_writer) ? a.s_out + (int64_t)bh * D : nullptr,
-                                              w, r, g, zf, sf);
+                                              w, r, g, Zown, Sown);
     };
 
     // ---- per-chunk pieces of the output
@@ -1200,17 +1216,13 @@ __global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F
 
     // ---- one chunk of the streaming loop (and of the non-causal readout):
     // stage K, V and phi(q); the output rows; the state update
-    // (resident bf16 groups: phi(K) is split in registers once; `split_done`
-    // says the group's own-state step already did it)
-    bool split_done = false;
+    // (resident bf16 groups: phi(K) is split into hi + lo in registers, then
+    // copied to LDS; the own-state step's split is not held, register budget)
     auto step = [&](int ch, auto slot) {
         constexpr int S_ = decltype(slot)::value;
         const int t0 = t_begin + ch * C;
         if constexpr (RES && !F32) {
-            // the split of the first KEEP chunks is held from the group's own-
-            // state step; later ones are split again (register budget)
-            constexpr int KEEP = LA_KEEP_SPLIT;
-            if (!split_done || S_ >= KEEP) R[S_].phi_split(tid, min(C, t_end - t0));
+            R[S_].phi_split(tid, min(C, t_end - t0));
             R[S_].stage(tid, sm);
         } else if (CAUSAL) {
             R[S_].fill(tid, sm, min(C, t_end - t0));
@@ -1289,7 +1301,6 @@ __global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F
                 });
                 publish_slot(Zown, Sown, false);
                 set_flag();
-                split_done = true;
             } else {
                 issue_rest();
                 if (grp == 0 && a.wait_s) set_flag();   // only signals that z_in / s_in have been read
@@ -1312,13 +1323,12 @@ __global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F
             static_for<CPG>([&](auto c) {
                 if (c.value < nch) step(c.value, c);
             });
-            if (last) store_final(nullptr, nullptr);
+            if (last) store_final();
             return;
         } else {
             // ================= streamed group: A, B, C as described above
             const bool publish = !last;
-            const bool need_a = publish || MODE == MODE_STATE;
-            if (need_a) {
+            if (publish) {
                 if (grp == 0) {
 #pragma unroll
                     for (int m = 0; m < G_::ZT; ++m) Zown[m] = Zin[m];
@@ -1349,32 +1359,24 @@ __global__ void __launch_bounds__(NTHR, CPG > 0 ? res_minwg(F32, D) : minwg_of(F
                     step_a(i, IC<0>{});
                     step_a(i + 1, IC<1>{});
                 }
-                if (publish) publish_slot(Zown, Sown, false);
+                publish_slot(Zown, Sown, false);
             }
             // group 0 also signals that it has read z_in / s_in (in-place states)
             if (publish || (grp == 0 && a.wait_s)) set_flag();
-            if constexpr (MODE == MODE_STATE) {
-                if (last) {
-                    add_slots(grp);
-                    store_final(nullptr, nullptr);
-                }
-                return;
+            issue(0, IC<0>{});   // the first chunk's loads overlap the look-back
+            if (grp == 0) {
+#pragma unroll
+                for (int m = 0; m < G_::ZT; ++m) Zown[m] = Zin[m];
+#pragma unroll
+                for (int m = 0; m < G_::SMAX; ++m) Sown[m] = Sin[m];
             } else {
-                issue(0, IC<0>{});   // the first chunk's loads overlap the look-back
-                if (grp == 0) {
-#pragma unroll
-                    for (int m = 0; m < G_::ZT; ++m) Zown[m] = Zin[m];
-#pragma unroll
-                    for (int m = 0; m < G_::SMAX; ++m) Sown[m] = Sin[m];
-                } else {
-                    zero_state();
-                    add_slots(grp);
-                }
-                publish_state<F32, D, DV, C>(sm, w, r, g, Zown, Sown);
-                static_assert(DEPTH == 1, "one chunk of loads in flight");
-                for (int ch = 0; ch < nch; ++ch) step(ch, IC<0>{});
-                if (last) store_final(nullptr, nullptr);
+                zero_state();
+                add_slots(grp);
             }
+            publish_state<F32, D, DV, C>(sm, w, r, g, Zown, Sown);
+            static_assert(DEPTH == 1, "one chunk of loads in flight");
+            for (int ch = 0; ch < nch; ++ch) step(ch, IC<0>{});
+            if (last) store_final();
         }
     }
 }
@@ -1787,7 +1789,8 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
     auto look_back = [&]() __attribute__((always_inline)) {
         __syncthreads();   // every wave is done with chunk 0's S operands (buffer 0)
         load_state(Ze, Se, nullptr, nullptr);
-        const bool local = wait_flags(a.flags + (int64_t)hp * a.G, 1, grp, a.epoch, my_xcc, lane);
+        bool ok;
+        const bool local = wait_flags(a.flags + (int64_t)hp * a.G, 1, grp, a.wait_tag, my_xcc, lane, a.spin_limit, ok);
         constexpr int LB = JT <= 4 ? 4 : 2;   // slots in flight (register budget)
         const char *base = (const char *)a.part + (size_t)hp * a.G * FS::BYTES;
         auto sum = [&](auto cpol) __attribute__((always_inline)) {
@@ -1814,6 +1817,13 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
         };
         if (local) sum(IC<CPOL_XCD>{});
         else sum(IC<CPOL_DEVICE>{});
+        if (!ok) {   // the earlier groups' state is unknown: poison it
+            count_giveup(a.giveups, lane);
+#pragma unroll
+            for (int jt = 0; jt < JT; ++jt) Ze[jt] = (f32x4){NAN, NAN, NAN, NAN};
+#pragma unroll
+            for (int m = 0; m < SPW; ++m) Se[m] = (f32x4){NAN, NAN, NAN, NAN};
+        }
         put_sops(Se, 0);
         __syncthreads();
         bf16x8 zh[KS], zl[KS];
@@ -2089,7 +2099,15 @@ __global__ void __launch_bounds__(NTHR, 2) k_cs_fwd(const Args a)
     });
     // ---- the final state (last group): the running state after the last chunk
     if (last) {
-        if (a.wait_s && s_writer) (void)wait_flags(a.flags + (int64_t)bh * a.P * a.G, a.G, a.P, a.epoch, my_xcc, lane);
+        if (a.wait_s && s_writer) {
+            bool ok;
+            (void)wait_flags(a.flags + (int64_t)bh * a.P * a.G, a.G, a.P, a.wait_tag, my_xcc, lane, a.spin_limit, ok);
+            if (!ok) {   // s_in may not have been read yet: poison s_out
+                count_giveup(a.giveups, lane);
+#pragma unroll
+                for (int m = 0; m < SPW; ++m) S[m] = (f32x4){NAN, NAN, NAN, NAN};
+            }
+        }
         float *zo = a.z_out ? a.z_out + (int64_t)bh * D * D + p * DV + 16 * w + r : nullptr;
         float *so = (a.s_out && s_writer && r == 0) ? a.s_out + (int64_t)bh * D : nullptr;
 #pragma unroll
@@ -2629,19 +2647,16 @@ struct Plan {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Token groups: enough workgroups to cover the chip, each group a whole
-// number of chunks, at most LA_MAX_GROUPS groups per head.
-#ifndef LA_MAX_GROUPS
-#define LA_MAX_GROUPS 32
-#endif
-#ifndef LA_CAUSAL_TARGET_WGS
-#define LA_CAUSAL_TARGET_WGS 512
-#endif
+// number of chunks, at most MAX_GROUPS groups per head.
+constexpr int MAX_GROUPS = 32;
+constexpr int CAUSAL_TARGET_WGS = 512;
 // The last group of a causal call reads the slots of all earlier groups of its
 // (head, column block): at most this many bytes.
-#ifndef LA_LOOKBACK_BYTES
-#define LA_LOOKBACK_BYTES (256 * 1024)
-#endif
-int pick_groups(int64_t units, int N, int C, int target, int max_groups = LA_MAX_GROUPS)
+constexpr size_t LOOKBACK_BYTES = 256 * 1024;
+// A causal workspace starts with a status block: the 32-bit count of flag
+// waits that gave up, at byte offset 0.  The slots and flags follow it.
+constexpr size_t STATUS_BYTES = 256;
+int pick_groups(int64_t units, int N, int C, int target, int max_groups = MAX_GROUPS)
 {
     if (N <= 0) return 1;
     int64_t maxg = (N + C - 1) / C;
@@ -2660,11 +2675,9 @@ void set_groups(Plan &pl, int N)
     pl.G = N > 0 ? (int)((N + pl.L - 1) / pl.L) : 1;
 }
 
-// want_out: the output is computed (else state only).  inplace: z_out/s_out
-// equal z_in/s_in.
-// Single-pass causal plan: G token groups per (head, column block), one slot
-// and one flag per group.
-Plan plan_causal(int B, int H, int N, int d, la_dtype dt, int chunk, bool want_out)
+// Single-pass causal plan (calls with outputs): G token groups per (head,
+// column block), one slot and one flag per group, after the status block.
+Plan plan_causal(int B, int H, int N, int d, la_dtype dt, int chunk)
 {
     Plan pl;
     pl.C = pick_chunk(dt == LA_F32, d, chunk);
@@ -2672,18 +2685,17 @@ Plan plan_causal(int B, int H, int N, int d, la_dtype dt, int chunk, bool want_o
     pl.P = d / pl.DV;
     const int64_t BH = (int64_t)B * H;
     pl.slot_floats = (size_t)pl.DV * d + d;
-    int max_g = 1 + (int)(LA_LOOKBACK_BYTES / (pl.slot_floats * 4));
+    int max_g = 1 + (int)(LOOKBACK_BYTES / (pl.slot_floats * 4));
     // the column-split kernel at d = 128 holds 2 chunks per group: allow the
     // 16 groups that give it a full grid
-    if (LA_COLUMN_SPLIT && want_out && dt == LA_BF16 && d == 128 && pl.C == 64 && max_g < 16) max_g = 16;
-    pl.G = pick_groups(BH * pl.P, N, pl.C, want_out ? LA_CAUSAL_TARGET_WGS : 2 * LA_CAUSAL_TARGET_WGS,
-                       max_g < LA_MAX_GROUPS ? max_g : LA_MAX_GROUPS);
+    if (dt == LA_BF16 && d == 128 && pl.C == 64 && max_g < 16) max_g = 16;
+    pl.G = pick_groups(BH * pl.P, N, pl.C, CAUSAL_TARGET_WGS, max_g < MAX_GROUPS ? max_g : MAX_GROUPS);
     set_groups(pl, N);
     pl.NS = N > 0 ? pl.G : 0;
     pl.part_bytes = pl.G > 1 ? align256((size_t)BH * pl.P * pl.G * pl.slot_floats * 4) : 0;
-    pl.fin_off = pl.part_bytes;
+    pl.fin_off = STATUS_BYTES + pl.part_bytes;
     pl.fin_bytes = 0;
-    pl.flags_off = pl.part_bytes;
+    pl.flags_off = STATUS_BYTES + pl.part_bytes;
     pl.total = N > 0 ? pl.flags_off + align256((size_t)BH * pl.P * pl.G * 8) : 0;
     return pl;
 }
@@ -2722,6 +2734,16 @@ Plan plan_noncausal(int B, int H, int N, int d, la_dtype dt, int target = 1024)
     return pl;
 }
 
+// State-only causal calls (out = NULL, the prefill): the non-causal partial
+// states of the token shares, then their sum added to the carried-in state.
+Plan plan_state(int B, int H, int N, int d, la_dtype dt)
+{
+    Plan pl = plan_noncausal(B, H, N, d, dt);
+    pl.fin_bytes = 0;
+    pl.total = N > 0 ? pl.part_bytes : 0;
+    return pl;
+}
+
 // ---- kernel dispatch tables (dtype x d x chunk)
 template <bool F32, int D, int C>
 void launch_dc(int what, const Args &a, int nwg, hipStream_t st)
@@ -2731,7 +2753,6 @@ void launch_dc(int what, const Args &a, int nwg, hipStream_t st)
         if (what == 0) hipLaunchKernelGGL((k_group_state<F32, D, DV, C>), dim3(nwg), dim3(NTHR), 0, st, a);
         else if (what == 1) hipLaunchKernelGGL((k_chunk_fwd<F32, D, DV, C, MODE_OUT, 0>), dim3(nwg), dim3(NTHR), 0, st, a);
         else if (what == 2) hipLaunchKernelGGL((k_chunk_fwd<F32, D, DV, C, MODE_APPLY, 0>), dim3(nwg), dim3(NTHR), 0, st, a);
-        else if (what == 3) hipLaunchKernelGGL((k_chunk_fwd<F32, D, DV, C, MODE_STATE, 0>), dim3(nwg), dim3(NTHR), 0, st, a);
         else if constexpr (C == 64)
             hipLaunchKernelGGL((k_chunk_fwd<F32, D, DV, C, MODE_OUT, res_cpg(F32, D)>), dim3(nwg), dim3(NTHR), 0, st, a);
     }
@@ -2829,7 +2850,9 @@ const char *la_status_str(la_status s)
     case LA_ERR_SHAPE: return "LA_ERR_SHAPE: negative or too large size or stride";
     case LA_ERR_DTYPE: return "LA_ERR_DTYPE: dtype must be LA_F32 or LA_BF16";
     case LA_ERR_ALIGN: return "LA_ERR_ALIGN: pointers and strides must be 16-byte aligned";
-    case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED: d must be 32, 64 or 128 and chunk 0, 16, 32, 64 or 128";
+    case LA_ERR_UNSUPPORTED:
+        return "LA_ERR_UNSUPPORTED: d must be 32, 64 or 128 and chunk 0, 16, 32, 64 or 128, and a causal call "
+               "with outputs cannot be captured into a HIP graph";
     case LA_ERR_VALUE: return "LA_ERR_VALUE: eps must be finite and >= 0";
     case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE: workspace missing or too small";
     case LA_ERR_ALIAS: return "LA_ERR_ALIAS: output state overlaps an input state";
@@ -2840,16 +2863,17 @@ const char *la_status_str(la_status s)
 
 int la_version(void) { return 100; }
 
-size_t la_causal_fwd_workspace(int B, int H, int N, int d, la_dtype dt, int chunk, int flags)
+size_t la_causal_fwd_workspace(int B, int H, int N, int d, int chunk)
 {
-    if (check_common(B, H, N, d, dt, 0.f) != LA_OK) return 0;
+    if (check_common(B, H, N, d, LA_BF16, 0.f) != LA_OK) return 0;
     if (chunk != 0 && chunk != 16 && chunk != 32 && chunk != 64 && chunk != 128) return 0;
-    // the larger of the with-output and state-only plans (the flags argument
-    // is accepted for compatibility: in-place states need no extra space)
-    (void)flags;
-    Plan a = plan_causal(B, H, N, d, dt, chunk, true);
-    Plan b = plan_causal(B, H, N, d, dt, chunk, false);
-    return a.total > b.total ? a.total : b.total;
+    // the largest plan over both dtypes, with and without outputs
+    size_t total = 0;
+    for (la_dtype dt : {LA_F32, LA_BF16}) {
+        total = std::max(total, plan_causal(B, H, N, d, dt, chunk).total);
+        total = std::max(total, plan_state(B, H, N, d, dt).total);
+    }
+    return total;
 }
 
 }  // extern "C"
@@ -2870,7 +2894,8 @@ la_status causal_impl(const void *q, la_strides sq, const void *k, la_strides sk
     const bool want_out = out != nullptr;
     if (!want_out && !z_out && !s_out) return LA_ERR_NULL;
     if (N > 0) {
-        if ((st = check_tensor(q, sq, es)) != LA_OK) return st;
+        // a state-only call reads k and v only
+        if (want_out && (st = check_tensor(q, sq, es)) != LA_OK) return st;
         if ((st = check_tensor(k, sk, es)) != LA_OK) return st;
         if ((st = check_tensor(v, sv, es)) != LA_OK) return st;
         if (want_out && (st = check_tensor(out, so, 4)) != LA_OK) return st;
@@ -2884,7 +2909,7 @@ la_status causal_impl(const void *q, la_strides sq, const void *k, la_strides sk
     if (s_out && s_in && s_out != (float *)s_in && overlaps(s_out, sb, s_in, sb)) return LA_ERR_ALIAS;
     if (overlaps(z_out, zb, s_in, sb) || overlaps(s_out, sb, z_in, zb) || overlaps(z_out, zb, s_out, sb))
         return LA_ERR_ALIAS;
-    Plan pl = plan_causal(B, H, N, d, dt, chunk, want_out);
+    Plan pl = want_out ? plan_causal(B, H, N, d, dt, chunk) : plan_state(B, H, N, d, dt);
     if (ws_bytes < pl.total || (pl.total > 0 && !workspace)) return LA_ERR_WORKSPACE;
     if (BH == 0) return LA_OK;
 
@@ -2894,7 +2919,6 @@ la_status causal_impl(const void *q, la_strides sq, const void *k, la_strides sk
     a.z_in = z_in; a.s_in = s_in; a.z_out = z_out; a.s_out = s_out;
     a.unnorm = unnorm;
     a.P = pl.P; a.L = pl.L; a.NS = pl.NS; a.G = pl.G;
-    a.part = (float *)workspace;
     const bool f32 = dt == LA_F32;
 
     if (N == 0) {
@@ -2902,20 +2926,50 @@ la_status causal_impl(const void *q, la_strides sq, const void *k, la_strides sk
         launch_slots(d, a, BH, pl.P, 0, 1, stream);
         return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
     }
+    if (!want_out) {
+        // prefill: the partial states of the token shares (k and v only),
+        // then z_out = z_in + their sum in share order (each state element
+        // read and written by one thread, so in place is safe)
+        a.part = (float *)workspace;
+        a.slot0 = 0;
+        const unsigned nwg = (unsigned)(BH * pl.P * pl.G);
+        if (!f32 && (d == 64 || d == 128) && pl.C == 64) launch_cs_state(d, a, nwg, stream);
+        else dispatch(f32, d, pl.C, 0, a, (int)nwg, stream);
+        launch_slots(d, a, BH, pl.P, pl.G, 1, stream);
+        return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
+    }
+    // the look-back's tag is fixed here, so a captured graph would replay it
+    {
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        const hipError_t e = hipStreamIsCapturing(stream, &cap);
+        (void)hipGetLastError();
+        if ((e == hipSuccess && cap != hipStreamCaptureStatusNone) || e == hipErrorStreamCaptureImplicit)
+            return LA_ERR_UNSUPPORTED;
+    }
+    a.giveups = (unsigned *)workspace;
+    a.part = (float *)((char *)workspace + STATUS_BYTES);
     a.flags = (unsigned long long *)((char *)workspace + pl.flags_off);
     a.epoch = next_epoch();
+    a.wait_tag = a.epoch;
+    a.spin_limit = SPIN_LIMIT;
+    // test hook: every wait looks for a tag that no workgroup stores and
+    // gives up after the given number of polls (the kernels still end)
+    if (const char *e = getenv("LA_TEST_LOOKBACK_TIMEOUT")) {
+        const int n = atoi(e);
+        if (n > 0) { a.wait_tag = a.epoch ^ 0x10ull; a.spin_limit = n; }
+    }
     a.wait_s = (s_out && s_out == s_in && pl.P > 1) ? 1 : 0;
     const bool resident = pl.C == 64 && pl.L <= res_cpg(f32, d) * pl.C;
     const int nwg = (int)(BH * pl.P * pl.G);
 #define LA_CS(DD, UN) hipLaunchKernelGGL((k_cs_fwd<DD, res_cpg(false, DD), UN>), dim3(nwg), dim3(NTHR), 0, stream, a)
-    if (LA_COLUMN_SPLIT && want_out && resident && !f32 && d == 64) {
+    if (resident && !f32 && d == 64) {
         if (unnorm) LA_CS(64, true); else LA_CS(64, false);
-    } else if (LA_COLUMN_SPLIT && want_out && resident && !f32 && d == 128) {
+    } else if (resident && !f32 && d == 128) {
         if (unnorm) LA_CS(128, true); else LA_CS(128, false);
     }
 #undef LA_CS
     else
-        dispatch(f32, d, pl.C, want_out ? (resident ? 4 : 1) : 3, a, nwg, stream);
+        dispatch(f32, d, pl.C, resident ? 4 : 1, a, nwg, stream);
     return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }
 }  // namespace
@@ -2969,10 +3023,10 @@ la_status la_decode_step(const void *q, const void *k, const void *v, la_dtype d
     return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }
 
-size_t la_noncausal_workspace(int B, int H, int N, int d, la_dtype dt)
+size_t la_noncausal_workspace(int B, int H, int N, int d)
 {
-    if (check_common(B, H, N, d, dt, 0.f) != LA_OK) return 0;
-    return plan_noncausal(B, H, N, d, dt).total;
+    if (check_common(B, H, N, d, LA_BF16, 0.f) != LA_OK) return 0;
+    return std::max(plan_noncausal(B, H, N, d, LA_F32).total, plan_noncausal(B, H, N, d, LA_BF16).total);
 }
 
 la_status la_noncausal_fwd(const void *q, la_strides sq, const void *k, la_strides sk,
@@ -3005,7 +3059,7 @@ la_status la_noncausal_fwd(const void *q, la_strides sq, const void *k, la_strid
     // 1) partial states of the token groups, 2) their sum per head in group
     // order, 3) every query against the global state
     a.G = pl.G; a.L = pl.L; a.slot0 = 0;
-    const bool cs = LA_COLUMN_SPLIT && !f32 && (d == 64 || d == 128) && pl.C == 64;
+    const bool cs = !f32 && (d == 64 || d == 128) && pl.C == 64;
     if (cs) launch_cs_state(d, a, (unsigned)(BH * pl.P * pl.G), stream);
     else dispatch(f32, d, pl.C, 0, a, (int)(BH * pl.P * pl.G), stream);
     launch_slots(d, a, BH, pl.P, pl.G, 2, stream);
@@ -3021,18 +3075,14 @@ la_status la_noncausal_fwd(const void *q, la_strides sq, const void *k, la_strid
 // fewer, longer token groups than the non-causal plan, so that a group's
 // published state does not outweigh its inputs, and shorter apply
 // workgroups, so that the readout still covers the chip.
-#ifndef LA_MEM_GROUP_TARGET
-#define LA_MEM_GROUP_TARGET 128
-#endif
-#ifndef LA_MEM_APPLY_CHUNKS
-#define LA_MEM_APPLY_CHUNKS 2
-#endif
-Plan plan_memory(int B, int H, int N, int d, la_dtype dt) { return plan_noncausal(B, H, N, d, dt, LA_MEM_GROUP_TARGET); }
+constexpr int MEM_GROUP_TARGET = 128;
+constexpr int MEM_APPLY_CHUNKS = 2;
+Plan plan_memory(int B, int H, int N, int d, la_dtype dt) { return plan_noncausal(B, H, N, d, dt, MEM_GROUP_TARGET); }
 
-size_t la_memory_workspace(int B, int H, int N, int d, la_dtype dt)
+size_t la_memory_workspace(int B, int H, int N, int d)
 {
-    if (check_common(B, H, N, d, dt, 0.f) != LA_OK) return 0;
-    return plan_memory(B, H, N, d, dt).total;
+    if (check_common(B, H, N, d, LA_BF16, 0.f) != LA_OK) return 0;
+    return std::max(plan_memory(B, H, N, d, LA_F32).total, plan_memory(B, H, N, d, LA_BF16).total);
 }
 
 // The non-causal kernels with the carried-in memory as the state that the
@@ -3084,7 +3134,7 @@ la_status la_memory_fwd(const void *q, la_strides sq, const void *k, la_strides 
     a.fin = want_out ? (float *)(ws + pl.fin_off) : nullptr;
     const bool f32 = dt == LA_F32;
     a.G = pl.G; a.L = pl.L; a.slot0 = 0;
-    const bool cs = LA_COLUMN_SPLIT && !f32 && (d == 64 || d == 128) && pl.C == 64;
+    const bool cs = !f32 && (d == 64 || d == 128) && pl.C == 64;
     if (cs && want_out) {
         // one launch: the partial states and the reads of the memory (two
         // workgroups per share), then the memory after the segment
@@ -3098,7 +3148,7 @@ la_status la_memory_fwd(const void *q, la_strides sq, const void *k, la_strides 
     else dispatch(f32, d, pl.C, 0, a, (int)(BH * pl.P * pl.G), stream);
     launch_slots(d, a, BH, pl.P, pl.G, 3, stream);
     if (want_out) {
-        const int la = pl.C * LA_MEM_APPLY_CHUNKS;
+        const int la = pl.C * MEM_APPLY_CHUNKS;
         a.L = la;
         a.G = (N + la - 1) / la;
         if (cs) launch_cs_apply(d, a, (unsigned)(BH * pl.P * a.G), stream);

@@ -5,6 +5,7 @@ No compute call is made here: every call below fails validation, which the
 library does before its first HIP call (fake, never dereferenced pointers).
 """
 import ctypes
+import os
 
 import pytest
 import torch
@@ -13,6 +14,10 @@ import segment_wise_compressive_amd as la
 from segment_wise_compressive_amd import la_strides
 
 FAKE = 0x10000000  # 16-byte aligned, never dereferenced
+# la_status values (linattn.h)
+NULL_, SHAPE, DTYPE, ALIGN, UNSUP, WS, LAUNCH, VALUE, ALIAS = (la.STATUS[n] for n in (
+    "LA_ERR_NULL", "LA_ERR_SHAPE", "LA_ERR_DTYPE", "LA_ERR_ALIGN", "LA_ERR_UNSUPPORTED", "LA_ERR_WORKSPACE",
+    "LA_ERR_LAUNCH", "LA_ERR_VALUE", "LA_ERR_ALIAS"))
 
 # Calls with fake pointers must never reach a device: these tests only run
 # where there is none.
@@ -35,22 +40,26 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, 10):
+    # the values of the header's enum, each with its own text
+    header = open(os.path.join(os.path.dirname(os.path.dirname(la.__file__)), "include", "linattn.h")).read()
+    for name, code in la.STATUS.items():
+        assert f"{name} = {code}" in header, name
         s = la.la_status_str(code)
-        assert s.startswith("LA_")
+        assert s.startswith(name), (name, s)
+    assert sorted(la.STATUS.values()) == list(range(-9, 1))
     assert "unknown" in la.la_status_str(99)
     assert la.la_version() >= 100
 
 
 def test_workspace_queries(lib):
-    assert la.la_causal_fwd_workspace(4, 8, 4096, 64, torch.bfloat16, 64) > 0
-    assert la.la_causal_fwd_workspace(4, 8, 4096, 48, torch.bfloat16, 64) == 0   # bad d
-    assert la.la_causal_fwd_workspace(4, 8, 4096, 64, torch.bfloat16, 24) == 0   # bad chunk
-    inplace = la.la_causal_fwd_workspace(1, 16, 2048, 128, torch.bfloat16, 0, True)
-    plain = la.la_causal_fwd_workspace(1, 16, 2048, 128, torch.bfloat16, 0, False)
-    assert inplace >= plain
-    assert la.la_noncausal_workspace(8, 16, 16384, 64, torch.bfloat16) > 0
-    assert la.la_noncausal_workspace(8, 16, 0, 64, torch.bfloat16) == 0
+    assert la.la_causal_fwd_workspace(4, 8, 4096, 64, 64) > 0
+    assert la.la_causal_fwd_workspace(4, 8, 4096, 48, 64) == 0   # bad d
+    assert la.la_causal_fwd_workspace(4, 8, 4096, 64, 24) == 0   # bad chunk
+    assert la.la_causal_fwd_workspace(4, 8, 0, 64) == 0          # N = 0 needs none
+    # the status block (give-up counter) comes first in every causal workspace
+    assert la.la_causal_fwd_workspace(1, 1, 1, 32) >= 256
+    assert la.la_noncausal_workspace(8, 16, 16384, 64) > 0
+    assert la.la_noncausal_workspace(8, 16, 0, 64) == 0
 
 
 def _causal(lib, **kw):
@@ -69,19 +78,21 @@ def _causal(lib, **kw):
 
 @no_device
 @pytest.mark.parametrize("kw, status", [
-    (dict(d=48), 5), (dict(d=16), 5), (dict(chunk=24), 5), (dict(chunk=256), 5),
-    (dict(dt=7), 3),
-    (dict(eps=-1.0), 6), (dict(eps=float("inf")), 6), (dict(eps=float("nan")), 6),
-    (dict(N=-1), 2), (dict(B=-1), 2),
-    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1),
-    (dict(out=None), 1),                                 # state only needs z_out or s_out
-    (dict(q=FAKE + 2), 4), (dict(out=FAKE + 0x300004), 4),
-    (dict(sq=la_strides(2 * 128 * 64, 128 * 64, 60)), 4),  # 120-byte row stride
-    (dict(sk=la_strides(-64, 0, 64)), 2),
-    (dict(ws=None), 7), (dict(ws_bytes=16), 7),
-    (dict(z_in=FAKE + 0x500000, z_out=FAKE + 0x500000 + 64), 8),   # partial overlap
-    (dict(s_in=FAKE + 0x500000, z_out=FAKE + 0x500000 - 256), 8),  # z_out runs into s_in
-    (dict(z_in=FAKE + 0x500008), 4),
+    (dict(d=48), UNSUP), (dict(d=16), UNSUP), (dict(chunk=24), UNSUP), (dict(chunk=256), UNSUP),
+    (dict(dt=7), DTYPE),
+    (dict(eps=-1.0), VALUE), (dict(eps=float("inf")), VALUE), (dict(eps=float("nan")), VALUE),
+    (dict(N=-1), SHAPE), (dict(B=-1), SHAPE),
+    (dict(q=None), NULL_), (dict(k=None), NULL_), (dict(v=None), NULL_),
+    (dict(out=None), NULL_),                             # state only needs z_out or s_out
+    (dict(out=None, q=None, k=None, z_out=FAKE + 0x500000), NULL_),  # state only still needs k
+    (dict(out=None, q=None, k=FAKE + 0x100002, z_out=FAKE + 0x500000), ALIGN),
+    (dict(q=FAKE + 2), ALIGN), (dict(out=FAKE + 0x300004), ALIGN),
+    (dict(sq=la_strides(2 * 128 * 64, 128 * 64, 60)), ALIGN),  # 120-byte row stride
+    (dict(sk=la_strides(-64, 0, 64)), SHAPE),
+    (dict(ws=None), WS), (dict(ws_bytes=16), WS),
+    (dict(z_in=FAKE + 0x500000, z_out=FAKE + 0x500000 + 64), ALIAS),   # partial overlap
+    (dict(s_in=FAKE + 0x500000, z_out=FAKE + 0x500000 - 256), ALIAS),  # z_out runs into s_in
+    (dict(z_in=FAKE + 0x500008), ALIGN),
 ])
 def test_causal_validation(lib, kw, status):
     assert _causal(lib, **kw) == status
@@ -94,15 +105,15 @@ def test_decode_validation(lib):
     ok = [vp(FAKE), vp(FAKE + 0x1000), vp(FAKE + 0x2000), 1, vp(FAKE + 0x3000), vp(FAKE + 0x100000),
           vp(FAKE + 0x200000), 2, 3, 64, 1e-6, None]
     bad = list(ok); bad[9] = 100
-    assert f(*bad) == 5
+    assert f(*bad) == UNSUP
     bad = list(ok); bad[0] = None
-    assert f(*bad) == 1
+    assert f(*bad) == NULL_
     bad = list(ok); bad[4] = vp(FAKE + 0x3004)
-    assert f(*bad) == 4
+    assert f(*bad) == ALIGN
     bad = list(ok); bad[3] = 2
-    assert f(*bad) == 3
+    assert f(*bad) == DTYPE
     bad = list(ok); bad[10] = -1.0
-    assert f(*bad) == 6
+    assert f(*bad) == VALUE
 
 
 @no_device
@@ -112,13 +123,13 @@ def test_noncausal_validation(lib):
     base = [vp(FAKE), st, vp(FAKE + 0x100000), st, vp(FAKE + 0x200000), st, 1, vp(FAKE + 0x300000), st,
             1, 2, 64, 64, 1e-6, vp(FAKE + 0x400000), 1 << 30, None]
     bad = list(base); bad[12] = 96
-    assert lib.la_noncausal_fwd(*bad) == 5
+    assert lib.la_noncausal_fwd(*bad) == UNSUP
     bad = list(base); bad[7] = None
-    assert lib.la_noncausal_fwd(*bad) == 1
+    assert lib.la_noncausal_fwd(*bad) == NULL_
     bad = list(base); bad[15] = 0
-    assert lib.la_noncausal_fwd(*bad) == 7
+    assert lib.la_noncausal_fwd(*bad) == WS
     bad = list(base); bad[2] = vp(FAKE + 0x100002)
-    assert lib.la_noncausal_fwd(*bad) == 4
+    assert lib.la_noncausal_fwd(*bad) == ALIGN
 
 
 @no_device
@@ -129,13 +140,13 @@ def test_unnormalized_validation(lib):
     base = [vp(FAKE), st, vp(FAKE + 0x100000), st, vp(FAKE + 0x200000), st, 1, vp(FAKE + 0x300000), st,
             1, 2, 128, 64, 0, 1e-6, None, None, None, None, vp(FAKE + 0x400000), 1 << 30, None]
     bad = list(base); bad[12] = 48
-    assert lib.la_causal_fwd_unnormalized(*bad) == 5
+    assert lib.la_causal_fwd_unnormalized(*bad) == UNSUP
     bad = list(base); bad[13] = 24
-    assert lib.la_causal_fwd_unnormalized(*bad) == 5
+    assert lib.la_causal_fwd_unnormalized(*bad) == UNSUP
     bad = list(base); bad[7] = None
-    assert lib.la_causal_fwd_unnormalized(*bad) == 1
+    assert lib.la_causal_fwd_unnormalized(*bad) == NULL_
     bad = list(base); bad[20] = 16
-    assert lib.la_causal_fwd_unnormalized(*bad) == 7
+    assert lib.la_causal_fwd_unnormalized(*bad) == WS
 
 
 def _memory(lib, **kw):
@@ -154,23 +165,23 @@ def _memory(lib, **kw):
 
 @no_device
 @pytest.mark.parametrize("kw, status", [
-    (dict(d=48), 5), (dict(dt=7), 3), (dict(eps=-1.0), 6), (dict(eps=float("nan")), 6),
-    (dict(N=-1), 2), (dict(q=None), 1), (dict(v=None), 1),
-    (dict(out=None), 1),                                 # update only needs z_out or s_out
-    (dict(k=FAKE + 0x100002), 4), (dict(out=FAKE + 0x300004), 4),
-    (dict(ws=None), 7), (dict(ws_bytes=16), 7),
-    (dict(z_in=FAKE + 0x500000, z_out=FAKE + 0x500000 + 64), 8),
-    (dict(s_in=FAKE + 0x500000, z_out=FAKE + 0x500000 - 256), 8),
-    (dict(s_out=FAKE + 0x500008), 4),
+    (dict(d=48), UNSUP), (dict(dt=7), DTYPE), (dict(eps=-1.0), VALUE), (dict(eps=float("nan")), VALUE),
+    (dict(N=-1), SHAPE), (dict(q=None), NULL_), (dict(v=None), NULL_),
+    (dict(out=None), NULL_),                             # update only needs z_out or s_out
+    (dict(k=FAKE + 0x100002), ALIGN), (dict(out=FAKE + 0x300004), ALIGN),
+    (dict(ws=None), WS), (dict(ws_bytes=16), WS),
+    (dict(z_in=FAKE + 0x500000, z_out=FAKE + 0x500000 + 64), ALIAS),
+    (dict(s_in=FAKE + 0x500000, z_out=FAKE + 0x500000 - 256), ALIAS),
+    (dict(s_out=FAKE + 0x500008), ALIGN),
 ])
 def test_memory_validation(lib, kw, status):
     assert _memory(lib, **kw) == status
 
 
 def test_memory_workspace_query(lib):
-    assert la.la_memory_workspace(1, 16, 2048, 128, torch.bfloat16) > 0
-    assert la.la_memory_workspace(1, 16, 0, 128, torch.bfloat16) == 0
-    assert la.la_memory_workspace(1, 16, 2048, 96, torch.bfloat16) == 0
+    assert la.la_memory_workspace(1, 16, 2048, 128) > 0
+    assert la.la_memory_workspace(1, 16, 0, 128) == 0
+    assert la.la_memory_workspace(1, 16, 2048, 96) == 0
 
 
 def test_binding_rejects_bad_tensors():

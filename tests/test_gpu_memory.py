@@ -123,37 +123,6 @@ def test_memory_bitwise_deterministic():
     assert all(torch.equal(x, y) for x, y in zip(a, b))
 
 
-def test_memory_segmented_workload_sampled_heads():
-    """The 32 x 2048-token segment loop of B1 H16 d128 (the segmented
-    workload's shape), every read of two heads against the oracle's loop."""
-    w = inp.WORKLOADS[inp.SEGMENTED]
-    _log(f"memory loop over {w.name}")
-    q, k, v = inp.workload_inputs(w)
-    B, H, N, d = q.shape
-    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
-    out = torch.empty(B, H, N, d, device=DEV)
-    zs = [torch.zeros(B, H, d, d, device=DEV) for _ in range(2)]
-    ss = [torch.zeros(B, H, d, device=DEV) for _ in range(2)]
-    nseg = N // w.segment
-    for i in range(nseg):
-        sl = slice(i * w.segment, (i + 1) * w.segment)
-        la.la_memory_fwd(qd[:, :, sl], kd[:, :, sl], vd[:, :, sl], out[:, :, sl], eps=w.eps,
-                         z_in=zs[i & 1] if i else None, s_in=ss[i & 1] if i else None,
-                         z_out=zs[(i + 1) & 1], s_out=ss[(i + 1) & 1])
-    torch.cuda.synchronize()
-    oc = out.cpu()
-    assert torch.isfinite(oc).all()
-    for h in (0, 11):
-        zr = sr = None
-        for i in range(nseg):
-            sl = slice(i * w.segment, (i + 1) * w.segment)
-            ro, zr, sr = oracle.memory(q[0, h, sl], k[0, h, sl], v[0, h, sl], w.eps, zr, sr)
-            if i:
-                assert heads_err(oc[0, h, sl], ro, d) < 2e-3, (h, i)
-        assert block_err(zs[nseg & 1][0, h].cpu(), zr, d * d) < 2e-3
-        assert block_err(ss[nseg & 1][0, h].cpu(), sr, d) < 2e-3
-
-
 def test_memory_strided_inputs_and_wide_output():
     # [B, N, H, d] storage viewed as [B, H, N, d]; reads into a wider buffer
     B, H, N, d = 2, 4, 777, 128

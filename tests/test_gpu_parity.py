@@ -4,9 +4,8 @@ Tolerance: max row-wise relative error (max_j |x_j - y_j| / max_j |y_j| over
 each output row, each head's Z block and each head's S) of 2e-3 for bf16
 inputs with fp32 accumulation and 1e-5 for fp32 inputs.
 
-Small cases compare every element; the full-size workloads compare every
-output of a sample of heads (the oracle computes a head independently of the
-others) plus properties of the whole output.
+Every case compares every element; the full-size workloads are in
+test_gpu_fullsize.py.
 """
 import numpy as np
 import pytest
@@ -88,10 +87,12 @@ def test_causal_group_orders(B, H, N, d):
     assert state_err(s.cpu(), torch.from_numpy(rs)) < 2e-3
 
 
-@pytest.mark.parametrize("chunk", [16, 32, 64, 128])
-@pytest.mark.parametrize("d", [64, 128])
+# chunk sizes that run as themselves: 64 everywhere; 128 for bf16 at d = 32
+# and 64 (the earlier kernel with 128-token chunks, while 64 runs the
+# column-split kernel at d = 64)
+@pytest.mark.parametrize("chunk,d", [(64, 32), (128, 32), (64, 64), (128, 64), (64, 128)])
 def test_causal_chunk_sizes_and_groups(chunk, d):
-    # one head and a long sequence: many token groups (mode-4 scan) and a
+    # two heads and a long sequence: many token groups (mode-4 scan) and a
     # ragged tail; every chunk size must agree with the oracle
     B, H, N = 1, 2, 3000 + 37
     _log(f"causal chunk={chunk} d={d} N={N}")
@@ -101,6 +102,24 @@ def test_causal_chunk_sizes_and_groups(chunk, d):
     assert heads_err(out.cpu(), ro, d) < 2e-3
     assert state_err(z.cpu(), torch.from_numpy(rz)) < 2e-3
     assert state_err(s.cpu(), torch.from_numpy(rs)) < 2e-3
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_chunk_results_do_not_depend_on_chunk(d):
+    # 64 against 128 where both run as themselves (d = 64: different kernels);
+    # the requests that the header says run as 64 (16, 32, and 128 at d = 128)
+    # give exactly the 64-token result
+    B, H, N = 1, 3, 2000 + 11
+    _log(f"chunk independence d={d}")
+    q, k, v = (t.to(DEV) for t in inp.qkv((B, H, N, d), 520 + d, torch.bfloat16, d ** -0.5))
+    base = run_causal(q, k, v, chunk=64)
+    for c in (16, 32) + ((128,) if d == 128 else ()):
+        other = run_causal(q, k, v, chunk=c)
+        assert all(torch.equal(x, y) for x, y in zip(base, other)), c
+    if d == 64:
+        o128 = run_causal(q, k, v, chunk=128)
+        assert heads_err(o128[0].cpu(), base[0].cpu(), d) < 2e-3
+        assert state_err(o128[1].cpu(), base[1].cpu()) < 2e-3
 
 
 def test_small_fp32_workload():
@@ -121,89 +140,6 @@ def test_constant_v_gpu():
     out, _, _ = run_causal(q.to(DEV), k.to(DEV), v.to(DEV), eps=0.0)
     err = rowwise_rel_err(out.cpu().reshape(-1, d), c.float().expand(B, H, N, d).reshape(-1, d))
     assert err < 1e-5
-
-
-# ---------------------------------------------------------------- full-size workloads (sampled heads)
-def test_headline_workload_sampled_heads():
-    w = inp.WORKLOADS[inp.HEADLINE]
-    _log(f"workload {w.name}")
-    q, k, v = inp.workload_inputs(w)
-    out, z, s = run_causal(*(t.to(DEV) for t in (q, k, v)), chunk=w.chunk, eps=w.eps)
-    out, z, s = out.cpu(), z.cpu(), s.cpu()
-    assert torch.isfinite(out).all()
-    for b, h in [(0, 0), (1, 3), (2, 5), (3, 7)]:
-        ro, rz, rs = oracle.causal(q[b, h], k[b, h], v[b, h], w.eps)
-        assert heads_err(out[b, h], ro, w.d) < 2e-3, (b, h)
-        assert rowwise_rel_err(z[b, h].reshape(1, -1), rz.reshape(1, -1)) < 2e-3
-        assert rowwise_rel_err(s[b, h].reshape(1, -1), rs.reshape(1, -1)) < 2e-3
-
-
-def test_segmented_workload_sampled_heads():
-    w = inp.WORKLOADS[inp.SEGMENTED]
-    _log(f"workload {w.name}")
-    q, k, v = inp.workload_inputs(w)
-    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
-    B, H, N, d = q.shape
-    out = torch.empty(B, H, N, d, dtype=torch.float32, device=DEV)
-    zs = [torch.zeros(B, H, d, d, device=DEV), torch.empty(B, H, d, d, device=DEV)]
-    ss = [torch.zeros(B, H, d, device=DEV), torch.empty(B, H, d, device=DEV)]
-    nseg = N // w.segment
-    for i in range(nseg):
-        sl = slice(i * w.segment, (i + 1) * w.segment)
-        la.la_causal_fwd(qd[:, :, sl], kd[:, :, sl], vd[:, :, sl], out[:, :, sl], eps=w.eps,
-                         z_in=zs[i & 1] if i else None, s_in=ss[i & 1] if i else None,
-                         z_out=zs[(i + 1) & 1], s_out=ss[(i + 1) & 1])
-    torch.cuda.synchronize()
-    zf, sf = zs[nseg & 1].cpu(), ss[nseg & 1].cpu()
-    oc = out.cpu()
-    assert torch.isfinite(oc).all()
-    for h in (0, 11):
-        ro, rz, rs = oracle.causal(q[0, h], k[0, h], v[0, h], w.eps)
-        assert heads_err(oc[0, h], ro, d) < 2e-3, h
-        assert rowwise_rel_err(zf[0, h].reshape(1, -1), rz.reshape(1, -1)) < 2e-3
-        assert rowwise_rel_err(sf[0, h].reshape(1, -1), rs.reshape(1, -1)) < 2e-3
-    # the carried segments agree with one call over the whole sequence
-    full, zfull, _ = run_causal(qd, kd, vd, eps=w.eps)
-    assert heads_err(oc, full.cpu(), d) < 2e-3
-    assert state_err(zf, zfull.cpu()) < 2e-3
-
-
-def test_decode_workload_sampled_heads():
-    w = inp.WORKLOADS[inp.DECODE]
-    _log(f"workload {w.name}")
-    (pq, pk, pv), (sq, sk, sv) = inp.workload_inputs(w)
-    B, H, d, T = w.B, w.H, w.d, w.N
-    z = torch.empty(B, H, d, d, device=DEV)
-    s = torch.empty(B, H, d, device=DEV)
-    la.la_causal_fwd(pq.to(DEV), pk.to(DEV), pv.to(DEV), None, eps=w.eps, z_out=z, s_out=s)
-    sqd, skd, svd = (t.to(DEV) for t in (sq, sk, sv))
-    outs = torch.empty(T, B, H, d, device=DEV)
-    for t in range(T):
-        la.la_decode_step(sqd[t], skd[t], svd[t], z, s, outs[t], eps=w.eps)
-    torch.cuda.synchronize()
-    oc, zc, sc = outs.cpu(), z.cpu(), s.cpu()
-    assert torch.isfinite(oc).all()
-    for b, h in [(0, 0), (37, 19), (63, 31)]:
-        qq = torch.cat([pq[b, h], sq[:, b, h]], 0)
-        kk = torch.cat([pk[b, h], sk[:, b, h]], 0)
-        vv = torch.cat([pv[b, h], sv[:, b, h]], 0)
-        ro, rz, rs = oracle.causal(qq, kk, vv, w.eps)
-        assert heads_err(oc[:, b, h], ro[w.prefix:], d) < 2e-3, (b, h)
-        assert rowwise_rel_err(zc[b, h].reshape(1, -1), rz.reshape(1, -1)) < 2e-3
-        assert rowwise_rel_err(sc[b, h].reshape(1, -1), rs.reshape(1, -1)) < 2e-3
-
-
-def test_noncausal_workload_sampled_heads():
-    w = inp.WORKLOADS[inp.NONCAUSAL]
-    _log(f"workload {w.name}")
-    q, k, v = inp.workload_inputs(w)
-    out = la.noncausal_fwd(q.to(DEV), k.to(DEV), v.to(DEV), eps=w.eps)
-    torch.cuda.synchronize()
-    oc = out.cpu()
-    assert torch.isfinite(oc).all()
-    for b, h in [(0, 0), (3, 9), (7, 15)]:
-        ro, _, _ = oracle.noncausal(q[b, h], k[b, h], v[b, h], w.eps)
-        assert heads_err(oc[b, h], ro, w.d) < 2e-3, (b, h)
 
 
 # ---------------------------------------------------------------- other entry points, small
@@ -240,18 +176,27 @@ def test_decode_small(dtype, d):
 
 
 # ---------------------------------------------------------------- edge cases and invariants
-@pytest.mark.parametrize("d", [64, 128])
-def test_state_only_equals_full_call(d):
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_state_only_from_k_and_v(dtype, d):
+    # out = NULL: the state from k and v alone (q is not passed), carried in
+    # and in place, against the oracle
     B, H, N = 2, 2, 999
-    q, k, v = inp.qkv((B, H, N, d), 44, torch.bfloat16, d ** -0.5)
+    _log(f"state only dtype={dtype} d={d}")
+    scale = 1.0 if dtype == torch.float32 else d ** -0.5
+    q, k, v = inp.qkv((B, H, N, d), 44, dtype, scale)
     z0, s0 = rand_state(B, H, d, 8)
     _, rz, rs = oracle.causal(q, k, v, 1e-6, z0, s0, want_out=False)
     z = torch.empty(B, H, d, d, device=DEV)
     s = torch.empty(B, H, d, device=DEV)
-    la.la_causal_fwd(q.to(DEV), k.to(DEV), v.to(DEV), None, z_in=z0.to(DEV), s_in=s0.to(DEV), z_out=z, s_out=s)
+    la.la_causal_fwd(None, k.to(DEV), v.to(DEV), None, z_in=z0.to(DEV), s_in=s0.to(DEV), z_out=z, s_out=s)
+    zi, si = z0.to(DEV), s0.to(DEV)
+    la.la_causal_fwd(None, k.to(DEV), v.to(DEV), None, z_in=zi, s_in=si, z_out=zi, s_out=si)
     torch.cuda.synchronize()
-    assert state_err(z.cpu(), torch.from_numpy(rz)) < 2e-3
-    assert state_err(s.cpu(), torch.from_numpy(rs)) < 2e-3
+    tol = TOL[dtype]
+    assert state_err(z.cpu(), torch.from_numpy(rz)) < tol
+    assert state_err(s.cpu(), torch.from_numpy(rs)) < tol
+    assert torch.equal(z, zi) and torch.equal(s, si)
 
 
 def test_zero_length_passes_state_through():
@@ -318,7 +263,7 @@ def test_reused_workspace_new_inputs(d):
     the partial states published between workgroups must be this call's."""
     B, H, N = 1, 2, 2048 if d == 128 else 4096
     _log(f"reused workspace d={d}")
-    ws = torch.empty(la.la_causal_fwd_workspace(B, H, N, d, torch.bfloat16), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(la.la_causal_fwd_workspace(B, H, N, d), dtype=torch.uint8, device=DEV)
     out = torch.empty(B, H, N, d, dtype=torch.float32, device=DEV)
     z = torch.empty(B, H, d, d, dtype=torch.float32, device=DEV)
     s = torch.empty(B, H, d, dtype=torch.float32, device=DEV)
@@ -349,13 +294,112 @@ def test_errors_raise_before_launch():
     q = torch.zeros(1, 2, 8, 48, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(la.LinAttnError) as e:
         la.la_causal_fwd(q, q, q, torch.empty(1, 2, 8, 48, device=DEV))
-    assert e.value.status == 5
+    assert e.value.status == la.STATUS["LA_ERR_UNSUPPORTED"]
     q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(la.LinAttnError) as e:
         la.la_causal_fwd(q, q, q, torch.empty(1, 2, 8, 64, device=DEV), eps=-1.0)
-    assert e.value.status == 6
+    assert e.value.status == la.STATUS["LA_ERR_VALUE"]
     big = torch.zeros(1, 2, 9, 64, dtype=torch.bfloat16, device=DEV)
     mis = big.view(-1)[1:1 + 2 * 8 * 64].view(1, 2, 8, 64)   # 2-byte offset
     with pytest.raises(la.LinAttnError) as e:
         la.la_causal_fwd(mis, q, q, torch.empty(1, 2, 8, 64, device=DEV))
-    assert e.value.status == 4
+    assert e.value.status == la.STATUS["LA_ERR_ALIGN"]
+
+
+def test_infinite_v_follows_the_chunk_formulas():
+    """An infinite v_s (column c) under IEEE arithmetic.  The recurrent form
+    keeps every output before s finite; the chunk formulas (a masked score
+    matrix times V) may turn column c of earlier outputs of s's 64-token chunk
+    into NaN, since a masked zero times infinity is NaN.  Pinned: outputs of
+    earlier chunks and all other columns match the oracle, column c is
+    non-finite from token s on."""
+    B, H, N, d = 1, 1, 500, 64
+    s_tok, c = 300, 7
+    q, k, v = inp.qkv((B, H, N, d), 49, torch.bfloat16, 0.125)
+    v[0, 0, s_tok, c] = float("inf")
+    ro, _, _ = oracle.causal(q, k, v, 1e-6)
+    out, _, _ = run_causal(q.to(DEV), k.to(DEV), v.to(DEV))
+    oc = out.cpu().double().numpy()[0, 0]
+    r = ro[0, 0]
+    chunk0 = (s_tok // 64) * 64
+    assert np.isfinite(oc[:chunk0]).all()
+    assert heads_err(oc[:chunk0], r[:chunk0], d) < 2e-3
+    others = [j for j in range(d) if j != c]
+    assert np.isfinite(oc[:, others]).all()
+    assert heads_err(oc[:, others], r[:, others], d - 1) < 2e-3
+    assert not np.isfinite(oc[s_tok:, c]).any() and not np.isfinite(r[s_tok:, c]).any()
+    # between the chunk start and s: the oracle's value, or NaN
+    mid, ref_mid = oc[chunk0:s_tok, c], r[chunk0:s_tok, c]
+    scale = np.abs(r[chunk0:s_tok][:, others]).max(axis=1)
+    assert (np.isnan(mid) | (np.abs(mid - ref_mid) <= 2e-3 * np.maximum(scale, np.abs(ref_mid)))).all()
+
+
+# the column-split kernel (bf16, d = 64 / 128 with groups of at most 4 / 2
+# chunks) and the earlier kernel (streamed groups: bf16 d = 128 N = 4096, fp32)
+@pytest.mark.parametrize("dtype,d,N", [(torch.bfloat16, 64, 4096), (torch.bfloat16, 128, 2048),
+                                       (torch.bfloat16, 128, 4096), (torch.float32, 64, 4096)])
+def test_lookback_giveup_poisons_and_counts(dtype, d, N, monkeypatch):
+    """A look-back wait that gives up must not return a plausible answer.
+    The library's test hook makes every wait look for a tag that no
+    workgroup stores, with a short poll limit, so every kernel still ends;
+    then every token group after the first must come out NaN (outputs and
+    final state), and the give-up counter at workspace offset 0 counts the
+    waves that gave up.  Without the hook the same workspace gives the
+    oracle's result and the counter stays put."""
+    B, H = 1, 2
+    _log(f"look-back give-up dtype={dtype} d={d} N={N}")
+    scale = 1.0 if dtype == torch.float32 else d ** -0.5
+    q, k, v = inp.qkv((B, H, N, d), 50 + d, dtype, scale)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    ws = torch.zeros(la.la_causal_fwd_workspace(B, H, N, d), dtype=torch.uint8, device=DEV)
+    counter = lambda: int(ws[:4].view(torch.int32).item())
+    out = torch.empty(B, H, N, d, device=DEV)
+    z = torch.empty(B, H, d, d, device=DEV)
+    s = torch.empty(B, H, d, device=DEV)
+    monkeypatch.setenv("LA_TEST_LOOKBACK_TIMEOUT", "64")
+    la.la_causal_fwd(qd, kd, vd, out, z_out=z, s_out=s, workspace=ws)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("LA_TEST_LOOKBACK_TIMEOUT")
+    n_giveups = counter()
+    oc = out.cpu()
+    nan_rows = torch.isnan(oc).all(dim=-1)[0]           # [H, N]
+    fin_rows = torch.isfinite(oc).all(dim=-1)[0]
+    assert (nan_rows | fin_rows).all()
+    first_nan = int(torch.nonzero(nan_rows[0])[0])       # the first row of group 1
+    assert first_nan > 0 and first_nan % 64 == 0 and N % first_nan == 0
+    assert nan_rows[:, first_nan:].all() and fin_rows[:, :first_nan].all()
+    ro, _, _ = oracle.causal(q, k, v, 1e-6)
+    assert heads_err(oc[:, :, :first_nan], ro[:, :, :first_nan], d) < TOL[dtype]
+    assert torch.isnan(z.cpu()).all() and torch.isnan(s.cpu()).all()
+    groups = N // first_nan
+    blocks = d // min(d, 64)                              # value-column blocks per head
+    assert n_giveups == B * H * blocks * (groups - 1) * 4, (n_giveups, groups)
+    # the same workspace without the hook: the oracle's result, counter unchanged
+    la.la_causal_fwd(qd, kd, vd, out, z_out=z, s_out=s, workspace=ws)
+    torch.cuda.synchronize()
+    assert counter() == n_giveups
+    assert heads_err(out.cpu(), ro, d) < TOL[dtype]
+
+
+def test_causal_call_refused_under_graph_capture():
+    # the look-back tag is fixed when a call is issued: a captured graph would
+    # replay it, so the library refuses before recording any work
+    B, H, N, d = 1, 2, 1024, 64
+    q, k, v = (t.to(DEV) for t in inp.qkv((B, H, N, d), 51, torch.bfloat16, 0.125))
+    out = torch.empty(B, H, N, d, device=DEV)
+    ws = torch.empty(la.la_causal_fwd_workspace(B, H, N, d), dtype=torch.uint8, device=DEV)
+    call = la.prepare_causal_fwd(q, k, v, out, workspace=ws)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    refused = None
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        try:
+            call()
+        except la.LinAttnError as e:
+            refused = e.status
+    assert refused == la.STATUS["LA_ERR_UNSUPPORTED"]
+    call()   # outside the capture the same call runs
+    torch.cuda.synchronize()
+    ro, _, _ = oracle.causal(q.cpu(), k.cpu(), v.cpu(), 1e-6)
+    assert heads_err(out.cpu(), ro, d) < 2e-3
