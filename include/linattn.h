@@ -134,6 +134,34 @@ la_status la_causal_fwd(const void *q, la_strides sq, const void *k, la_strides 
                         void *workspace, size_t ws_bytes, void *hip_stream);
 
 /*
+ * la_causal_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (tight serving loops, harnesses that forbid
+ * hipMalloc).  It allocates nothing: its scratch memory is a fixed array of
+ * la_noalloc_scratch_bytes() bytes per GPU inside the library, held until
+ * the process ends.  Arguments, results and errors are those of
+ * la_causal_fwd, except:
+ *  - a call whose workspace would exceed la_noalloc_scratch_bytes() (that
+ *    is, la_causal_fwd_workspace(...) > la_noalloc_scratch_bytes()) returns
+ *    LA_ERR_WORKSPACE before any device work;
+ *  - every call on one GPU shares that GPU's array, so calls that can
+ *    overlap on one GPU (different streams, different host threads without
+ *    ordering) race and must not be issued;
+ *  - the give-up counter of the look-back lives in the array and cannot be
+ *    read; a wait that gives up still shows as NaN outputs and state;
+ *  - like la_causal_fwd with outputs, it cannot be captured into a HIP graph
+ *    (LA_ERR_UNSUPPORTED).
+ */
+la_status la_causal_fwd_noalloc(const void *q, la_strides sq, const void *k, la_strides sk,
+                                const void *v, la_strides sv, la_dtype dt,
+                                float *out, la_strides so,
+                                int B, int H, int N, int d, int chunk, float eps,
+                                const float *z_in, const float *s_in,
+                                float *z_out, float *s_out, void *hip_stream);
+
+/* Bytes of the per-GPU scratch array of la_causal_fwd_noalloc (32 MiB). */
+size_t la_noalloc_scratch_bytes(void);
+
+/*
  * The unnormalised causal form: the chunk formulas of "Attention Kernel Mask"
  * (section "How to accelerate causal linear attention", chunk-sequential and
  * materialised modes) as printed, with no denominator:

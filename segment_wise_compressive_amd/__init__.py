@@ -24,6 +24,7 @@ __all__ = [
     "library_path", "load_library",
     "la_status_str", "la_version",
     "la_causal_fwd_workspace", "la_causal_fwd", "la_causal_fwd_unnormalized",
+    "la_causal_fwd_noalloc", "la_noalloc_scratch_bytes",
     "la_decode_step",
     "la_noncausal_workspace", "la_noncausal_fwd",
     "la_memory_workspace", "la_memory_fwd",
@@ -77,6 +78,11 @@ def load_library():
     lib.la_causal_fwd.restype = i32
     lib.la_causal_fwd_unnormalized.argtypes = lib.la_causal_fwd.argtypes
     lib.la_causal_fwd_unnormalized.restype = i32
+    lib.la_causal_fwd_noalloc.argtypes = [vp, S, vp, S, vp, S, i32, vp, S, i32, i32, i32, i32, i32, f32,
+                                          vp, vp, vp, vp, vp]
+    lib.la_causal_fwd_noalloc.restype = i32
+    lib.la_noalloc_scratch_bytes.argtypes = []
+    lib.la_noalloc_scratch_bytes.restype = sz
     lib.la_decode_step.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, f32, vp]
     lib.la_decode_step.restype = i32
     lib.la_noncausal_workspace.argtypes = [i32, i32, i32, i32]
@@ -233,6 +239,36 @@ def la_causal_fwd_unnormalized(q, k, v, out=None, *, chunk: int = 0, eps: float 
     in linattn.h); arguments as for prepare_causal_fwd."""
     prepare_causal_fwd(q, k, v, out, chunk=chunk, eps=eps, z_in=z_in, s_in=s_in, z_out=z_out, s_out=s_out,
                        workspace=workspace, stream=stream, normalize=False)()
+
+
+def la_noalloc_scratch_bytes() -> int:
+    """Bytes of the per-GPU scratch array behind la_causal_fwd_noalloc."""
+    return int(load_library().la_noalloc_scratch_bytes())
+
+
+def la_causal_fwd_noalloc(q, k, v, out=None, *, chunk: int = 0, eps: float = 1e-6,
+                          z_in=None, s_in=None, z_out=None, s_out=None, stream=None) -> None:
+    """la_causal_fwd_noalloc in linattn.h: la_causal_fwd with the library's
+    fixed per-GPU scratch array instead of a workspace (allocates nothing;
+    calls that overlap on one GPU race).  Arguments as for prepare_causal_fwd."""
+    B, H, N, d = k.shape
+    if (q is not None and tuple(q.shape) != (B, H, N, d)) or tuple(v.shape) != (B, H, N, d):
+        raise ValueError("q, k, v must have the same shape")
+    if (q is not None and q.dtype != k.dtype) or v.dtype != k.dtype:
+        raise TypeError("q, k, v must have the same dtype")
+    if out is not None and (out.dtype != torch.float32 or tuple(out.shape) != (B, H, N, d)):
+        raise ValueError("out must be float32 [B, H, N, d]")
+    for t, shp, nm in ((z_in, (B, H, d, d), "z_in"), (z_out, (B, H, d, d), "z_out"),
+                       (s_in, (B, H, d), "s_in"), (s_out, (B, H, d), "s_out")):
+        _state_check(t, shp, nm)
+    so = _strides(out) if out is not None else la_strides(0, 0, 0)
+    sq = _strides(q) if q is not None else la_strides(0, 0, 0)
+    st = load_library().la_causal_fwd_noalloc(
+        _ptr(q), sq, _ptr(k), _strides(k), _ptr(v), _strides(v), _dtype_code(k),
+        _ptr(out), so, B, H, N, d, int(chunk), ctypes.c_float(eps),
+        _ptr(z_in), _ptr(s_in), _ptr(z_out), _ptr(s_out), _stream(stream, k.device))
+    if st != 0:
+        raise LinAttnError(st, "la_causal_fwd_noalloc")
 
 
 def prepare_decode_step(q, k, v, z, s, out, *, eps: float = 1e-6, stream=None) -> Prepared:

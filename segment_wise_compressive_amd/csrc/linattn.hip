@@ -49,6 +49,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <stdlib.h>
 
 #include "linattn.h"
@@ -2837,6 +2838,37 @@ Args make_args(const void *q, la_strides sq, const void *k, la_strides sk, const
     return a;
 }
 
+// ---- scratch memory of la_causal_fwd_noalloc: one array per GPU, held by the
+// code object until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device array: the device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void *scratch_addr[MAX_DEVICES];
+
+// the current device's scratch address (nullptr if it cannot be resolved)
+void *device_scratch()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_addr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        scratch_addr[dev] = p;
+    }
+    return scratch_addr[dev];
+}
+
 }  // namespace
 
 // ====================================================================== C ABI
@@ -2885,7 +2917,8 @@ la_status causal_impl(const void *q, la_strides sq, const void *k, la_strides sk
                       int B, int H, int N, int d, int chunk, float eps,
                       const float *z_in, const float *s_in,
                       float *z_out, float *s_out,
-                      void *workspace, size_t ws_bytes, void *hip_stream, int unnorm)
+                      void *workspace, size_t ws_bytes, void *hip_stream, int unnorm,
+                      bool use_scratch = false)
 {
     la_status st = check_common(B, H, N, d, dt, eps);
     if (st != LA_OK) return st;
@@ -2910,8 +2943,9 @@ la_status causal_impl(const void *q, la_strides sq, const void *k, la_strides sk
     if (overlaps(z_out, zb, s_in, sb) || overlaps(s_out, sb, z_in, zb) || overlaps(z_out, zb, s_out, sb))
         return LA_ERR_ALIAS;
     Plan pl = want_out ? plan_causal(B, H, N, d, dt, chunk) : plan_state(B, H, N, d, dt);
-    if (ws_bytes < pl.total || (pl.total > 0 && !workspace)) return LA_ERR_WORKSPACE;
+    if (ws_bytes < pl.total || (pl.total > 0 && !workspace && !use_scratch)) return LA_ERR_WORKSPACE;
     if (BH == 0) return LA_OK;
+    if (use_scratch && pl.total > 0 && !(workspace = device_scratch())) return LA_ERR_LAUNCH;
 
     hipStream_t stream = (hipStream_t)hip_stream;
     (void)hipGetLastError();
@@ -2987,6 +3021,21 @@ la_status la_causal_fwd(const void *q, la_strides sq, const void *k, la_strides 
     return causal_impl(q, sq, k, sk, v, sv, dt, out, so, B, H, N, d, chunk, eps, z_in, s_in, z_out, s_out,
                        workspace, ws_bytes, hip_stream, 0);
 }
+
+la_status la_causal_fwd_noalloc(const void *q, la_strides sq, const void *k, la_strides sk,
+                                const void *v, la_strides sv, la_dtype dt,
+                                float *out, la_strides so,
+                                int B, int H, int N, int d, int chunk, float eps,
+                                const float *z_in, const float *s_in,
+                                float *z_out, float *s_out, void *hip_stream)
+{
+    // the sizes whose workspace (as la_causal_fwd_workspace states it) fits
+    if (la_causal_fwd_workspace(B, H, N, d, chunk) > NOALLOC_SCRATCH_BYTES) return LA_ERR_WORKSPACE;
+    return causal_impl(q, sq, k, sk, v, sv, dt, out, so, B, H, N, d, chunk, eps, z_in, s_in, z_out, s_out,
+                       nullptr, NOALLOC_SCRATCH_BYTES, hip_stream, 0, true);
+}
+
+size_t la_noalloc_scratch_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
 
 la_status la_causal_fwd_unnormalized(const void *q, la_strides sq, const void *k, la_strides sk,
                                      const void *v, la_strides sv, la_dtype dt,

@@ -33,7 +33,8 @@ def test_exports_every_declared_symbol(lib):
     names = la.declared_entry_points()
     assert set(names) == {"la_status_str", "la_version", "la_causal_fwd_workspace", "la_causal_fwd",
                           "la_decode_step", "la_noncausal_workspace", "la_noncausal_fwd",
-                          "la_memory_workspace", "la_memory_fwd", "la_causal_fwd_unnormalized"}
+                          "la_memory_workspace", "la_memory_fwd", "la_causal_fwd_unnormalized",
+                          "la_causal_fwd_noalloc", "la_noalloc_scratch_bytes"}
     raw = ctypes.CDLL(la.library_path())
     for n in names:
         assert hasattr(raw, n), n
@@ -193,3 +194,26 @@ def test_binding_rejects_bad_tensors():
         la.la_causal_fwd(q, q, q[:, :, :4], torch.zeros(1, 2, 8, 64))
     with pytest.raises(ValueError):
         la.la_causal_fwd(q, q, q, torch.zeros(1, 2, 8, 64), z_in=torch.zeros(1, 2, 64, 63))
+
+
+def test_noalloc_scratch_size(lib):
+    assert la.la_noalloc_scratch_bytes() == 32 << 20
+
+
+@no_device
+def test_noalloc_validation(lib):
+    # the allocation-free entry point checks as la_causal_fwd does, and
+    # rejects a call whose workspace would not fit in the scratch array
+    vp = ctypes.c_void_p
+
+    def call(B=1, H=2, N=128, d=64, out=FAKE + 0x300000, q=FAKE, eps=1e-6):
+        st = la_strides(H * N * d, N * d, d)
+        return lib.la_causal_fwd_noalloc(None if q is None else vp(q), st, vp(FAKE + 0x100000), st,
+                                         vp(FAKE + 0x200000), st, la.LA_BF16, None if out is None else vp(out),
+                                         st, B, H, N, d, 0, eps, None, None, None, None, None)
+    assert call(d=48) == UNSUP
+    assert call(q=None) == NULL_
+    assert call(eps=-1.0) == VALUE
+    big = (1, 64, 1 << 16, 128)
+    assert la.la_causal_fwd_workspace(*big) > la.la_noalloc_scratch_bytes()
+    assert call(*big) == WS
