@@ -45,6 +45,31 @@ MUTANTS = {
     "unnormalized_read_transposed": ("acc += phiq[a] * W[a * d + b];", "acc += phiq[a] * W[b * d + a];"),
 }
 
+# planted in the backward pass (oracle_causal_bwd); checked by its own pins
+BACKWARD_MUTANTS = {
+    "bwd_phi_derivative_is_one": ("static double dphi(double x) { return x > 0.0 ? 1.0 : exp(x); }",
+                                  "static double dphi(double x) { return x > 0.0 ? 1.0 : 1.0; }"),
+    "bwd_phi_derivative_is_exp": ("static double dphi(double x) { return x > 0.0 ? 1.0 : exp(x); }",
+                                  "static double dphi(double x) { return exp(x); }"),
+    "bwd_normaliser_term_dropped": ("dD[t] = -dodo / den;", "dD[t] = 0.0 * dodo;"),
+    "bwd_normaliser_sign_flipped": ("dD[t] = -dodo / den;", "dD[t] = dodo / den;"),
+    "bwd_dq_misses_key_sum": ("double acc = S[j] * dD[t];", "double acc = 0.0 * S[j] * dD[t];"),
+    "bwd_dq_uses_key_derivative": ("dq[(h * N + t) * d + j] = acc * dphi((double)qt[j]);",
+                                   "dq[(h * N + t) * d + j] = acc * dphi((double)kt[j]);"),
+    "bwd_dk_adjoint_transposed": ("for (c = 0; c < d; ++c) acc += R[j * d + c] * (double)vt[c];",
+                                  "for (c = 0; c < d; ++c) acc += R[c * d + j] * (double)vt[c];"),
+    "bwd_dv_adjoint_transposed": ("for (j = 0; j < d; ++j) acc += R[j * d + c] * f[j];",
+                                  "for (j = 0; j < d; ++j) acc += R[c * d + j] * f[j];"),
+    "bwd_dk_misses_key_sum_adjoint": ("                double acc = r[j];", "                double acc = 0.0 * r[j];"),
+    "bwd_adjoint_excludes_own_token": (
+        "            for (j = 0; j < d; ++j) g[j] = phi((double)qt[j]);\n            for (j = 0; j < d; ++j) {\n"
+        "                for (c = 0; c < d; ++c) R[j * d + c] += g[j] * dn[t * d + c];",
+        "            for (j = 0; j < d; ++j) g[j] = t + 1 < N ? phi((double)qt[j + d]) : 0.0;\n"
+        "            for (j = 0; j < d; ++j) {\n"
+        "                for (c = 0; c < d; ++c) R[j * d + c] += g[j] * (t + 1 < N ? dn[(t + 1) * d + c] : 0.0);"),
+    "bwd_final_state_gradient_ignored": ("if (dz_out) memcpy(R,", "if (0) memcpy(R,"),
+}
+
 
 def _build(tmp_path, name, src_text):
     c = tmp_path / f"{name}.c"
@@ -55,18 +80,19 @@ def _build(tmp_path, name, src_text):
     return str(so)
 
 
-def _run_pins(lib):
+def _run_pins(lib, pins="test_oracle_pins.py"):
     env = dict(os.environ, LINATTN_ORACLE_LIB_OVERRIDE=lib, OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", pins)],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     return r.returncode, r.stdout[-2000:]
 
 
 def test_unmodified_oracle_passes_pins(tmp_path):
     lib = _build(tmp_path, "clean", open(SRC).read())
-    rc, out = _run_pins(lib)
-    assert rc == 0, out
+    for pins in ("test_oracle_pins.py", "test_oracle_backward_pins.py"):
+        rc, out = _run_pins(lib, pins)
+        assert rc == 0, out
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -77,3 +103,13 @@ def test_mutant_is_caught(tmp_path, name):
     lib = _build(tmp_path, name, src.replace(old, new))
     rc, out = _run_pins(lib)
     assert rc != 0, f"mutant {name} passed every pin:\n{out}"
+
+
+@pytest.mark.parametrize("name", sorted(BACKWARD_MUTANTS))
+def test_backward_mutant_is_caught(tmp_path, name):
+    src = open(SRC).read()
+    old, new = BACKWARD_MUTANTS[name]
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique/absent"
+    lib = _build(tmp_path, name, src.replace(old, new))
+    rc, out = _run_pins(lib, "test_oracle_backward_pins.py")
+    assert rc != 0, f"mutant {name} passed every backward pin:\n{out}"
