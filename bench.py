@@ -356,6 +356,29 @@ def bench_prefill(args, torch, la, inp):
     return res
 
 
+def bench_backward(args, torch, la, inp):
+    """la_causal_bwd on the headline shape (B4 H8 N4096 d64, bf16 q, k, v;
+    fp32 out from the forward call and fp32 dout): dq, dk, dv.  Algorithmic
+    bytes: q, k, v (bf16), out and dout (fp32) read once, dq, dk, dv (fp32)
+    written once: 26 d bytes per head-token."""
+    w = inp.WORKLOADS[inp.HEADLINE]
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in inp.workload_inputs(w))
+    dout = torch.randn(w.B, w.H, w.N, w.d, generator=torch.Generator().manual_seed(w.seed + 7)).to(dev)
+    out = torch.empty(w.B, w.H, w.N, w.d, device=dev)
+    la.la_causal_fwd(q, k, v, out, eps=w.eps)
+    dq, dk, dv = (torch.empty(w.B, w.H, w.N, w.d, device=dev) for _ in range(3))
+    ws = torch.empty(max(1, la.la_causal_bwd_workspace(w.B, w.H, w.N, w.d)), dtype=torch.uint8, device=dev)
+    call = la.prepare_causal_bwd(q, k, v, out, dout, dq, dk, dv, eps=w.eps, workspace=ws)
+    steps, warm = leg_counts(args, 50, 10)
+    prewarm(lambda _: call(), 1, args.prewarm_s, batch=10)
+    ms = time_steps(lambda _: call(), steps, warm, 1) / steps
+    b = w.head_tokens * (3 * w.d * w.dtype.itemsize + 2 * 4 * w.d + 3 * 4 * w.d)
+    return {"workload": w.name + "_backward", "value": round(w.head_tokens / (ms * 1e-3), 1),
+            "unit": "head-tokens/s", "ms_per_step": round(ms, 5), "alg_bytes_per_call": b,
+            "roofline": roofline(b, ms, None)}
+
+
 def cpu_baseline(w, qkv, seconds):
     """The fp64 oracle, as it is, on the host cores: whole steps of the same
     workload repeated until `seconds` of wall time have passed (at least 2)."""
@@ -373,9 +396,10 @@ def cpu_baseline(w, qkv, seconds):
                       f"fp64 recurrent form, run back to back for about {seconds:g} s"}
 
 
-LEGS = ("headline", "segmented", "decode", "noncausal", "memory", "unnormalized", "prefill")
+LEGS = ("headline", "segmented", "decode", "noncausal", "memory", "unnormalized", "prefill", "backward")
 LEG_FNS = {"segmented": bench_segmented, "decode": bench_decode, "noncausal": bench_noncausal,
-           "memory": bench_memory, "unnormalized": bench_unnormalized, "prefill": bench_prefill}
+           "memory": bench_memory, "unnormalized": bench_unnormalized, "prefill": bench_prefill,
+           "backward": bench_backward}
 
 
 def main():

@@ -179,6 +179,45 @@ la_status la_causal_fwd_unnormalized(const void *q, la_strides sq, const void *k
                                      void *workspace, size_t ws_bytes, void *hip_stream);
 
 /*
+ * Backward pass of the causal form: the gradients of la_causal_fwd's outputs
+ * and final state with respect to q, k, v and the carried-in state.
+ * "Attention Kernel Mask" names this pass (the "Training-Backward" row of its
+ * table under "Causal Attention Training and Inferencing"; training needs all
+ * outputs, the cumsum problem of its "Causal linear attention" notes) but
+ * does not write it out; it is computed as the exact derivative of the
+ * forward definition.  With g_t = phi(q_t), f_t = phi(k_t), the running state
+ * Z_t, S_t (carried-in state included), D_t = g_t . S_t + eps and
+ * out_t = Z_t^T g_t / D_t:
+ *   dn_t = dout_t / D_t,   dD_t = -(dout_t . out_t) / D_t,
+ *   dq_t = phi'(q_t) * (Z_t dn_t + S_t dD_t),
+ *   R_t = dz_out + sum_{u>=t} g_u dn_u^T,   r_t = ds_out + sum_{u>=t} g_u dD_u,
+ *   dk_t = phi'(k_t) * (R_t v_t + r_t),   dv_t = R_t^T f_t,
+ *   dz_in = R_0,   ds_in = r_0,
+ * where phi'(x) = 1 for x > 0 and e^x otherwise.
+ * q, k, v, dt, z_in, s_in, eps, B, H, N, d: the arguments of the forward call
+ * whose gradients are taken (z_in / s_in NULL = zeros).  out: that call's
+ * float32 output (it supplies dD_t).  dout: float32 [B, H, N, d], the
+ * gradient reaching out.  dz_out / ds_out: the gradient reaching the final
+ * state ([B, H, d, d] / [B, H, d]); NULL = zeros, which is the detached
+ * memory of "Segment-Wise Attention" (its thread discusses carrying the
+ * memory across segments without gradients).
+ * dq, dk, dv: float32 [B, H, N, d] with their own strides (unit stride along
+ * d).  dz_in / ds_in: the gradient reaching z_in / s_in; NULL = not written.
+ * No gradient may overlap an input or another gradient (LA_ERR_ALIAS).
+ * Strides, alignment, dtypes and sizes follow the common conventions.
+ * Workspace: at least la_causal_bwd_workspace(...) bytes, any contents.
+ */
+size_t la_causal_bwd_workspace(int B, int H, int N, int d);
+la_status la_causal_bwd(const void *q, la_strides sq, const void *k, la_strides sk,
+                        const void *v, la_strides sv, la_dtype dt,
+                        const float *out, la_strides so, const float *dout, la_strides sdo,
+                        int B, int H, int N, int d, float eps,
+                        const float *z_in, const float *s_in, const float *dz_out, const float *ds_out,
+                        float *dq, la_strides sdq, float *dk, la_strides sdk, float *dv, la_strides sdv,
+                        float *dz_in, float *ds_in,
+                        void *workspace, size_t ws_bytes, void *hip_stream);
+
+/*
  * One generation step per head ("Attention Kernel Mask", mode 2: recurrent
  * generation with a fixed-size state and no KV cache):
  *   Z += phi(k) v^T;  S += phi(k);  out = phi(q)^T Z / (phi(q) . S + eps).

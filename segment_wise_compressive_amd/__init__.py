@@ -25,6 +25,7 @@ __all__ = [
     "la_status_str", "la_version",
     "la_causal_fwd_workspace", "la_causal_fwd", "la_causal_fwd_unnormalized",
     "la_causal_fwd_noalloc", "la_noalloc_scratch_bytes",
+    "la_causal_bwd_workspace", "la_causal_bwd", "prepare_causal_bwd", "causal_bwd",
     "la_decode_step",
     "la_noncausal_workspace", "la_noncausal_fwd",
     "la_memory_workspace", "la_memory_fwd",
@@ -81,6 +82,11 @@ def load_library():
     lib.la_causal_fwd_noalloc.argtypes = [vp, S, vp, S, vp, S, i32, vp, S, i32, i32, i32, i32, i32, f32,
                                           vp, vp, vp, vp, vp]
     lib.la_causal_fwd_noalloc.restype = i32
+    lib.la_causal_bwd_workspace.argtypes = [i32, i32, i32, i32]
+    lib.la_causal_bwd_workspace.restype = sz
+    lib.la_causal_bwd.argtypes = [vp, S, vp, S, vp, S, i32, vp, S, vp, S, i32, i32, i32, i32, f32,
+                                  vp, vp, vp, vp, vp, S, vp, S, vp, S, vp, vp, vp, sz, vp]
+    lib.la_causal_bwd.restype = i32
     lib.la_noalloc_scratch_bytes.argtypes = []
     lib.la_noalloc_scratch_bytes.restype = sz
     lib.la_decode_step.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, f32, vp]
@@ -269,6 +275,67 @@ def la_causal_fwd_noalloc(q, k, v, out=None, *, chunk: int = 0, eps: float = 1e-
         _ptr(z_in), _ptr(s_in), _ptr(z_out), _ptr(s_out), _stream(stream, k.device))
     if st != 0:
         raise LinAttnError(st, "la_causal_fwd_noalloc")
+
+
+@functools.lru_cache(maxsize=4096)
+def la_causal_bwd_workspace(B: int, H: int, N: int, d: int) -> int:
+    """Workspace bytes of la_causal_bwd."""
+    return int(load_library().la_causal_bwd_workspace(B, H, N, d))
+
+
+def prepare_causal_bwd(q, k, v, out, dout, dq, dk, dv, *, eps: float = 1e-6,
+                       z_in=None, s_in=None, dz_out=None, ds_out=None, dz_in=None, ds_in=None,
+                       workspace: Optional[torch.Tensor] = None, stream=None) -> Prepared:
+    """Check and marshal a la_causal_bwd call (nothing runs until it is called).
+
+    q, k, v: the forward call's inputs; out: its float32 output; dout: float32
+    gradient of out; dq, dk, dv: float32 [B, H, N, d] results (any strides with
+    unit d stride).  States and their gradients: float32 contiguous.
+    """
+    B, H, N, d = q.shape
+    for t, nm in ((k, "k"), (v, "v")):
+        if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype:
+            raise ValueError(f"{nm} must match q in shape and dtype")
+    for t, nm in ((out, "out"), (dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, H, N, d):
+            raise ValueError(f"{nm} must be float32 [B, H, N, d]")
+    for t, shp, nm in ((z_in, (B, H, d, d), "z_in"), (dz_out, (B, H, d, d), "dz_out"), (dz_in, (B, H, d, d), "dz_in"),
+                       (s_in, (B, H, d), "s_in"), (ds_out, (B, H, d), "ds_out"), (ds_in, (B, H, d), "ds_in")):
+        _state_check(t, shp, nm)
+    ws_bytes = la_causal_bwd_workspace(B, H, N, d)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = [_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v), _dtype_code(q),
+            _ptr(out), _strides(out), _ptr(dout), _strides(dout), B, H, N, d, ctypes.c_float(eps),
+            _ptr(z_in), _ptr(s_in), _ptr(dz_out), _ptr(ds_out),
+            _ptr(dq), _strides(dq), _ptr(dk), _strides(dk), _ptr(dv), _strides(dv), _ptr(dz_in), _ptr(ds_in),
+            _ptr(workspace), ctypes.c_size_t(have), _opt_stream(stream, q.device)]
+    return Prepared(load_library().la_causal_bwd, args, q.device, "la_causal_bwd",
+                    (q, k, v, out, dout, dq, dk, dv, z_in, s_in, dz_out, ds_out, dz_in, ds_in, workspace))
+
+
+def la_causal_bwd(q, k, v, out, dout, dq, dk, dv, **kw) -> None:
+    """Backward pass of the causal form (la_causal_bwd in linattn.h); arguments
+    as for prepare_causal_bwd."""
+    prepare_causal_bwd(q, k, v, out, dout, dq, dk, dv, **kw)()
+
+
+def causal_bwd(q, k, v, out, dout, *, eps: float = 1e-6, state=None, dstate=None, want_dstate: bool = False):
+    """(dq, dk, dv) of causal linear attention, plus (dz_in, ds_in) when
+    want_dstate.  state: the forward call's (z_in, s_in); dstate: the
+    gradient (dz_out, ds_out) reaching its final state."""
+    B, H, N, d = q.shape
+    dq, dk, dv = (torch.empty(B, H, N, d, dtype=torch.float32, device=q.device) for _ in range(3))
+    z_in, s_in = state if state is not None else (None, None)
+    dz_out, ds_out = dstate if dstate is not None else (None, None)
+    dz_in = ds_in = None
+    if want_dstate:
+        dz_in = torch.empty(B, H, d, d, dtype=torch.float32, device=q.device)
+        ds_in = torch.empty(B, H, d, dtype=torch.float32, device=q.device)
+    la_causal_bwd(q, k, v, out, dout, dq, dk, dv, eps=eps, z_in=z_in, s_in=s_in, dz_out=dz_out, ds_out=ds_out,
+                  dz_in=dz_in, ds_in=ds_in)
+    return (dq, dk, dv, dz_in, ds_in) if want_dstate else (dq, dk, dv)
 
 
 def prepare_decode_step(q, k, v, z, s, out, *, eps: float = 1e-6, stream=None) -> Prepared:

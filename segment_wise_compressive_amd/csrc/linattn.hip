@@ -2614,6 +2614,322 @@ __global__ void __launch_bounds__(256) k_decode(const void *qp, const void *kp, 
     }
 }
 
+// ================================================================ backward pass
+// Gradients of the causal form (the backward pass of training, which
+// "Attention Kernel Mask" lists as a row of its table under "Causal Attention
+// Training and Inferencing" without writing it out).  With g_t = phi(q_t),
+// f_s = phi(k_s), the running state Z_t, S_t (carried-in state included),
+// D_t = g_t . S_t + eps and an upstream gradient dout_t:
+//   dn_t = dout_t / D_t,  dD_t = -(dout_t . out_t) / D_t,
+//   dq_t = phi'(q_t) * (Z_t dn_t + S_t dD_t),
+//   dk_s = phi'(k_s) * (R_s v_s + r_s),  dv_s = R_s^T f_s,
+// where R_s = dz_out + sum_{t >= s} g_t dn_t^T and r_s = ds_out + sum_{t >= s}
+// g_t dD_t are the adjoint state.  phi'(x) = min(phi(x), 1).
+// Per 64-token chunk c (inclusive masks inside the chunk), with A_ts =
+// v_s . dn_t + dD_t and P_ts = g_t . f_s:
+//   dq_t = phi'(q_t) * (Z_c dn_t + S_c dD_t + sum_{s <= t} A_ts f_s)
+//   dk_s = phi'(k_s) * (R'_c v_s + r'_c + sum_{t >= s} A_ts g_t)
+//   dv_s = R'_c^T f_s + sum_{t >= s} P_ts dn_t
+// where (Z_c, S_c) is the state before the chunk and (R'_c, r'_c) the adjoint
+// state after it.  Both are materialised at every chunk boundary (the mode of
+// "How to accelerate causal linear attention" that scans all chunk states
+// first and then computes every chunk independently): the forward states by
+// k_group_state + a k_slots scan, the adjoint ones by k_bwd_prep + a k_slots
+// scan over reverse-indexed slots.  Every product runs on fp32 MFMA.
+struct BwdArgs {
+    const void *q, *k, *v;
+    const float *out, *dout;
+    int64_t sqb, sqh, sqn, skb, skh, skn, svb, svh, svn, sob, soh, son, sdb, sdh, sdn;
+    float *dq, *dk, *dv;
+    int64_t gqb, gqh, gqn, gkb, gkh, gkn, gvb, gvh, gvn;
+    int B, H, N, nch, P, NS;
+    float eps;
+    const float *fwd;   // forward slots [B*H*P][NS]: slot c = the state before chunk c
+    float *rev;         // adjoint slots: chunk c writes slot nch - c; after the scan slot nch - 1 - c is
+                        // the adjoint state after chunk c
+    float *den, *dden;  // D_t and dD_t [B*H][N]
+};
+
+// Stage 64 rows (a chunk) of one head into an fp32 [64][D + 4] LDS array.
+// MODE 0: the values; 1: phi of the values, zero from row `nval` on; 2: the
+// values times 1 / den[row] (zero from row `nval` on).
+template <bool F32, int D, int MODE>
+__device__ __forceinline__ void bwd_stage(rsrc_t src, int64_t rs, float *dst, int nval, int tid,
+                                          const float *den = nullptr)
+{
+    constexpr int VEC = F32 ? 4 : 8, VPR = D / VEC, ITEMS = 64 * VPR, LD = D + 4;
+    static_assert(ITEMS % NTHR == 0, "whole 16-byte vectors per thread");
+    u32x4 raw[ITEMS / NTHR];
+#pragma unroll
+    for (int it = 0; it < ITEMS / NTHR; ++it) {
+        const int item = tid + it * NTHR, row = item / VPR, vec = item % VPR;
+        raw[it] = bload16(src, (uint32_t)(row * rs + vec * 16));
+    }
+#pragma unroll
+    for (int it = 0; it < ITEMS / NTHR; ++it) {
+        const int item = tid + it * NTHR, row = item / VPR, vec = item % VPR;
+        float f[VEC];
+        Vec<F32>::to_float(raw[it], f);
+        const bool live = row < nval;
+        const float scale = MODE == 2 ? (live ? 1.f / den[row] : 0.f) : 1.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            if (MODE == 1) f[e] = live ? phi<F32>(f[e]) : 0.f;
+            if (MODE == 2) f[e] *= scale;
+        }
+        float *p = dst + row * LD + vec * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) *reinterpret_cast<f32x4 *>(p + e) = (f32x4){f[e], f[e + 1], f[e + 2], f[e + 3]};
+    }
+}
+
+// The adjoint part of one chunk: D_t and dD_t of its tokens (to den / dden),
+// and  dR_c = sum_t g_t dn_t^T,  dr_c = sum_t g_t dD_t  to adjoint slot
+// nch - c (every column block holds dr_c).  Wave w owns tokens 16 w .. + 15
+// for the normalisers; the state tiles are split over the waves.
+template <bool F32, int D>
+__global__ void __launch_bounds__(NTHR) k_bwd_prep(const BwdArgs a)
+{
+    constexpr int C = 64, LD = D + 4, KT = D / 16, DV = D < 64 ? D : 64, SL = DV * D + D, ES = F32 ? 4 : 2;
+    __shared__ __attribute__((aligned(16))) float sm[3 * C * LD + C];
+    float *Gs = sm, *Fs = sm + C * LD, *Ns = sm + 2 * C * LD, *dDs = sm + 3 * C * LD;
+    const int tid = threadIdx.x, lane = tid % WAVE, r = lane % 16, g = lane / 16;
+    const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
+    const int ch = blockIdx.x % a.nch, bh = blockIdx.x / a.nch;
+    const int b = bh / a.H, h = bh % a.H;
+    const int t0 = ch * C, nval = min(C, a.N - t0);
+    const RowView qv{(const char *)a.q + (b * a.sqb + h * a.sqh) * ES, a.sqn * ES, (a.N - 1) * a.sqn * ES + D * ES};
+    const RowView kv{(const char *)a.k + (b * a.skb + h * a.skh) * ES, a.skn * ES, (a.N - 1) * a.skn * ES + D * ES};
+    const RowView ov{(const char *)(a.out + b * a.sob + h * a.soh), a.son * 4, (a.N - 1) * a.son * 4 + D * 4};
+    const RowView dov{(const char *)(a.dout + b * a.sdb + h * a.sdh), a.sdn * 4, (a.N - 1) * a.sdn * 4 + D * 4};
+    bwd_stage<F32, D, 1>(qv.at(t0), qv.rs, Gs, nval, tid);
+    bwd_stage<F32, D, 1>(kv.at(t0), kv.rs, Fs, nval, tid);
+    bwd_stage<true, D, 0>(dov.at(t0), dov.rs, Ns, nval, tid);
+    __syncthreads();
+
+    // ---- normaliser of token t = 16 w + r: g_t . S_c + sum_{s <= t} P_ts + eps
+    const int t = 16 * w + r;
+    const float *sc = a.fwd + ((int64_t)bh * a.P * a.NS + ch) * SL + DV * D;   // S_c (column block 0)
+    float rsum = 0.f, gs = 0.f, dot = 0.f;
+#pragma unroll
+    for (int sa = 0; sa < 4; ++sa) {
+        if (sa > w) break;
+        f32x4 pt = {0.f, 0.f, 0.f, 0.f};   // P^T: keys 16 sa + 4g + i, query t
+#pragma unroll
+        for (int js = 0; js < KT; ++js)
+            pt = mma1(pt, nat4(Fs + (16 * sa + r) * LD + 16 * js + 4 * g), nat4(Gs + t * LD + 16 * js + 4 * g));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rsum += (16 * sa + 4 * g + i <= t) ? pt[i] : 0.f;
+    }
+    const rsrc_t orow = ov.at(t0 + t, t < nval);
+#pragma unroll
+    for (int js = 0; js < KT; ++js) {
+        const f32x4 gq = nat4(Gs + t * LD + 16 * js + 4 * g);
+        const f32x4 s4 = *reinterpret_cast<const f32x4 *>(sc + 16 * js + 4 * g);
+        const f32x4 o4 = __builtin_bit_cast(f32x4, bload16(orow, (uint32_t)((16 * js + 4 * g) * 4)));
+        const f32x4 d4 = nat4(Ns + t * LD + 16 * js + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            gs += gq[i] * s4[i];
+            dot += d4[i] * o4[i];
+        }
+    }
+#pragma unroll
+    for (int m = 16; m < WAVE; m <<= 1) {
+        rsum += __shfl_xor(rsum, m);
+        gs += __shfl_xor(gs, m);
+        dot += __shfl_xor(dot, m);
+    }
+    const bool live = t < nval;
+    const float den = gs + rsum + a.eps;
+    const float ddn = live ? -dot / den : 0.f;
+    const float inv = live ? 1.f / den : 0.f;
+    if (g == 0) {
+        dDs[t] = ddn;
+        if (live) {
+            a.den[(int64_t)bh * a.N + t0 + t] = den;
+            a.dden[(int64_t)bh * a.N + t0 + t] = ddn;
+        }
+    }
+    // dn_t = dout_t / D_t in place (lane (r, g) holds dims 16 js + 4g .. + 3)
+#pragma unroll
+    for (int js = 0; js < KT; ++js) {
+        float *p = Ns + t * LD + 16 * js + 4 * g;
+        *reinterpret_cast<f32x4 *>(p) = nat4(p) * inv;
+    }
+    __syncthreads();
+
+    // ---- dR_c tiles (rows j, columns c), split over the waves
+    float *slot0 = a.rev + ((int64_t)bh * a.P * a.NS + (a.nch - ch)) * SL;
+    for (int tile = w; tile < KT * KT; tile += NWAVE) {
+        const int jt = tile / KT, ct = tile % KT;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ta = 0; ta < 4; ++ta) acc = mma1(acc, trf(Gs, LD, 16 * ta, 16 * jt, r, g), trf(Ns, LD, 16 * ta, 16 * ct, r, g));
+        const int c = 16 * ct + r;
+        float *sl = slot0 + (int64_t)(c / DV) * a.NS * SL + c % DV;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sl[(16 * jt + 4 * g + i) * DV] = acc[i];
+    }
+    // ---- dr_c = sum_t g_t dD_t, into every column block's slot
+    if (tid < D) {
+        float acc = 0.f;
+        for (int tt = 0; tt < C; ++tt) acc += Gs[tt * LD + tid] * dDs[tt];
+        for (int p = 0; p < a.P; ++p) slot0[(int64_t)p * a.NS * SL + DV * D + tid] = acc;
+    }
+}
+
+// dq, dk, dv of one chunk from the state before it, the adjoint state after
+// it and the chunk's own tokens.  Wave w owns tokens 16 w .. + 15: their dq
+// (as queries) and their dk, dv (as keys).
+template <bool F32, int D>
+__global__ void __launch_bounds__(NTHR) k_bwd_chunk(const BwdArgs a)
+{
+    constexpr int C = 64, LD = D + 4, KT = D / 16, DV = D < 64 ? D : 64, SL = DV * D + D, ES = F32 ? 4 : 2;
+    __shared__ __attribute__((aligned(16))) float sm[4 * C * LD + C];
+    float *Gs = sm, *Fs = sm + C * LD, *Vs = sm + 2 * C * LD, *Ns = sm + 3 * C * LD, *dDs = sm + 4 * C * LD;
+    const int tid = threadIdx.x, lane = tid % WAVE, r = lane % 16, g = lane / 16;
+    const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
+    const int ch = blockIdx.x % a.nch, bh = blockIdx.x / a.nch;
+    const int b = bh / a.H, h = bh % a.H;
+    const int t0 = ch * C, nval = min(C, a.N - t0);
+    const RowView qv{(const char *)a.q + (b * a.sqb + h * a.sqh) * ES, a.sqn * ES, (a.N - 1) * a.sqn * ES + D * ES};
+    const RowView kv{(const char *)a.k + (b * a.skb + h * a.skh) * ES, a.skn * ES, (a.N - 1) * a.skn * ES + D * ES};
+    const RowView vv{(const char *)a.v + (b * a.svb + h * a.svh) * ES, a.svn * ES, (a.N - 1) * a.svn * ES + D * ES};
+    const RowView dov{(const char *)(a.dout + b * a.sdb + h * a.sdh), a.sdn * 4, (a.N - 1) * a.sdn * 4 + D * 4};
+    const float *denc = a.den + (int64_t)bh * a.N + t0;
+    bwd_stage<F32, D, 1>(qv.at(t0), qv.rs, Gs, nval, tid);
+    bwd_stage<F32, D, 1>(kv.at(t0), kv.rs, Fs, nval, tid);
+    bwd_stage<F32, D, 0>(vv.at(t0), vv.rs, Vs, nval, tid);
+    bwd_stage<true, D, 2>(dov.at(t0), dov.rs, Ns, nval, tid, denc);
+    if (tid < C) dDs[tid] = tid < nval ? a.dden[(int64_t)bh * a.N + t0 + tid] : 0.f;
+    __syncthreads();
+
+    const int me = 16 * w + r;   // this lane's token (query for dq, key for dk / dv)
+    const bool live = me < nval;
+    // the state before the chunk (Z_c, S_c) and the adjoint state after it
+    // (R', r'), column block p at + p * NS * SL
+    const float *zc = a.fwd + ((int64_t)bh * a.P * a.NS + ch) * SL;
+    const float *rc = a.rev + ((int64_t)bh * a.P * a.NS + (a.nch - 1 - ch)) * SL;
+    auto zrow4 = [&](const float *st, int j, int c0) {   // st[j][c0 .. c0 + 3]
+        return *reinterpret_cast<const f32x4 *>(st + (int64_t)(c0 / DV) * a.NS * SL + j * DV + c0 % DV);
+    };
+
+    // ---- dq (query me): rows j = 16 jt + 4g + i, column me
+    {
+        f32x4 acc[KT];
+        const float ddt = dDs[me];
+#pragma unroll
+        for (int jt = 0; jt < KT; ++jt) {
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int cs = 0; cs < KT; ++cs)
+                x = mma1(x, zrow4(zc, 16 * jt + r, 16 * cs + 4 * g), nat4(Ns + me * LD + 16 * cs + 4 * g));
+            const f32x4 s4 = *reinterpret_cast<const f32x4 *>(zc + DV * D + 16 * jt + 4 * g);
+            acc[jt] = x + s4 * ddt;
+        }
+#pragma unroll
+        for (int sa = 0; sa < 4; ++sa) {
+            if (sa > w) break;
+            f32x4 at = {0.f, 0.f, 0.f, 0.f};   // A^T: keys 16 sa + 4g + i, query me
+#pragma unroll
+            for (int cs = 0; cs < KT; ++cs)
+                at = mma1(at, nat4(Vs + (16 * sa + r) * LD + 16 * cs + 4 * g), nat4(Ns + me * LD + 16 * cs + 4 * g));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) at[i] = (16 * sa + 4 * g + i <= me) ? at[i] + ddt : 0.f;
+#pragma unroll
+            for (int jt = 0; jt < KT; ++jt) acc[jt] = mma1(acc[jt], trf(Fs, LD, 16 * sa, 16 * jt, r, g), at);
+        }
+        float *dst = a.dq + b * a.gqb + h * a.gqh + (int64_t)(t0 + me) * a.gqn;
+        if (live) {
+#pragma unroll
+            for (int jt = 0; jt < KT; ++jt) {
+                const f32x4 gq = nat4(Gs + me * LD + 16 * jt + 4 * g);
+                f32x4 dphi;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dphi[i] = fminf(gq[i], 1.f);
+                *reinterpret_cast<f32x4 *>(dst + 16 * jt + 4 * g) = acc[jt] * dphi;
+            }
+        }
+    }
+    // ---- dk (key me): rows j, column me
+    {
+        f32x4 acc[KT];
+#pragma unroll
+        for (int jt = 0; jt < KT; ++jt) {
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int cs = 0; cs < KT; ++cs)
+                x = mma1(x, zrow4(rc, 16 * jt + r, 16 * cs + 4 * g), nat4(Vs + me * LD + 16 * cs + 4 * g));
+            acc[jt] = x + *reinterpret_cast<const f32x4 *>(rc + DV * D + 16 * jt + 4 * g);
+        }
+#pragma unroll
+        for (int ta = 0; ta < 4; ++ta) {
+            if (ta < w) continue;
+            f32x4 at = {0.f, 0.f, 0.f, 0.f};   // A: queries 16 ta + 4g + i, key me
+#pragma unroll
+            for (int cs = 0; cs < KT; ++cs)
+                at = mma1(at, nat4(Ns + (16 * ta + r) * LD + 16 * cs + 4 * g), nat4(Vs + me * LD + 16 * cs + 4 * g));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tq = 16 * ta + 4 * g + i;
+                at[i] = tq >= me ? at[i] + dDs[tq] : 0.f;
+            }
+#pragma unroll
+            for (int jt = 0; jt < KT; ++jt) acc[jt] = mma1(acc[jt], trf(Gs, LD, 16 * ta, 16 * jt, r, g), at);
+        }
+        float *dst = a.dk + b * a.gkb + h * a.gkh + (int64_t)(t0 + me) * a.gkn;
+        if (live) {
+#pragma unroll
+            for (int jt = 0; jt < KT; ++jt) {
+                const f32x4 fk = nat4(Fs + me * LD + 16 * jt + 4 * g);
+                f32x4 dphi;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dphi[i] = fminf(fk[i], 1.f);
+                *reinterpret_cast<f32x4 *>(dst + 16 * jt + 4 * g) = acc[jt] * dphi;
+            }
+        }
+    }
+    // ---- dv: rows s = 16 w + 4g + i, columns c = 16 ct + r
+    {
+        f32x4 acc[KT];
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct) {
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            const int c = 16 * ct + r;
+            const float *rcol = rc + (int64_t)(c / DV) * a.NS * SL + c % DV;
+#pragma unroll
+            for (int js = 0; js < KT; ++js) {
+                f32x4 rb;   // R'[16 js + 4g + i][c]
+#pragma unroll
+                for (int i = 0; i < 4; ++i) rb[i] = rcol[(16 * js + 4 * g + i) * DV];
+                x = mma1(x, nat4(Fs + me * LD + 16 * js + 4 * g), rb);
+            }
+            acc[ct] = x;
+        }
+#pragma unroll
+        for (int ta = 0; ta < 4; ++ta) {
+            if (ta < w) continue;
+            f32x4 pt = {0.f, 0.f, 0.f, 0.f};   // P: queries 16 ta + 4g + i, key me
+#pragma unroll
+            for (int js = 0; js < KT; ++js)
+                pt = mma1(pt, nat4(Gs + (16 * ta + r) * LD + 16 * js + 4 * g), nat4(Fs + me * LD + 16 * js + 4 * g));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pt[i] = (16 * ta + 4 * g + i >= me) ? pt[i] : 0.f;
+#pragma unroll
+            for (int ct = 0; ct < KT; ++ct) acc[ct] = mma1(acc[ct], pt, trf(Ns, LD, 16 * ta, 16 * ct, r, g));
+        }
+        float *dst = a.dv + b * a.gvb + h * a.gvh + (int64_t)t0 * a.gvn;
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s = 16 * w + 4 * g + i;
+                if (s < nval) dst[(int64_t)s * a.gvn + 16 * ct + r] = acc[ct][i];
+            }
+    }
+}
+
 // ------------------------------------------------------------------ host side
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -2911,6 +3227,43 @@ size_t la_causal_fwd_workspace(int B, int H, int N, int d, int chunk)
 }  // extern "C"
 
 namespace {
+// ---- backward pass: workspace = forward slots, adjoint slots (nch + 1 per
+// head and column block each), then D_t and dD_t per token
+struct BwdPlan {
+    int nch, DV, P, NS;
+    size_t SL, slots_bytes, den_off, dden_off, total;
+};
+BwdPlan plan_bwd(int B, int H, int N, int d)
+{
+    BwdPlan pl;
+    pl.nch = (N + 63) / 64;
+    pl.DV = cols_per_wg(d);
+    pl.P = d / pl.DV;
+    pl.NS = pl.nch + 1;
+    pl.SL = (size_t)pl.DV * d + d;
+    const int64_t BH = (int64_t)B * H;
+    pl.slots_bytes = align256((size_t)BH * pl.P * pl.NS * pl.SL * 4);
+    pl.den_off = 2 * pl.slots_bytes;
+    pl.dden_off = pl.den_off + align256((size_t)BH * N * 4);
+    pl.total = N > 0 ? pl.dden_off + align256((size_t)BH * N * 4) : 0;
+    return pl;
+}
+
+// bytes from p to one past the last element of a [B, H, N, d] tensor
+size_t extent(la_strides s, int B, int H, int N, int d, size_t es)
+{
+    if (B == 0 || H == 0 || N == 0) return 0;
+    return ((size_t)(B - 1) * s.b + (size_t)(H - 1) * s.h + (size_t)(N - 1) * s.n + d) * es;
+}
+
+// Memory calls run one segment at a time (a few thousand tokens per head):
+// fewer, longer token groups than the non-causal plan, so that a group's
+// published state does not outweigh its inputs, and shorter apply
+// workgroups, so that the readout still covers the chip.
+constexpr int MEM_GROUP_TARGET = 128;
+constexpr int MEM_APPLY_CHUNKS = 2;
+Plan plan_memory(int B, int H, int N, int d, la_dtype dt) { return plan_noncausal(B, H, N, d, dt, MEM_GROUP_TARGET); }
+
 la_status causal_impl(const void *q, la_strides sq, const void *k, la_strides sk,
                       const void *v, la_strides sv, la_dtype dt,
                       float *out, la_strides so,
@@ -3120,13 +3473,113 @@ la_status la_noncausal_fwd(const void *q, la_strides sq, const void *k, la_strid
     return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }
 
-// Memory calls run one segment at a time (a few thousand tokens per head):
-// fewer, longer token groups than the non-causal plan, so that a group's
-// published state does not outweigh its inputs, and shorter apply
-// workgroups, so that the readout still covers the chip.
-constexpr int MEM_GROUP_TARGET = 128;
-constexpr int MEM_APPLY_CHUNKS = 2;
-Plan plan_memory(int B, int H, int N, int d, la_dtype dt) { return plan_noncausal(B, H, N, d, dt, MEM_GROUP_TARGET); }
+size_t la_causal_bwd_workspace(int B, int H, int N, int d)
+{
+    if (check_common(B, H, N, d, LA_BF16, 0.f) != LA_OK) return 0;
+    return plan_bwd(B, H, N, d).total;
+}
+
+la_status la_causal_bwd(const void *q, la_strides sq, const void *k, la_strides sk,
+                        const void *v, la_strides sv, la_dtype dt,
+                        const float *out, la_strides so, const float *dout, la_strides sdo,
+                        int B, int H, int N, int d, float eps,
+                        const float *z_in, const float *s_in, const float *dz_out, const float *ds_out,
+                        float *dq, la_strides sdq, float *dk, la_strides sdk, float *dv, la_strides sdv,
+                        float *dz_in, float *ds_in,
+                        void *workspace, size_t ws_bytes, void *hip_stream)
+{
+    la_status st = check_common(B, H, N, d, dt, eps);
+    if (st != LA_OK) return st;
+    const size_t es = dt == LA_F32 ? 4 : 2;
+    if (N > 0) {
+        if ((st = check_tensor(q, sq, es)) != LA_OK) return st;
+        if ((st = check_tensor(k, sk, es)) != LA_OK) return st;
+        if ((st = check_tensor(v, sv, es)) != LA_OK) return st;
+        if ((st = check_tensor(out, so, 4)) != LA_OK) return st;
+        if ((st = check_tensor(dout, sdo, 4)) != LA_OK) return st;
+        if ((st = check_tensor(dq, sdq, 4)) != LA_OK) return st;
+        if ((st = check_tensor(dk, sdk, 4)) != LA_OK) return st;
+        if ((st = check_tensor(dv, sdv, 4)) != LA_OK) return st;
+    }
+    for (const void *p : {(const void *)z_in, (const void *)s_in, (const void *)dz_out, (const void *)ds_out,
+                          (const void *)dz_in, (const void *)ds_in})
+        if (p && !aligned16(p)) return LA_ERR_ALIGN;
+    const int64_t BH = (int64_t)B * H;
+    const size_t zb = (size_t)BH * d * d * 4, sb = (size_t)BH * d * 4;
+    // the gradients overlap no input and no other gradient
+    {
+        const void *ins[] = {q, k, v, out, dout, z_in, s_in, dz_out, ds_out};
+        const size_t in_n[] = {extent(sq, B, H, N, d, es), extent(sk, B, H, N, d, es), extent(sv, B, H, N, d, es),
+                               extent(so, B, H, N, d, 4), extent(sdo, B, H, N, d, 4), zb, sb, zb, sb};
+        void *outs[] = {dq, dk, dv, dz_in, ds_in};
+        const size_t out_n[] = {extent(sdq, B, H, N, d, 4), extent(sdk, B, H, N, d, 4), extent(sdv, B, H, N, d, 4),
+                                zb, sb};
+        for (int i = 0; i < 5; ++i) {
+            for (int j = 0; j < 9; ++j)
+                if (overlaps(outs[i], out_n[i], ins[j], in_n[j])) return LA_ERR_ALIAS;
+            for (int j = i + 1; j < 5; ++j)
+                if (overlaps(outs[i], out_n[i], outs[j], out_n[j])) return LA_ERR_ALIAS;
+        }
+    }
+    const BwdPlan pl = plan_bwd(B, H, N, d);
+    if (ws_bytes < pl.total || (pl.total > 0 && !workspace)) return LA_ERR_WORKSPACE;
+    if (BH == 0) return LA_OK;
+    hipStream_t stream = (hipStream_t)hip_stream;
+    (void)hipGetLastError();
+    char *ws = (char *)workspace;
+    const bool f32 = dt == LA_F32;
+    // the slot kernels' view: (Z_c, S_c) slots, scans, totals
+    Args a = make_args(q, sq, k, sk, v, sv, nullptr, la_strides{0, 0, 0}, B, H, N, eps);
+    a.P = pl.P;
+    a.NS = pl.NS;
+    if (N == 0) {
+        // no token: the gradient reaching the carried-in state is dz_out
+        a.z_in = dz_out; a.s_in = ds_out; a.z_out = dz_in; a.s_out = ds_in;
+        if (dz_in || ds_in) launch_slots(d, a, BH, pl.P, 0, 1, stream);
+        return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
+    }
+    float *fwd = (float *)ws, *rev = (float *)(ws + pl.slots_bytes);
+    // 1) the forward state before every chunk: chunk partial states into
+    //    slots 1.., then the scan (slot c = state_in + chunks 0 .. c-1)
+    a.part = fwd; a.G = pl.nch; a.L = 64; a.slot0 = 1;
+    a.z_in = z_in; a.s_in = s_in;
+    dispatch(f32, d, 64, 0, a, (int)(BH * pl.P * pl.nch), stream);
+    launch_slots(d, a, BH, pl.P, pl.NS, 0, stream);
+    // 2) normalisers and the chunks' adjoint parts (reverse-indexed slots)
+    BwdArgs ba;
+    memset(&ba, 0, sizeof(ba));
+    ba.q = q; ba.k = k; ba.v = v; ba.out = out; ba.dout = dout;
+    ba.sqb = sq.b; ba.sqh = sq.h; ba.sqn = sq.n; ba.skb = sk.b; ba.skh = sk.h; ba.skn = sk.n;
+    ba.svb = sv.b; ba.svh = sv.h; ba.svn = sv.n; ba.sob = so.b; ba.soh = so.h; ba.son = so.n;
+    ba.sdb = sdo.b; ba.sdh = sdo.h; ba.sdn = sdo.n;
+    ba.dq = dq; ba.dk = dk; ba.dv = dv;
+    ba.gqb = sdq.b; ba.gqh = sdq.h; ba.gqn = sdq.n; ba.gkb = sdk.b; ba.gkh = sdk.h; ba.gkn = sdk.n;
+    ba.gvb = sdv.b; ba.gvh = sdv.h; ba.gvn = sdv.n;
+    ba.B = B; ba.H = H; ba.N = N; ba.nch = pl.nch; ba.P = pl.P; ba.NS = pl.NS; ba.eps = eps;
+    ba.fwd = fwd; ba.rev = rev;
+    ba.den = (float *)(ws + pl.den_off); ba.dden = (float *)(ws + pl.dden_off);
+    const dim3 grid((unsigned)(BH * pl.nch));
+#define LA_BWD(KERN, F, DD) hipLaunchKernelGGL((KERN<F, DD>), grid, dim3(NTHR), 0, stream, ba)
+#define LA_BWD_ALL(KERN) \
+    if (f32) { if (d == 32) LA_BWD(KERN, true, 32); else if (d == 64) LA_BWD(KERN, true, 64); else LA_BWD(KERN, true, 128); } \
+    else { if (d == 32) LA_BWD(KERN, false, 32); else if (d == 64) LA_BWD(KERN, false, 64); else LA_BWD(KERN, false, 128); }
+    LA_BWD_ALL(k_bwd_prep)
+    // 3) the gradient reaching the carried-in state: dz_out + every chunk's part
+    a.z_in = dz_out; a.s_in = ds_out; a.z_out = dz_in; a.s_out = ds_in;
+    if (dz_in || ds_in) {
+        Args t = a;
+        t.part = rev + pl.SL;   // slots 1 .. nch of every (head, column block)
+        launch_slots(d, t, BH, pl.P, pl.nch, 1, stream);
+    }
+    // 4) the adjoint state after every chunk (slot nch - 1 - c)
+    a.part = rev;
+    launch_slots(d, a, BH, pl.P, pl.NS, 0, stream);
+    // 5) dq, dk, dv of every chunk
+    LA_BWD_ALL(k_bwd_chunk)
+#undef LA_BWD_ALL
+#undef LA_BWD
+    return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
+}
 
 size_t la_memory_workspace(int B, int H, int N, int d)
 {

@@ -93,3 +93,59 @@ def rowwise_rel_err(x, y):
     with np.errstate(divide="ignore", invalid="ignore"):
         r = np.where(den > 0, num / np.where(den > 0, den, 1.0), np.where(num > 0, np.inf, 0.0))
     return float(r.max()) if r.size else 0.0
+
+
+def chunked_bwd(q, k, v, dout, eps, C, z_in=None, s_in=None, dz_out=None, ds_out=None):
+    """Backward pass of one head in chunk form with every chunk state
+    materialised (mode 4 of "How to accelerate causal linear attention",
+    applied to the forward state and to the adjoint state).  With
+    A_ts = v_s . dn_t + dD_t and P_ts = g_t . f_s inside a chunk (inclusive
+    masks), (Z_c, S_c) the state before chunk c and (R_c, r_c) the adjoint
+    state after it:
+      dq_t = phi'(q_t) (Z_c dn_t + S_c dD_t + sum_{s<=t} A_ts f_s)
+      dk_s = phi'(k_s) (R_c v_s + r_c + sum_{t>=s} A_ts g_t)
+      dv_s = R_c^T f_s + sum_{t>=s} P_ts dn_t
+    Returns (dq, dk, dv, dz_in, ds_in)."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    N, d = q.shape
+    g, f = phi(q), phi(k)
+    dphi_q, dphi_k = np.minimum(g, 1.0), np.minimum(f, 1.0)
+    chunks = [slice(c0, min(c0 + C, N)) for c0 in range(0, N, C)]
+    # forward chunk states, then the normalisers
+    Zs, Ss = [], []
+    Z = np.zeros((d, d)) if z_in is None else _f64(z_in).copy()
+    S = np.zeros(d) if s_in is None else _f64(s_in).copy()
+    den = np.zeros(N)
+    num = np.zeros((N, d))
+    for sl in chunks:
+        Zs.append(Z.copy())
+        Ss.append(S.copy())
+        n = sl.stop - sl.start
+        M = np.tril(np.ones((n, n)))
+        P = (g[sl] @ f[sl].T) * M
+        den[sl] = g[sl] @ S + P.sum(1) + eps
+        num[sl] = g[sl] @ Z + P @ v[sl]
+        Z = Z + f[sl].T @ v[sl]
+        S = S + f[sl].sum(0)
+    out = num / den[:, None]
+    dn = dout / den[:, None]
+    dD = -(dout * out).sum(1) / den
+    # adjoint chunk states (after each chunk), from the last chunk back
+    R = np.zeros((d, d)) if dz_out is None else _f64(dz_out).copy()
+    r = np.zeros(d) if ds_out is None else _f64(ds_out).copy()
+    Rs, rs = [None] * len(chunks), [None] * len(chunks)
+    for i in reversed(range(len(chunks))):
+        sl = chunks[i]
+        Rs[i], rs[i] = R.copy(), r.copy()
+        R = R + g[sl].T @ dn[sl]
+        r = r + g[sl].T @ dD[sl]
+    dq, dk, dv = np.zeros((N, d)), np.zeros((N, d)), np.zeros((N, d))
+    for i, sl in enumerate(chunks):
+        n = sl.stop - sl.start
+        M = np.tril(np.ones((n, n)))
+        A = (dn[sl] @ v[sl].T + dD[sl][:, None]) * M
+        P = (g[sl] @ f[sl].T) * M
+        dq[sl] = dphi_q[sl] * (dn[sl] @ Zs[i].T + dD[sl][:, None] * Ss[i][None, :] + A @ f[sl])
+        dk[sl] = dphi_k[sl] * (v[sl] @ Rs[i].T + rs[i][None, :] + A.T @ g[sl])
+        dv[sl] = f[sl] @ Rs[i] + P.T @ dn[sl]
+    return dq, dk, dv, R, r

@@ -34,7 +34,8 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"la_status_str", "la_version", "la_causal_fwd_workspace", "la_causal_fwd",
                           "la_decode_step", "la_noncausal_workspace", "la_noncausal_fwd",
                           "la_memory_workspace", "la_memory_fwd", "la_causal_fwd_unnormalized",
-                          "la_causal_fwd_noalloc", "la_noalloc_scratch_bytes"}
+                          "la_causal_fwd_noalloc", "la_noalloc_scratch_bytes",
+                          "la_causal_bwd_workspace", "la_causal_bwd"}
     raw = ctypes.CDLL(la.library_path())
     for n in names:
         assert hasattr(raw, n), n
@@ -217,3 +218,33 @@ def test_noalloc_validation(lib):
     big = (1, 64, 1 << 16, 128)
     assert la.la_causal_fwd_workspace(*big) > la.la_noalloc_scratch_bytes()
     assert call(*big) == WS
+
+
+@no_device
+def test_backward_validation(lib):
+    vp = ctypes.c_void_p
+    B, H, N, d = 1, 2, 128, 64
+    st = la_strides(H * N * d, N * d, d)
+
+    def call(**kw):
+        p = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, out=FAKE + 0x300000, dout=FAKE + 0x400000,
+                 dq=FAKE + 0x500000, dk=FAKE + 0x600000, dv=FAKE + 0x700000, dz_in=None, ds_in=None,
+                 ws=FAKE + 0x800000, ws_bytes=1 << 30, d=d, eps=1e-6, dt=la.LA_BF16)
+        p.update(kw)
+        x = lambda a: None if a is None else vp(a)
+        return lib.la_causal_bwd(x(p["q"]), st, x(p["k"]), st, x(p["v"]), st, p["dt"], x(p["out"]), st,
+                                 x(p["dout"]), st, B, H, N, p["d"], p["eps"], None, None, None, None,
+                                 x(p["dq"]), st, x(p["dk"]), st, x(p["dv"]), st, x(p["dz_in"]), x(p["ds_in"]),
+                                 x(p["ws"]), p["ws_bytes"], None)
+    assert call(d=48) == UNSUP
+    assert call(dt=5) == DTYPE
+    assert call(eps=-1.0) == VALUE
+    assert call(dout=None) == NULL_
+    assert call(dv=None) == NULL_
+    assert call(dk=FAKE + 0x600004) == ALIGN
+    assert call(dq=FAKE + 0x100000) == ALIAS          # dq over k
+    assert call(dk=FAKE + 0x500000 + 64) == ALIAS     # dk over dq
+    assert call(ws=None) == WS
+    assert call(ws_bytes=64) == WS
+    assert la.la_causal_bwd_workspace(B, H, N, d) > 0
+    assert la.la_causal_bwd_workspace(B, H, 0, d) == 0

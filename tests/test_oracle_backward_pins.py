@@ -197,3 +197,21 @@ def test_constant_v_without_eps_has_no_q_or_k_gradient():
     scale = np.abs(dv).max()
     assert np.abs(dq).max() < 1e-12 * scale and np.abs(dk).max() < 1e-12 * scale
     assert scale > 0.1
+
+
+@pytest.mark.parametrize("C", [1, 3, 16, 64])
+def test_backward_equals_chunked_materialised_form(C):
+    # the chunk decomposition (every chunk's forward and adjoint state
+    # materialised, then each chunk on its own) equals the recurrent oracle
+    from reference_forms import chunked_bwd
+    BH, N, d, eps = 2, 150, 8, 1e-6
+    q, k, v = (_grid((BH, N, d), 800 + i, scale=0.5) for i in range(3))
+    dout = _grid((BH, N, d), 810)
+    rng = np.random.default_rng(811)
+    z0, s0 = rng.standard_normal((BH, d, d)), rng.random((BH, d)) + 1
+    dzN, dsN = rng.standard_normal((BH, d, d)), rng.standard_normal((BH, d))
+    got = oracle.causal_bwd(q, k, v, dout, eps, z0, s0, dzN, dsN)
+    for h in range(BH):
+        ref = chunked_bwd(q[h], k[h], v[h], dout[h], eps, C, z0[h], s0[h], dzN[h], dsN[h])
+        for i in range(5):
+            assert _rel(got[i][h], ref[i]) < 1e-10, (h, i, _rel(got[i][h], ref[i]))
