@@ -16,8 +16,10 @@ SRC = os.path.join(ROOT, "oracle", "linattn_oracle.c")
 MUTANTS = {
     "phi_drops_plus_one": ("x > 0.0 ? x + 1.0 : exp(x)", "x > 0.0 ? x : exp(x)"),
     "phi_branch_flipped": ("x > 0.0 ? x + 1.0 : exp(x)", "x < 0.0 ? x + 1.0 : exp(x)"),
-    "state_update_transposed": ("for (c = 0; c < d; ++c) Z[j * d + c] += f[j] * (double)vt[c];",
-                                "for (c = 0; c < d; ++c) Z[c * d + j] += f[j] * (double)vt[c];"),
+    "state_update_transposed": ("for (c = 0; c < d; ++c) Z[j * d + c] += f[j] * (double)vt[c];\n"
+                                "                S[j] += f[j];\n            }\n            if (!out)",
+                                "for (c = 0; c < d; ++c) Z[c * d + j] += f[j] * (double)vt[c];\n"
+                                "                S[j] += f[j];\n            }\n            if (!out)"),
     "key_sum_without_phi": ("                S[j] += f[j];\n            }\n            if (!out)",
                             "                S[j] += (double)kt[j];\n            }\n            if (!out)"),
     "eps_dropped": ("                den += eps;\n                for (c = 0; c < d; ++c) {\n                    double num = 0.0;\n                    for (j = 0; j < d; ++j) num += g[j] * Z[j * d + c];\n                    ot[c]",
@@ -26,7 +28,14 @@ MUTANTS = {
                            "for (j = 0; j < d; ++j) num += g[j] * Z[c * d + j];\n                    ot[c] = num / den;\n                }\n            }\n        }"),
     "query_uses_key": ("for (j = 0; j < d; ++j) g[j] = phi((double)qt[j]);\n            {",
                        "for (j = 0; j < d; ++j) g[j] = phi((double)kt[j]);\n            {"),
-    "state_in_ignored": ("if (z_in) memcpy(Z,", "if (0) memcpy(Z,"),
+    "state_in_ignored": ("if (z_in) memcpy(Z, z_in + h * d * d, (size_t)(d * d) * sizeof(double));\n"
+                         "        if (s_in) memcpy(S, s_in + h * d, (size_t)d * sizeof(double));\n"
+                         "        for (t = 0; t < N; ++t) {\n            const float *kt = k + (h * N + t) * d;\n"
+                         "            const float *vt = v + (h * N + t) * d;\n            const float *qt",
+                         "if (0) memcpy(Z, z_in + h * d * d, (size_t)(d * d) * sizeof(double));\n"
+                         "        if (s_in) memcpy(S, s_in + h * d, (size_t)d * sizeof(double));\n"
+                         "        for (t = 0; t < N; ++t) {\n            const float *kt = k + (h * N + t) * d;\n"
+                         "            const float *vt = v + (h * N + t) * d;\n            const float *qt"),
     "exclusive_causality": ("            const float *kt = k + (h * N + t) * d;\n            const float *vt = v + (h * N + t) * d;\n            const float *qt = q + (h * N + t) * d;",
                             "            const float *kt = k + (h * N + t) * d;\n            const float *vt = v + (h * N + t) * d;\n            const float *qt = q + (h * N + (t + 1 < N ? t + 1 : t)) * d;"),
     "decode_skips_key_sum": ("            Sh[j] += fj;", "            Sh[j] += 0.0 * fj;"),
