@@ -3053,9 +3053,13 @@ Plan plan_noncausal(int B, int H, int N, int d, la_dtype dt, int target = 1024)
 
 // State-only causal calls (out = NULL, the prefill): the non-causal partial
 // states of the token shares, then their sum added to the carried-in state.
+// Fewer, longer shares than the non-causal plan: the published states are
+// then small next to k and v (B4 H8 N4096 d64: 14.2 us with about 256
+// workgroups, 21.2 us with 1024, 19.2 us with 128).
+constexpr int PREFILL_TARGET_WGS = 256;
 Plan plan_state(int B, int H, int N, int d, la_dtype dt)
 {
-    Plan pl = plan_noncausal(B, H, N, d, dt);
+    Plan pl = plan_noncausal(B, H, N, d, dt, PREFILL_TARGET_WGS);
     pl.fin_bytes = 0;
     pl.total = N > 0 ? pl.part_bytes : 0;
     return pl;
