@@ -350,9 +350,10 @@ def bench_prefill(args, torch, la, inp):
         prewarm(lambda _: call(), 1, args.prewarm_s)
         ms = time_steps(lambda _: call(), steps, warm, 1) / steps
         b = w.B * w.H * (N * 2 * w.d * w.dtype.itemsize + (w.d * w.d + w.d) * 4)
+        traffic = measured_traffic("prefill_bf16_b4h8n4096d64") if label == "headline_shape" else None
         res[label] = {"shape": [w.B, w.H, N, w.d], "ms_per_call": round(ms, 5),
                       "value": round(w.B * w.H * N / (ms * 1e-3), 1), "unit": "head-tokens/s",
-                      "alg_bytes_per_call": b, "roofline": roofline(b, ms, None)}
+                      "alg_bytes_per_call": b, "roofline": roofline(b, ms, traffic)}
     return res
 
 
@@ -376,7 +377,7 @@ def bench_backward(args, torch, la, inp):
     b = w.head_tokens * (3 * w.d * w.dtype.itemsize + 2 * 4 * w.d + 3 * 4 * w.d)
     return {"workload": w.name + "_backward", "value": round(w.head_tokens / (ms * 1e-3), 1),
             "unit": "head-tokens/s", "ms_per_step": round(ms, 5), "alg_bytes_per_call": b,
-            "roofline": roofline(b, ms, None)}
+            "roofline": roofline(b, ms, measured_traffic("backward_bf16_b4h8n4096d64"))}
 
 
 def cpu_baseline(w, qkv, seconds):

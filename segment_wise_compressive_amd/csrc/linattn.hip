@@ -160,6 +160,7 @@ struct Args {
     unsigned *giveups;             // counter of waits that gave up (workspace offset 0)
     int wait_s;   // s_out is s_in and shared by P > 1 column blocks
     int unnorm;   // causal outputs without the normaliser (numerators only)
+    int direct;   // k_cs_state with one share: write z_out = z_in + Z (no slot)
 };
 
 // A slot holds one (head, column block) state in the layout of the state
@@ -2225,6 +2226,22 @@ __global__ void __launch_bounds__(NTHR, D <= 64 ? 4 : 2) k_cs_state(const Args a
         step(ch, 0, 0);
         step(ch + 1, 1, 1);
     }
+    if (a.direct) {
+        // one share per (head, column block): the final state itself,
+        // z_out = z_in + Z and (column block 0) s_out = s_in + S; each
+        // element is read and written by one thread, so in place is safe
+        const int64_t zo = (int64_t)bh * D * D + p * DV + 16 * w + r;
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int dim = cs_dim(jt, 4 * g + i);
+                if (a.z_out) a.z_out[zo + dim * D] = Z[jt][i] + (a.z_in ? a.z_in[zo + dim * D] : 0.f);
+                if (a.s_out && p == 0 && w == 0 && r == 0)
+                    a.s_out[(int64_t)bh * D + dim] = S[jt][i] + ntok + (a.s_in ? a.s_in[(int64_t)bh * D + dim] : 0.f);
+            }
+        return;
+    }
     // the slot: Z in [D][DV] layout, S (wave 0)
     float *slot = a.part + ((int64_t)hp * a.NS + grp) * SL;
 #pragma unroll
@@ -3324,8 +3341,15 @@ la_status causal_impl(const void *q, la_strides sq, const void *k, la_strides sk
         a.part = (float *)workspace;
         a.slot0 = 0;
         const unsigned nwg = (unsigned)(BH * pl.P * pl.G);
-        if (!f32 && (d == 64 || d == 128) && pl.C == 64) launch_cs_state(d, a, nwg, stream);
-        else dispatch(f32, d, pl.C, 0, a, (int)nwg, stream);
+        if (!f32 && (d == 64 || d == 128) && pl.C == 64) {
+            // one share per head and column block: the state kernel writes
+            // the final state itself (no slots, no second launch)
+            a.direct = pl.G == 1;
+            launch_cs_state(d, a, nwg, stream);
+            if (a.direct) return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
+        } else {
+            dispatch(f32, d, pl.C, 0, a, (int)nwg, stream);
+        }
         launch_slots(d, a, BH, pl.P, pl.G, 1, stream);
         return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
     }

@@ -199,6 +199,32 @@ def test_state_only_from_k_and_v(dtype, d):
     assert torch.equal(z, zi) and torch.equal(s, si)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_state_only_one_share_per_head(d):
+    # many heads: the plan gives every (head, column block) one share, and
+    # the state kernel writes z_out = z_in + its state itself (also in place)
+    B, H, N = 4, 80, 200
+    _log(f"state only, one share per head, d={d}")
+    q, k, v = inp.qkv((B, H, N, d), 45 + d, torch.bfloat16, d ** -0.5)
+    z0, s0 = rand_state(B, H, d, 12)
+    _, rz, rs = oracle.causal(q, k, v, 1e-6, z0, s0, want_out=False)
+    z = torch.empty(B, H, d, d, device=DEV)
+    s = torch.empty(B, H, d, device=DEV)
+    la.la_causal_fwd(None, k.to(DEV), v.to(DEV), None, z_in=z0.to(DEV), s_in=s0.to(DEV), z_out=z, s_out=s)
+    zi, si = z0.to(DEV), s0.to(DEV)
+    la.la_causal_fwd(None, k.to(DEV), v.to(DEV), None, z_in=zi, s_in=si, z_out=zi, s_out=si)
+    zn = torch.empty(B, H, d, d, device=DEV)
+    sn = torch.empty(B, H, d, device=DEV)
+    la.la_causal_fwd(None, k.to(DEV), v.to(DEV), None, z_out=zn, s_out=sn)
+    torch.cuda.synchronize()
+    assert state_err(z.cpu(), torch.from_numpy(rz)) < 2e-3
+    assert state_err(s.cpu(), torch.from_numpy(rs)) < 2e-3
+    assert torch.equal(z, zi) and torch.equal(s, si)
+    _, rz0, rs0 = oracle.causal(q, k, v, 1e-6, want_out=False)
+    assert state_err(zn.cpu(), torch.from_numpy(rz0)) < 2e-3
+    assert state_err(sn.cpu(), torch.from_numpy(rs0)) < 2e-3
+
+
 def test_zero_length_passes_state_through():
     B, H, d = 2, 3, 64
     z0, s0 = rand_state(B, H, d, 9)
