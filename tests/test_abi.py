@@ -215,7 +215,7 @@ def test_noalloc_validation(lib):
     assert call(d=48) == UNSUP
     assert call(q=None) == NULL_
     assert call(eps=-1.0) == VALUE
-    big = (1, 64, 1 << 16, 128)
+    big = (1, 1024, 4096, 128)
     assert la.la_causal_fwd_workspace(*big) > la.la_noalloc_scratch_bytes()
     assert call(*big) == WS
 
