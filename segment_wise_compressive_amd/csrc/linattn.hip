@@ -2947,6 +2947,287 @@ __global__ void __launch_bounds__(NTHR) k_bwd_chunk(const BwdArgs a)
     }
 }
 
+// Stage 64 rows (a chunk) of one head into two swizzled bf16 [64][D] arrays:
+// the values rounded to bf16 (hi) and the remainders (lo), hi + lo carrying
+// about 16 significant bits.  MODE 1: phi of bf16 inputs; MODE 2: fp32 inputs
+// times 1 / den[row].  Both zero from row `nval` on.
+template <int D, int MODE>
+__device__ __forceinline__ void bwd_stage_split(rsrc_t src, int64_t rs, bf16 *hi, bf16 *lo, int nval, int tid,
+                                                const float *den = nullptr)
+{
+    constexpr int PPR = D / 8, ITEMS = 64 * PPR, NI = ITEMS / NTHR;   // 8-element pieces
+    static_assert(ITEMS % NTHR == 0, "whole pieces per thread");
+    float f[NI][8];
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+        const int item = tid + it * NTHR, row = item / PPR, pc = item % PPR;
+        if constexpr (MODE == 1) {
+            Vec<false>::to_float(bload16(src, (uint32_t)(row * rs + pc * 16)), f[it]);
+        } else {
+            Vec<true>::to_float(bload16(src, (uint32_t)(row * rs + pc * 32)), f[it]);
+            Vec<true>::to_float(bload16(src, (uint32_t)(row * rs + pc * 32 + 16)), f[it] + 4);
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+        const int item = tid + it * NTHR, row = item / PPR, pc = item % PPR;
+        const bool live = row < nval;
+        const float scale = MODE == 2 ? (live ? 1.f / den[row] : 0.f) : 1.f;
+        u32x4 h, l;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float x0 = f[it][2 * e], x1 = f[it][2 * e + 1];
+            if constexpr (MODE == 1) { x0 = live ? phi<false>(x0) : 0.f; x1 = live ? phi<false>(x1) : 0.f; }
+            else { x0 *= scale; x1 *= scale; }
+            const uint2 s_ = split_pk(x0, x1);
+            h[e] = s_.x;
+            l[e] = s_.y;
+        }
+        *reinterpret_cast<u32x4 *>(hi + swz<D>(row, pc * 8)) = h;
+        *reinterpret_cast<u32x4 *>(lo + swz<D>(row, pc * 8)) = l;
+    }
+}
+
+// k_bwd_chunk for bf16 inputs: the same gradients, every product on bf16
+// MFMA (v_mfma_f32_16x16x32_bf16) with fp32 operands split into hi + lo
+// (three products: hi hi, hi lo, lo hi; two where one side is the exact bf16
+// v).  G, F and dn are staged as hi + lo, V as it is.  Products contract
+// either over dims / value columns (operands read as rows) or over tokens in
+// steps of 32, in the token order t(g, j) = s0 + 4g + (j & 3) + 16 (j >> 2):
+// then the two 16-token accumulator tiles at s0 and s0 + 16 are, lane by
+// lane, the 8 operand values of the next product, and the other operand is a
+// transpose read of a staged [token][dim] array.  The dq and dk tiles hold
+// dims in the state tile order cs_dim (rows 4g .. 4g + 3 of tile jt are the
+// consecutive dims 32 (jt >> 1) + 8g + 4 (jt & 1) + i), the layout of the
+// transposed G and F operands; the state products read Z_c and R'_c rows in
+// the same order.
+template <int D>
+__global__ void __launch_bounds__(NTHR) k_bwd_chunk_bf(const BwdArgs a)
+{
+    constexpr int C = 64, JT = D / 16, KS = D / 32, DV = D < 64 ? D : 64, SL = DV * D + D;
+    __shared__ __attribute__((aligned(16))) bf16 sm[7 * C * D];
+    __shared__ float dDs[C];
+    bf16 *Gh = sm, *Gl = sm + C * D, *Fh = sm + 2 * C * D, *Fl = sm + 3 * C * D;
+    bf16 *Nh = sm + 4 * C * D, *Nl = sm + 5 * C * D, *Vs = sm + 6 * C * D;
+    const int tid = threadIdx.x, lane = tid % WAVE, r = lane % 16, g = lane / 16;
+    const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
+    const int ch = blockIdx.x % a.nch, bh = blockIdx.x / a.nch;
+    const int b = bh / a.H, h = bh % a.H;
+    const int t0 = ch * C, nval = min(C, a.N - t0);
+    const RowView qv{(const char *)a.q + (b * a.sqb + h * a.sqh) * 2, a.sqn * 2, (a.N - 1) * a.sqn * 2 + D * 2};
+    const RowView kv{(const char *)a.k + (b * a.skb + h * a.skh) * 2, a.skn * 2, (a.N - 1) * a.skn * 2 + D * 2};
+    const RowView vv{(const char *)a.v + (b * a.svb + h * a.svh) * 2, a.svn * 2, (a.N - 1) * a.svn * 2 + D * 2};
+    const RowView dov{(const char *)(a.dout + b * a.sdb + h * a.sdh), a.sdn * 4, (a.N - 1) * a.sdn * 4 + D * 4};
+    const float *denc = a.den + (int64_t)bh * a.N + t0;
+    bwd_stage_split<D, 1>(qv.at(t0), qv.rs, Gh, Gl, nval, tid);
+    bwd_stage_split<D, 1>(kv.at(t0), kv.rs, Fh, Fl, nval, tid);
+    {
+        constexpr int PPR = D / 8, NI = 64 * PPR / NTHR;
+        const rsrc_t vr = vv.at(t0);   // rows past the sequence read as zeros
+#pragma unroll
+        for (int it = 0; it < NI; ++it) {
+            const int item = tid + it * NTHR, row = item / PPR, pc = item % PPR;
+            *reinterpret_cast<u32x4 *>(Vs + swz<D>(row, pc * 8)) = bload16(vr, (uint32_t)(row * vv.rs + pc * 16));
+        }
+    }
+    bwd_stage_split<D, 2>(dov.at(t0), dov.rs, Nh, Nl, nval, tid, denc);
+    if (tid < C) dDs[tid] = tid < nval ? a.dden[(int64_t)bh * a.N + t0 + tid] : 0.f;
+    __syncthreads();
+
+    const int me = 16 * w + r;   // this lane's token (query for dq, key for dk / dv)
+    const bool live = me < nval;
+    const float *zc = a.fwd + ((int64_t)bh * a.P * a.NS + ch) * SL;
+    const float *rc = a.rev + ((int64_t)bh * a.P * a.NS + (a.nch - 1 - ch)) * SL;
+    auto zrow4 = [&](const float *st, int j, int c0) {   // st[j][c0 .. c0 + 3]
+        return *reinterpret_cast<const f32x4 *>(st + (int64_t)(c0 / DV) * a.NS * SL + j * DV + c0 % DV);
+    };
+    auto dim0 = [&](int jt) { return 32 * (jt >> 1) + 8 * g + 4 * (jt & 1); };   // first dim of a lane's rows
+    auto val4 = [&](const bf16 *hi, const bf16 *lo, int row, int col) {   // hi + lo of 4 staged values
+        const uint2 x = *reinterpret_cast<const uint2 *>(hi + swz<D>(row, col));
+        const uint2 y = *reinterpret_cast<const uint2 *>(lo + swz<D>(row, col));
+        return (f32x4){bf_lo(x.x) + bf_lo(y.x), bf_hi(x.x) + bf_hi(y.x), bf_lo(x.y) + bf_lo(y.y), bf_hi(x.y) + bf_hi(y.y)};
+    };
+
+    // ---- dq (query me)
+    {
+        f32x4 acc[JT];
+        const float ddt = dDs[me];
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            const int jr = cs_dim(jt, r);
+#pragma unroll
+            for (int u = 0; u < KS; ++u) {
+                bf16x8 zh, zl;
+                cs_split(zrow4(zc, jr, 32 * u + 8 * g), zrow4(zc, jr, 32 * u + 8 * g + 4), zh, zl);
+                const bf16x8 nh = nat8(Nh + swz<D>(me, 32 * u + 8 * g)), nl = nat8(Nl + swz<D>(me, 32 * u + 8 * g));
+                x = mma8(x, zh, nh);
+                x = mma8(x, zh, nl);
+                x = mma8(x, zl, nh);
+            }
+            acc[jt] = x + *reinterpret_cast<const f32x4 *>(zc + DV * D + dim0(jt)) * ddt;
+        }
+        for (int v = 0; v <= (w >> 1); ++v) {   // keys up to the wave's last token
+            const int s0 = 32 * v;
+            f32x4 at[2];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                f32x4 t = {0.f, 0.f, 0.f, 0.f};   // v_s . dn_me, s = s0 + 16 hf + 4g + i
+#pragma unroll
+                for (int u = 0; u < KS; ++u) {
+                    const bf16x8 va = nat8(Vs + swz<D>(s0 + 16 * hf + r, 32 * u + 8 * g));
+                    t = mma8(t, va, nat8(Nh + swz<D>(me, 32 * u + 8 * g)));
+                    t = mma8(t, va, nat8(Nl + swz<D>(me, 32 * u + 8 * g)));
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) t[i] = (s0 + 16 * hf + 4 * g + i <= me) ? t[i] + ddt : 0.f;
+                at[hf] = t;
+            }
+            bf16x8 bh_, bl_;
+            cs_split(at[0], at[1], bh_, bl_);
+#pragma unroll
+            for (int jt = 0; jt < JT; ++jt) {
+                const bf16x8 fh = cs_ktr8<D>(Fh, s0, jt, r, g), fl = cs_ktr8<D>(Fl, s0, jt, r, g);
+                acc[jt] = mma8(acc[jt], fh, bh_);
+                acc[jt] = mma8(acc[jt], fh, bl_);
+                acc[jt] = mma8(acc[jt], fl, bh_);
+            }
+        }
+        if (live) {
+            float *dst = a.dq + b * a.gqb + h * a.gqh + (int64_t)(t0 + me) * a.gqn;
+#pragma unroll
+            for (int jt = 0; jt < JT; ++jt) {
+                const f32x4 gq = val4(Gh, Gl, me, dim0(jt));
+                f32x4 dphi;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dphi[i] = fminf(gq[i], 1.f);
+                *reinterpret_cast<f32x4 *>(dst + dim0(jt)) = acc[jt] * dphi;
+            }
+        }
+    }
+    // ---- dk (key me)
+    {
+        f32x4 acc[JT];
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            const int jr = cs_dim(jt, r);
+#pragma unroll
+            for (int u = 0; u < KS; ++u) {
+                bf16x8 rh, rl;
+                cs_split(zrow4(rc, jr, 32 * u + 8 * g), zrow4(rc, jr, 32 * u + 8 * g + 4), rh, rl);
+                const bf16x8 vb = nat8(Vs + swz<D>(me, 32 * u + 8 * g));
+                x = mma8(x, rh, vb);
+                x = mma8(x, rl, vb);
+            }
+            acc[jt] = x + *reinterpret_cast<const f32x4 *>(rc + DV * D + dim0(jt));
+        }
+        for (int v = w >> 1; v < 2; ++v) {   // queries from the wave's first token on
+            const int s0 = 32 * v;
+            f32x4 at[2];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                f32x4 t = {0.f, 0.f, 0.f, 0.f};   // dn_t . v_me, t = s0 + 16 hf + 4g + i
+#pragma unroll
+                for (int u = 0; u < KS; ++u) {
+                    const bf16x8 vb = nat8(Vs + swz<D>(me, 32 * u + 8 * g));
+                    t = mma8(t, nat8(Nh + swz<D>(s0 + 16 * hf + r, 32 * u + 8 * g)), vb);
+                    t = mma8(t, nat8(Nl + swz<D>(s0 + 16 * hf + r, 32 * u + 8 * g)), vb);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tq = s0 + 16 * hf + 4 * g + i;
+                    t[i] = tq >= me ? t[i] + dDs[tq] : 0.f;
+                }
+                at[hf] = t;
+            }
+            bf16x8 bh_, bl_;
+            cs_split(at[0], at[1], bh_, bl_);
+#pragma unroll
+            for (int jt = 0; jt < JT; ++jt) {
+                const bf16x8 gh = cs_ktr8<D>(Gh, s0, jt, r, g), gl = cs_ktr8<D>(Gl, s0, jt, r, g);
+                acc[jt] = mma8(acc[jt], gh, bh_);
+                acc[jt] = mma8(acc[jt], gh, bl_);
+                acc[jt] = mma8(acc[jt], gl, bh_);
+            }
+        }
+        if (live) {
+            float *dst = a.dk + b * a.gkb + h * a.gkh + (int64_t)(t0 + me) * a.gkn;
+#pragma unroll
+            for (int jt = 0; jt < JT; ++jt) {
+                const f32x4 fk = val4(Fh, Fl, me, dim0(jt));
+                f32x4 dphi;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dphi[i] = fminf(fk[i], 1.f);
+                *reinterpret_cast<f32x4 *>(dst + dim0(jt)) = acc[jt] * dphi;
+            }
+        }
+    }
+    // ---- dv: rows s = 16 w + 4g + i (keys), columns c = 16 ct + r
+    {
+        f32x4 acc[JT];
+#pragma unroll
+        for (int ct = 0; ct < JT; ++ct) {
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            const int c = 16 * ct + r;
+            const float *rcol = rc + (int64_t)(c / DV) * a.NS * SL + c % DV;
+#pragma unroll
+            for (int u = 0; u < KS; ++u) {
+                f32x4 r0, r1;   // R'[32u + 8g + jj][c]
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    r0[i] = rcol[(32 * u + 8 * g + i) * DV];
+                    r1[i] = rcol[(32 * u + 8 * g + 4 + i) * DV];
+                }
+                bf16x8 rh, rl;
+                cs_split(r0, r1, rh, rl);
+                const bf16x8 fh = nat8(Fh + swz<D>(16 * w + r, 32 * u + 8 * g)), fl = nat8(Fl + swz<D>(16 * w + r, 32 * u + 8 * g));
+                x = mma8(x, fh, rh);
+                x = mma8(x, fh, rl);
+                x = mma8(x, fl, rh);
+            }
+            acc[ct] = x;
+        }
+        for (int v = w >> 1; v < 2; ++v) {   // queries from the wave's first key on
+            const int s0 = 32 * v;
+            f32x4 pt[2];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                f32x4 t = {0.f, 0.f, 0.f, 0.f};   // g_t . f_s, t = s0 + 16 hf + 4g + i, s = 16 w + r
+#pragma unroll
+                for (int u = 0; u < KS; ++u) {
+                    const bf16x8 gh = nat8(Gh + swz<D>(s0 + 16 * hf + r, 32 * u + 8 * g));
+                    const bf16x8 gl = nat8(Gl + swz<D>(s0 + 16 * hf + r, 32 * u + 8 * g));
+                    const bf16x8 fh = nat8(Fh + swz<D>(me, 32 * u + 8 * g)), fl = nat8(Fl + swz<D>(me, 32 * u + 8 * g));
+                    t = mma8(t, gh, fh);
+                    t = mma8(t, gh, fl);
+                    t = mma8(t, gl, fh);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) t[i] = (s0 + 16 * hf + 4 * g + i >= me) ? t[i] : 0.f;
+                pt[hf] = t;
+            }
+            bf16x8 ph, pl;   // P^T rows s = 16 w + r over t(g, j)
+            cs_split(pt[0], pt[1], ph, pl);
+#pragma unroll
+            for (int ct = 0; ct < JT; ++ct) {
+                const bf16x8 nh = tr8<D>(Nh, s0, 16 * ct, r, g), nl = tr8<D>(Nl, s0, 16 * ct, r, g);
+                acc[ct] = mma8(acc[ct], ph, nh);
+                acc[ct] = mma8(acc[ct], ph, nl);
+                acc[ct] = mma8(acc[ct], pl, nh);
+            }
+        }
+        float *dst = a.dv + b * a.gvb + h * a.gvh + (int64_t)t0 * a.gvn;
+#pragma unroll
+        for (int ct = 0; ct < JT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s_ = 16 * w + 4 * g + i;
+                if (s_ < nval) dst[(int64_t)s_ * a.gvn + 16 * ct + r] = acc[ct][i];
+            }
+    }
+}
+
 // ------------------------------------------------------------------ host side
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -3603,7 +3884,13 @@ la_status la_causal_bwd(const void *q, la_strides sq, const void *k, la_strides 
     a.part = rev;
     launch_slots(d, a, BH, pl.P, pl.NS, 0, stream);
     // 5) dq, dk, dv of every chunk
-    LA_BWD_ALL(k_bwd_chunk)
+    if (f32) {
+        if (d == 32) LA_BWD(k_bwd_chunk, true, 32); else if (d == 64) LA_BWD(k_bwd_chunk, true, 64); else LA_BWD(k_bwd_chunk, true, 128);
+    } else {
+#define LA_BWD_BF(DD) hipLaunchKernelGGL((k_bwd_chunk_bf<DD>), grid, dim3(NTHR), 0, stream, ba)
+        if (d == 32) LA_BWD_BF(32); else if (d == 64) LA_BWD_BF(64); else LA_BWD_BF(128);
+#undef LA_BWD_BF
+    }
 #undef LA_BWD_ALL
 #undef LA_BWD
     return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
