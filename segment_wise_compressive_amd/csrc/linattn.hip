@@ -2708,8 +2708,8 @@ template <bool F32, int D>
 __global__ void __launch_bounds__(NTHR) k_bwd_prep(const BwdArgs a)
 {
     constexpr int C = 64, LD = D + 4, KT = D / 16, DV = D < 64 ? D : 64, SL = DV * D + D, ES = F32 ? 4 : 2;
-    __shared__ __attribute__((aligned(16))) float sm[3 * C * LD + C];
-    float *Gs = sm, *Fs = sm + C * LD, *Ns = sm + 2 * C * LD, *dDs = sm + 3 * C * LD;
+    __shared__ __attribute__((aligned(16))) float sm[3 * C * LD + C + NTHR];
+    float *Gs = sm, *Fs = sm + C * LD, *Ns = sm + 2 * C * LD, *dDs = sm + 3 * C * LD, *red = dDs + C;
     const int tid = threadIdx.x, lane = tid % WAVE, r = lane % 16, g = lane / 16;
     const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
     const int ch = blockIdx.x % a.nch, bh = blockIdx.x / a.nch;
@@ -2719,14 +2719,22 @@ __global__ void __launch_bounds__(NTHR) k_bwd_prep(const BwdArgs a)
     const RowView kv{(const char *)a.k + (b * a.skb + h * a.skh) * ES, a.skn * ES, (a.N - 1) * a.skn * ES + D * ES};
     const RowView ov{(const char *)(a.out + b * a.sob + h * a.soh), a.son * 4, (a.N - 1) * a.son * 4 + D * 4};
     const RowView dov{(const char *)(a.dout + b * a.sdb + h * a.sdh), a.sdn * 4, (a.N - 1) * a.sdn * 4 + D * 4};
+    // this lane's out row pieces and S_c pieces, requested with the stage
+    const int t = 16 * w + r;
+    const float *sc = a.fwd + ((int64_t)bh * a.P * a.NS + ch) * SL + DV * D;   // S_c (column block 0)
+    const rsrc_t orow = ov.at(t0 + t, t < nval);
+    f32x4 o4v[KT], s4v[KT];
+#pragma unroll
+    for (int js = 0; js < KT; ++js) {
+        o4v[js] = __builtin_bit_cast(f32x4, bload16(orow, (uint32_t)((16 * js + 4 * g) * 4)));
+        s4v[js] = *reinterpret_cast<const f32x4 *>(sc + 16 * js + 4 * g);
+    }
     bwd_stage<F32, D, 1>(qv.at(t0), qv.rs, Gs, nval, tid);
     bwd_stage<F32, D, 1>(kv.at(t0), kv.rs, Fs, nval, tid);
     bwd_stage<true, D, 0>(dov.at(t0), dov.rs, Ns, nval, tid);
     __syncthreads();
 
     // ---- normaliser of token t = 16 w + r: g_t . S_c + sum_{s <= t} P_ts + eps
-    const int t = 16 * w + r;
-    const float *sc = a.fwd + ((int64_t)bh * a.P * a.NS + ch) * SL + DV * D;   // S_c (column block 0)
     float rsum = 0.f, gs = 0.f, dot = 0.f;
 #pragma unroll
     for (int sa = 0; sa < 4; ++sa) {
@@ -2738,12 +2746,10 @@ __global__ void __launch_bounds__(NTHR) k_bwd_prep(const BwdArgs a)
 #pragma unroll
         for (int i = 0; i < 4; ++i) rsum += (16 * sa + 4 * g + i <= t) ? pt[i] : 0.f;
     }
-    const rsrc_t orow = ov.at(t0 + t, t < nval);
 #pragma unroll
     for (int js = 0; js < KT; ++js) {
         const f32x4 gq = nat4(Gs + t * LD + 16 * js + 4 * g);
-        const f32x4 s4 = *reinterpret_cast<const f32x4 *>(sc + 16 * js + 4 * g);
-        const f32x4 o4 = __builtin_bit_cast(f32x4, bload16(orow, (uint32_t)((16 * js + 4 * g) * 4)));
+        const f32x4 s4 = s4v[js], o4 = o4v[js];
         const f32x4 d4 = nat4(Ns + t * LD + 16 * js + 4 * g);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -2788,11 +2794,22 @@ __global__ void __launch_bounds__(NTHR) k_bwd_prep(const BwdArgs a)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sl[(16 * jt + 4 * g + i) * DV] = acc[i];
     }
-    // ---- dr_c = sum_t g_t dD_t, into every column block's slot
-    if (tid < D) {
+    // ---- dr_c = sum_t g_t dD_t (NTHR / D partial sums per dim), into every
+    // column block's slot
+    {
+        constexpr int NP = NTHR / D;
+        const int j = tid % D, part = tid / D;
         float acc = 0.f;
-        for (int tt = 0; tt < C; ++tt) acc += Gs[tt * LD + tid] * dDs[tt];
-        for (int p = 0; p < a.P; ++p) slot0[(int64_t)p * a.NS * SL + DV * D + tid] = acc;
+#pragma unroll
+        for (int tt = part; tt < C; tt += NP) acc += Gs[tt * LD + j] * dDs[tt];
+        red[tid] = acc;
+        __syncthreads();
+        if (tid < D) {
+            float sum = 0.f;
+#pragma unroll
+            for (int pp = 0; pp < NP; ++pp) sum += red[pp * D + tid];
+            for (int p = 0; p < a.P; ++p) slot0[(int64_t)p * a.NS * SL + DV * D + tid] = sum;
+        }
     }
 }
 
@@ -2991,7 +3008,7 @@ __device__ __forceinline__ void bwd_stage_split(rsrc_t src, int64_t rs, bf16 *hi
 // k_bwd_chunk for bf16 inputs: the same gradients, every product on bf16
 // MFMA (v_mfma_f32_16x16x32_bf16) with fp32 operands split into hi + lo
 // (three products: hi hi, hi lo, lo hi; two where one side is the exact bf16
-// v).  G, F and dn are staged as hi + lo, V as it is.  Products contract
+// v).  G, F and dn are staged as hi + lo; v rows are read from memory.  Products contract
 // either over dims / value columns (operands read as rows) or over tokens in
 // steps of 32, in the token order t(g, j) = s0 + 4g + (j & 3) + 16 (j >> 2):
 // then the two 16-token accumulator tiles at s0 and s0 + 16 are, lane by
@@ -3005,10 +3022,10 @@ template <int D>
 __global__ void __launch_bounds__(NTHR) k_bwd_chunk_bf(const BwdArgs a)
 {
     constexpr int C = 64, JT = D / 16, KS = D / 32, DV = D < 64 ? D : 64, SL = DV * D + D;
-    __shared__ __attribute__((aligned(16))) bf16 sm[7 * C * D];
+    __shared__ __attribute__((aligned(16))) bf16 sm[6 * C * D];
     __shared__ float dDs[C];
     bf16 *Gh = sm, *Gl = sm + C * D, *Fh = sm + 2 * C * D, *Fl = sm + 3 * C * D;
-    bf16 *Nh = sm + 4 * C * D, *Nl = sm + 5 * C * D, *Vs = sm + 6 * C * D;
+    bf16 *Nh = sm + 4 * C * D, *Nl = sm + 5 * C * D;
     const int tid = threadIdx.x, lane = tid % WAVE, r = lane % 16, g = lane / 16;
     const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
     const int ch = blockIdx.x % a.nch, bh = blockIdx.x / a.nch;
@@ -3021,15 +3038,10 @@ __global__ void __launch_bounds__(NTHR) k_bwd_chunk_bf(const BwdArgs a)
     const float *denc = a.den + (int64_t)bh * a.N + t0;
     bwd_stage_split<D, 1>(qv.at(t0), qv.rs, Gh, Gl, nval, tid);
     bwd_stage_split<D, 1>(kv.at(t0), kv.rs, Fh, Fl, nval, tid);
-    {
-        constexpr int PPR = D / 8, NI = 64 * PPR / NTHR;
-        const rsrc_t vr = vv.at(t0);   // rows past the sequence read as zeros
-#pragma unroll
-        for (int it = 0; it < NI; ++it) {
-            const int item = tid + it * NTHR, row = item / PPR, pc = item % PPR;
-            *reinterpret_cast<u32x4 *>(Vs + swz<D>(row, pc * 8)) = bload16(vr, (uint32_t)(row * vv.rs + pc * 16));
-        }
-    }
+    // v rows are read from memory (L2) as operands: rows past the sequence
+    // read as zeros
+    const rsrc_t vr = vv.at(t0);
+    auto vrow8 = [&](int row, int col) { return __builtin_bit_cast(bf16x8, bload16(vr, (uint32_t)(row * vv.rs + col * 2))); };
     bwd_stage_split<D, 2>(dov.at(t0), dov.rs, Nh, Nl, nval, tid, denc);
     if (tid < C) dDs[tid] = tid < nval ? a.dden[(int64_t)bh * a.N + t0 + tid] : 0.f;
     __syncthreads();
@@ -3075,7 +3087,7 @@ __global__ void __launch_bounds__(NTHR) k_bwd_chunk_bf(const BwdArgs a)
                 f32x4 t = {0.f, 0.f, 0.f, 0.f};   // v_s . dn_me, s = s0 + 16 hf + 4g + i
 #pragma unroll
                 for (int u = 0; u < KS; ++u) {
-                    const bf16x8 va = nat8(Vs + swz<D>(s0 + 16 * hf + r, 32 * u + 8 * g));
+                    const bf16x8 va = vrow8(s0 + 16 * hf + r, 32 * u + 8 * g);
                     t = mma8(t, va, nat8(Nh + swz<D>(me, 32 * u + 8 * g)));
                     t = mma8(t, va, nat8(Nl + swz<D>(me, 32 * u + 8 * g)));
                 }
@@ -3116,7 +3128,7 @@ __global__ void __launch_bounds__(NTHR) k_bwd_chunk_bf(const BwdArgs a)
             for (int u = 0; u < KS; ++u) {
                 bf16x8 rh, rl;
                 cs_split(zrow4(rc, jr, 32 * u + 8 * g), zrow4(rc, jr, 32 * u + 8 * g + 4), rh, rl);
-                const bf16x8 vb = nat8(Vs + swz<D>(me, 32 * u + 8 * g));
+                const bf16x8 vb = vrow8(me, 32 * u + 8 * g);
                 x = mma8(x, rh, vb);
                 x = mma8(x, rl, vb);
             }
@@ -3130,7 +3142,7 @@ __global__ void __launch_bounds__(NTHR) k_bwd_chunk_bf(const BwdArgs a)
                 f32x4 t = {0.f, 0.f, 0.f, 0.f};   // dn_t . v_me, t = s0 + 16 hf + 4g + i
 #pragma unroll
                 for (int u = 0; u < KS; ++u) {
-                    const bf16x8 vb = nat8(Vs + swz<D>(me, 32 * u + 8 * g));
+                    const bf16x8 vb = vrow8(me, 32 * u + 8 * g);
                     t = mma8(t, nat8(Nh + swz<D>(s0 + 16 * hf + r, 32 * u + 8 * g)), vb);
                     t = mma8(t, nat8(Nl + swz<D>(s0 + 16 * hf + r, 32 * u + 8 * g)), vb);
                 }
