@@ -2801,7 +2801,7 @@ __global__ void __launch_bounds__(NTHR) k_bwd_prep(const BwdArgs a)
         const int j = tid % D, part = tid / D;
         float acc = 0.f;
 #pragma unroll
-        for (int tt = part; tt < C; tt += NP) acc += Gs[tt * LD + j] * dDs[tt];
+        for (int i = 0; i < C / NP; ++i) acc += Gs[(part + i * NP) * LD + j] * dDs[part + i * NP];
         red[tid] = acc;
         __syncthreads();
         if (tid < D) {
