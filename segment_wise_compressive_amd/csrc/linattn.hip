@@ -3022,10 +3022,13 @@ template <int D>
 __global__ void __launch_bounds__(NTHR) k_bwd_chunk_bf(const BwdArgs a)
 {
     constexpr int C = 64, JT = D / 16, KS = D / 32, DV = D < 64 ? D : 64, SL = DV * D + D;
-    __shared__ __attribute__((aligned(16))) bf16 sm[6 * C * D];
+    // SH: Z_c and then R'_c are split once per workgroup into a shared
+    // [D][D] hi + lo pair (d <= 64: 16 KB more LDS), instead of by every wave
+    constexpr bool SH = D <= 64;
+    __shared__ __attribute__((aligned(16))) bf16 sm[6 * C * D + (SH ? 2 * D * D : 0)];
     __shared__ float dDs[C];
     bf16 *Gh = sm, *Gl = sm + C * D, *Fh = sm + 2 * C * D, *Fl = sm + 3 * C * D;
-    bf16 *Nh = sm + 4 * C * D, *Nl = sm + 5 * C * D;
+    bf16 *Nh = sm + 4 * C * D, *Nl = sm + 5 * C * D, *Th = sm + 6 * C * D, *Tl = Th + D * D;
     const int tid = threadIdx.x, lane = tid % WAVE, r = lane % 16, g = lane / 16;
     const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
     const int ch = blockIdx.x % a.nch, bh = blockIdx.x / a.nch;
@@ -3054,12 +3057,30 @@ __global__ void __launch_bounds__(NTHR) k_bwd_chunk_bf(const BwdArgs a)
         return *reinterpret_cast<const f32x4 *>(st + (int64_t)(c0 / DV) * a.NS * SL + j * DV + c0 % DV);
     };
     auto dim0 = [&](int jt) { return 32 * (jt >> 1) + 8 * g + 4 * (jt & 1); };   // first dim of a lane's rows
+    auto stage_state = [&](const float *st) {   // st[j][c] split into Th, Tl (swizzled [D][D])
+        constexpr int PPR = D / 8, NI = D * PPR / NTHR > 0 ? D * PPR / NTHR : 1;
+#pragma unroll
+        for (int it = 0; it < NI; ++it) {
+            const int item = tid + it * NTHR;
+            if (item < D * PPR) {
+                const int j = item / PPR, c8 = (item % PPR) * 8;
+                bf16x8 hi, lo;
+                cs_split(zrow4(st, j, c8), zrow4(st, j, c8 + 4), hi, lo);
+                *reinterpret_cast<bf16x8 *>(Th + swz<D>(j, c8)) = hi;
+                *reinterpret_cast<bf16x8 *>(Tl + swz<D>(j, c8)) = lo;
+            }
+        }
+    };
     auto val4 = [&](const bf16 *hi, const bf16 *lo, int row, int col) {   // hi + lo of 4 staged values
         const uint2 x = *reinterpret_cast<const uint2 *>(hi + swz<D>(row, col));
         const uint2 y = *reinterpret_cast<const uint2 *>(lo + swz<D>(row, col));
         return (f32x4){bf_lo(x.x) + bf_lo(y.x), bf_hi(x.x) + bf_hi(y.x), bf_lo(x.y) + bf_lo(y.y), bf_hi(x.y) + bf_hi(y.y)};
     };
 
+    if constexpr (SH) {
+        stage_state(zc);
+        __syncthreads();
+    }
     // ---- dq (query me)
     {
         f32x4 acc[JT];
@@ -3071,7 +3092,12 @@ __global__ void __launch_bounds__(NTHR) k_bwd_chunk_bf(const BwdArgs a)
 #pragma unroll
             for (int u = 0; u < KS; ++u) {
                 bf16x8 zh, zl;
-                cs_split(zrow4(zc, jr, 32 * u + 8 * g), zrow4(zc, jr, 32 * u + 8 * g + 4), zh, zl);
+                if constexpr (SH) {
+                    zh = nat8(Th + swz<D>(jr, 32 * u + 8 * g));
+                    zl = nat8(Tl + swz<D>(jr, 32 * u + 8 * g));
+                } else {
+                    cs_split(zrow4(zc, jr, 32 * u + 8 * g), zrow4(zc, jr, 32 * u + 8 * g + 4), zh, zl);
+                }
                 const bf16x8 nh = nat8(Nh + swz<D>(me, 32 * u + 8 * g)), nl = nat8(Nl + swz<D>(me, 32 * u + 8 * g));
                 x = mma8(x, zh, nh);
                 x = mma8(x, zh, nl);
@@ -3117,6 +3143,11 @@ __global__ void __launch_bounds__(NTHR) k_bwd_chunk_bf(const BwdArgs a)
             }
         }
     }
+    if constexpr (SH) {
+        __syncthreads();   // every wave is done with Z_c
+        stage_state(rc);
+        __syncthreads();
+    }
     // ---- dk (key me)
     {
         f32x4 acc[JT];
@@ -3127,7 +3158,12 @@ __global__ void __launch_bounds__(NTHR) k_bwd_chunk_bf(const BwdArgs a)
 #pragma unroll
             for (int u = 0; u < KS; ++u) {
                 bf16x8 rh, rl;
-                cs_split(zrow4(rc, jr, 32 * u + 8 * g), zrow4(rc, jr, 32 * u + 8 * g + 4), rh, rl);
+                if constexpr (SH) {
+                    rh = nat8(Th + swz<D>(jr, 32 * u + 8 * g));
+                    rl = nat8(Tl + swz<D>(jr, 32 * u + 8 * g));
+                } else {
+                    cs_split(zrow4(rc, jr, 32 * u + 8 * g), zrow4(rc, jr, 32 * u + 8 * g + 4), rh, rl);
+                }
                 const bf16x8 vb = vrow8(me, 32 * u + 8 * g);
                 x = mma8(x, rh, vb);
                 x = mma8(x, rl, vb);
@@ -3185,18 +3221,32 @@ __global__ void __launch_bounds__(NTHR) k_bwd_chunk_bf(const BwdArgs a)
             const float *rcol = rc + (int64_t)(c / DV) * a.NS * SL + c % DV;
 #pragma unroll
             for (int u = 0; u < KS; ++u) {
-                f32x4 r0, r1;   // R'[32u + 8g + jj][c]
+                if constexpr (SH) {
+                    // dims in the transpose read's order 32u + 4g + (jj & 3) + 16 (jj >> 2)
+                    const bf16x8 rh = tr8<D>(Th, 32 * u, 16 * ct, r, g), rl = tr8<D>(Tl, 32 * u, 16 * ct, r, g);
+                    auto frow = [&](const bf16 *base) {
+                        const bf16x4 x0 = *reinterpret_cast<const bf16x4 *>(base + swz<D>(16 * w + r, 32 * u + 4 * g));
+                        const bf16x4 x1 = *reinterpret_cast<const bf16x4 *>(base + swz<D>(16 * w + r, 32 * u + 16 + 4 * g));
+                        return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+                    };
+                    const bf16x8 fh = frow(Fh), fl = frow(Fl);
+                    x = mma8(x, fh, rh);
+                    x = mma8(x, fh, rl);
+                    x = mma8(x, fl, rh);
+                } else {
+                    f32x4 r0, r1;   // R'[32u + 8g + jj][c]
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    r0[i] = rcol[(32 * u + 8 * g + i) * DV];
-                    r1[i] = rcol[(32 * u + 8 * g + 4 + i) * DV];
+                    for (int i = 0; i < 4; ++i) {
+                        r0[i] = rcol[(32 * u + 8 * g + i) * DV];
+                        r1[i] = rcol[(32 * u + 8 * g + 4 + i) * DV];
+                    }
+                    bf16x8 rh, rl;
+                    cs_split(r0, r1, rh, rl);
+                    const bf16x8 fh = nat8(Fh + swz<D>(16 * w + r, 32 * u + 8 * g)), fl = nat8(Fl + swz<D>(16 * w + r, 32 * u + 8 * g));
+                    x = mma8(x, fh, rh);
+                    x = mma8(x, fh, rl);
+                    x = mma8(x, fl, rh);
                 }
-                bf16x8 rh, rl;
-                cs_split(r0, r1, rh, rl);
-                const bf16x8 fh = nat8(Fh + swz<D>(16 * w + r, 32 * u + 8 * g)), fl = nat8(Fl + swz<D>(16 * w + r, 32 * u + 8 * g));
-                x = mma8(x, fh, rh);
-                x = mma8(x, fh, rl);
-                x = mma8(x, fl, rh);
             }
             acc[ct] = x;
         }
