@@ -2966,11 +2966,12 @@ __global__ void __launch_bounds__(NTHR) k_bwd_chunk(const BwdArgs a)
 
 // Stage 64 rows (a chunk) of one head into two swizzled bf16 [64][D] arrays:
 // the values rounded to bf16 (hi) and the remainders (lo), hi + lo carrying
-// about 16 significant bits.  MODE 1: phi of bf16 inputs; MODE 2: fp32 inputs
-// times 1 / den[row].  Both zero from row `nval` on.
+// about 16 significant bits; `lo2`, when given, gets a third part (about 24
+// bits in all).  MODE 1: phi of bf16 inputs; MODE 2: fp32 inputs times
+// 1 / den[row].  Both zero from row `nval` on.
 template <int D, int MODE>
 __device__ __forceinline__ void bwd_stage_split(rsrc_t src, int64_t rs, bf16 *hi, bf16 *lo, int nval, int tid,
-                                                const float *den = nullptr)
+                                                const float *den = nullptr, bf16 *lo2 = nullptr)
 {
     constexpr int PPR = D / 8, ITEMS = 64 * PPR, NI = ITEMS / NTHR;   // 8-element pieces
     static_assert(ITEMS % NTHR == 0, "whole pieces per thread");
@@ -2990,7 +2991,7 @@ __device__ __forceinline__ void bwd_stage_split(rsrc_t src, int64_t rs, bf16 *hi
         const int item = tid + it * NTHR, row = item / PPR, pc = item % PPR;
         const bool live = row < nval;
         const float scale = MODE == 2 ? (live ? 1.f / den[row] : 0.f) : 1.f;
-        u32x4 h, l;
+        u32x4 h, l, l2;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float x0 = f[it][2 * e], x1 = f[it][2 * e + 1];
@@ -2999,16 +3000,22 @@ __device__ __forceinline__ void bwd_stage_split(rsrc_t src, int64_t rs, bf16 *hi
             const uint2 s_ = split_pk(x0, x1);
             h[e] = s_.x;
             l[e] = s_.y;
+            // third part: what hi + lo leave (hi + lo + lo2 carry about 24 bits)
+            l2[e] = pk_bf16(x0 - bf_lo(s_.x) - bf_lo(s_.y), x1 - bf_hi(s_.x) - bf_hi(s_.y));
         }
         *reinterpret_cast<u32x4 *>(hi + swz<D>(row, pc * 8)) = h;
         *reinterpret_cast<u32x4 *>(lo + swz<D>(row, pc * 8)) = l;
+        if (lo2) *reinterpret_cast<u32x4 *>(lo2 + swz<D>(row, pc * 8)) = l2;
     }
 }
 
 // k_bwd_chunk for bf16 inputs: the same gradients, every product on bf16
 // MFMA (v_mfma_f32_16x16x32_bf16) with fp32 operands split into hi + lo
-// (three products: hi hi, hi lo, lo hi; two where one side is the exact bf16
-// v).  G, F and dn are staged as hi + lo; v rows are read from memory.  Products contract
+// (three products: hi hi, hi lo, lo hi).  G, F and dn are staged as hi + lo;
+// v rows are read from memory.  v . dn, where v is exact, takes a third part
+// of dn (about 24 bits in all): in A_ts = v_s . dn_t + dD_t the two terms
+// cancel to the eps level at a head's first token (out_0 = v_0 up to eps),
+// and the 16-bit hi + lo of dn left errors near 2e-3 of the row scale there.  Products contract
 // either over dims / value columns (operands read as rows) or over tokens in
 // steps of 32, in the token order t(g, j) = s0 + 4g + (j & 3) + 16 (j >> 2):
 // then the two 16-token accumulator tiles at s0 and s0 + 16 are, lane by
@@ -3025,10 +3032,10 @@ __global__ void __launch_bounds__(NTHR) k_bwd_chunk_bf(const BwdArgs a)
     // SH: Z_c and then R'_c are split once per workgroup into a shared
     // [D][D] hi + lo pair (d <= 64: 16 KB more LDS), instead of by every wave
     constexpr bool SH = D <= 64;
-    __shared__ __attribute__((aligned(16))) bf16 sm[6 * C * D + (SH ? 2 * D * D : 0)];
+    __shared__ __attribute__((aligned(16))) bf16 sm[7 * C * D + (SH ? 2 * D * D : 0)];
     __shared__ float dDs[C];
     bf16 *Gh = sm, *Gl = sm + C * D, *Fh = sm + 2 * C * D, *Fl = sm + 3 * C * D;
-    bf16 *Nh = sm + 4 * C * D, *Nl = sm + 5 * C * D, *Th = sm + 6 * C * D, *Tl = Th + D * D;
+    bf16 *Nh = sm + 4 * C * D, *Nl = sm + 5 * C * D, *Nl2 = sm + 6 * C * D, *Th = sm + 7 * C * D, *Tl = Th + D * D;
     const int tid = threadIdx.x, lane = tid % WAVE, r = lane % 16, g = lane / 16;
     const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
     const int ch = blockIdx.x % a.nch, bh = blockIdx.x / a.nch;
@@ -3045,7 +3052,7 @@ __global__ void __launch_bounds__(NTHR) k_bwd_chunk_bf(const BwdArgs a)
     // read as zeros
     const rsrc_t vr = vv.at(t0);
     auto vrow8 = [&](int row, int col) { return __builtin_bit_cast(bf16x8, bload16(vr, (uint32_t)(row * vv.rs + col * 2))); };
-    bwd_stage_split<D, 2>(dov.at(t0), dov.rs, Nh, Nl, nval, tid, denc);
+    bwd_stage_split<D, 2>(dov.at(t0), dov.rs, Nh, Nl, nval, tid, denc, Nl2);
     if (tid < C) dDs[tid] = tid < nval ? a.dden[(int64_t)bh * a.N + t0 + tid] : 0.f;
     __syncthreads();
 
@@ -3116,6 +3123,7 @@ __global__ void __launch_bounds__(NTHR) k_bwd_chunk_bf(const BwdArgs a)
                     const bf16x8 va = vrow8(s0 + 16 * hf + r, 32 * u + 8 * g);
                     t = mma8(t, va, nat8(Nh + swz<D>(me, 32 * u + 8 * g)));
                     t = mma8(t, va, nat8(Nl + swz<D>(me, 32 * u + 8 * g)));
+                    t = mma8(t, va, nat8(Nl2 + swz<D>(me, 32 * u + 8 * g)));
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) t[i] = (s0 + 16 * hf + 4 * g + i <= me) ? t[i] + ddt : 0.f;
@@ -3181,6 +3189,7 @@ __global__ void __launch_bounds__(NTHR) k_bwd_chunk_bf(const BwdArgs a)
                     const bf16x8 vb = vrow8(me, 32 * u + 8 * g);
                     t = mma8(t, nat8(Nh + swz<D>(s0 + 16 * hf + r, 32 * u + 8 * g)), vb);
                     t = mma8(t, nat8(Nl + swz<D>(s0 + 16 * hf + r, 32 * u + 8 * g)), vb);
+                    t = mma8(t, nat8(Nl2 + swz<D>(s0 + 16 * hf + r, 32 * u + 8 * g)), vb);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -3931,10 +3940,11 @@ la_status la_causal_bwd(const void *q, la_strides sq, const void *k, la_strides 
     ba.den = (float *)(ws + pl.den_off); ba.dden = (float *)(ws + pl.dden_off);
     const dim3 grid((unsigned)(BH * pl.nch));
 #define LA_BWD(KERN, F, DD) hipLaunchKernelGGL((KERN<F, DD>), grid, dim3(NTHR), 0, stream, ba)
-#define LA_BWD_ALL(KERN) \
-    if (f32) { if (d == 32) LA_BWD(KERN, true, 32); else if (d == 64) LA_BWD(KERN, true, 64); else LA_BWD(KERN, true, 128); } \
-    else { if (d == 32) LA_BWD(KERN, false, 32); else if (d == 64) LA_BWD(KERN, false, 64); else LA_BWD(KERN, false, 128); }
-    LA_BWD_ALL(k_bwd_prep)
+    if (f32) {
+        if (d == 32) LA_BWD(k_bwd_prep, true, 32); else if (d == 64) LA_BWD(k_bwd_prep, true, 64); else LA_BWD(k_bwd_prep, true, 128);
+    } else {
+        if (d == 32) LA_BWD(k_bwd_prep, false, 32); else if (d == 64) LA_BWD(k_bwd_prep, false, 64); else LA_BWD(k_bwd_prep, false, 128);
+    }
     // 3) the gradient reaching the carried-in state: dz_out + every chunk's part
     a.z_in = dz_out; a.s_in = ds_out; a.z_out = dz_in; a.s_out = ds_in;
     if (dz_in || ds_in) {
@@ -3953,7 +3963,6 @@ la_status la_causal_bwd(const void *q, la_strides sq, const void *k, la_strides 
         if (d == 32) LA_BWD_BF(32); else if (d == 64) LA_BWD_BF(64); else LA_BWD_BF(128);
 #undef LA_BWD_BF
     }
-#undef LA_BWD_ALL
 #undef LA_BWD
     return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }
