@@ -2734,22 +2734,33 @@ __global__ void __launch_bounds__(NTHR) k_bwd_prep(const BwdArgs a)
     bwd_stage<true, D, 0>(dov.at(t0), dov.rs, Ns, nval, tid);
     __syncthreads();
 
-    // ---- normaliser of token t = 16 w + r: g_t . S_c + sum_{s <= t} P_ts + eps
-    float rsum = 0.f, gs = 0.f, dot = 0.f;
+    // ---- normaliser of token t = 16 w + r: g_t . (S_c + sum_{s <= t} f_s) + eps.
+    // F becomes its inclusive prefix over the chunk's rows in place: NSEG
+    // segments of rows per column, each summed by one thread, then offset by
+    // the totals of the segments before it
+    {
+        constexpr int NSEG = NTHR / D, SEG = C / NSEG;
+        const int j = tid % D, sg = tid / D;
+        float run = 0.f;
 #pragma unroll
-    for (int sa = 0; sa < 4; ++sa) {
-        if (sa > w) break;
-        f32x4 pt = {0.f, 0.f, 0.f, 0.f};   // P^T: keys 16 sa + 4g + i, query t
+        for (int i = 0; i < SEG; ++i) {
+            run += Fs[(sg * SEG + i) * LD + j];
+            Fs[(sg * SEG + i) * LD + j] = run;
+        }
+        __syncthreads();
+        float off = 0.f;
 #pragma unroll
-        for (int js = 0; js < KT; ++js)
-            pt = mma1(pt, nat4(Fs + (16 * sa + r) * LD + 16 * js + 4 * g), nat4(Gs + t * LD + 16 * js + 4 * g));
+        for (int s2 = 0; s2 < NSEG - 1; ++s2) off += s2 < sg ? Fs[(s2 * SEG + SEG - 1) * LD + j] : 0.f;
+        __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rsum += (16 * sa + 4 * g + i <= t) ? pt[i] : 0.f;
+        for (int i = 0; i < SEG; ++i) Fs[(sg * SEG + i) * LD + j] += off;
+        __syncthreads();
     }
+    float gs = 0.f, dot = 0.f;
 #pragma unroll
     for (int js = 0; js < KT; ++js) {
         const f32x4 gq = nat4(Gs + t * LD + 16 * js + 4 * g);
-        const f32x4 s4 = s4v[js], o4 = o4v[js];
+        const f32x4 s4 = s4v[js] + nat4(Fs + t * LD + 16 * js + 4 * g), o4 = o4v[js];
         const f32x4 d4 = nat4(Ns + t * LD + 16 * js + 4 * g);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -2759,12 +2770,11 @@ __global__ void __launch_bounds__(NTHR) k_bwd_prep(const BwdArgs a)
     }
 #pragma unroll
     for (int m = 16; m < WAVE; m <<= 1) {
-        rsum += __shfl_xor(rsum, m);
         gs += __shfl_xor(gs, m);
         dot += __shfl_xor(dot, m);
     }
     const bool live = t < nval;
-    const float den = gs + rsum + a.eps;
+    const float den = gs + a.eps;
     const float ddn = live ? -dot / den : 0.f;
     const float inv = live ? 1.f / den : 0.f;
     if (g == 0) {
