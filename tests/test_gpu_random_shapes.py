@@ -16,6 +16,8 @@ row) enters dq_0 through A_00 = dn_0 . (v_0 - out_0), which cancels to the eps
 level at a head's first token, and on heads where dout . v is small next to
 |dout| |v| it alone can exceed 2e-3 of the row's scale (seen at B1 H4 N272
 d32).  test_gpu_backward.py keeps the composed forward-then-backward cases.
+Every fourth causal case passes q, k, v and out as [B, H, N, d] views of
+[B, N, H, d] storage.
 """
 import numpy as np
 import pytest
@@ -69,19 +71,49 @@ def _err(gpu, ref, n):
     return rowwise_rel_err(np.asarray(gpu.cpu(), np.float64).reshape(-1, n), np.asarray(ref).reshape(-1, n))
 
 
+def _device_layout(t, token_major):
+    """t on the GPU, as a [B, H, N, d] view of [B, N, H, d] storage when
+    token_major (strides that are not the contiguous ones)."""
+    if not token_major:
+        return t.to(DEV)
+    return t.permute(0, 2, 1, 3).contiguous().to(DEV).permute(0, 2, 1, 3)
+
+
 @pytest.mark.parametrize("i", range(40))
 def test_random_causal(i):
     B, H, N, d, dtype, with_state = _case(i, 4096)
-    _log(f"random causal {i}: B{B} H{H} N{N} d{d} {dtype} state={with_state}")
+    token_major = i % 4 == 3
+    _log(f"random causal {i}: B{B} H{H} N{N} d{d} {dtype} state={with_state} token-major={token_major}")
     q, k, v = _inputs(B, H, N, d, dtype, 7100 + i)
     z_in, s_in = _state(B, H, d, 7200 + i) if with_state else (None, None)
     ref_out, ref_z, ref_s = oracle.causal(q, k, v, 1e-6, z_in, s_in)
+    out = torch.empty(B, N, H, d, device=DEV).permute(0, 2, 1, 3) if token_major else torch.empty(B, H, N, d, device=DEV)
+    z_out = torch.empty(B, H, d, d, device=DEV)
+    s_out = torch.empty(B, H, d, device=DEV)
+    la.la_causal_fwd(*(_device_layout(t, token_major) for t in (q, k, v)), out,
+                     z_in=None if z_in is None else z_in.to(DEV), s_in=None if s_in is None else s_in.to(DEV),
+                     z_out=z_out, s_out=s_out)
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    assert _err(out, ref_out, d) < tol
+    assert _err(z_out, ref_z, d * d) < tol
+    assert _err(s_out, ref_s, d) < tol
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_unnormalized(i):
+    B, H, N, d, dtype, with_state = _case(500 + i, 2048)
+    _log(f"random unnormalized {i}: B{B} H{H} N{N} d{d} {dtype} state={with_state}")
+    q, k, v = _inputs(B, H, N, d, dtype, 8300 + i)
+    z_in, s_in = _state(B, H, d, 8400 + i) if with_state else (None, None)
+    ref_out = oracle.causal_unnormalized(q, k, v, z_in)
+    _, ref_z, ref_s = oracle.causal(q, k, v, 1e-6, z_in, s_in, want_out=False)
     out = torch.empty(B, H, N, d, device=DEV)
     z_out = torch.empty(B, H, d, d, device=DEV)
     s_out = torch.empty(B, H, d, device=DEV)
-    la.la_causal_fwd(q.to(DEV), k.to(DEV), v.to(DEV), out,
-                     z_in=None if z_in is None else z_in.to(DEV), s_in=None if s_in is None else s_in.to(DEV),
-                     z_out=z_out, s_out=s_out)
+    la.la_causal_fwd_unnormalized(q.to(DEV), k.to(DEV), v.to(DEV), out,
+                                  z_in=None if z_in is None else z_in.to(DEV),
+                                  s_in=None if s_in is None else s_in.to(DEV), z_out=z_out, s_out=s_out)
     torch.cuda.synchronize()
     tol = TOL[dtype]
     assert _err(out, ref_out, d) < tol
