@@ -2824,8 +2824,9 @@ __global__ void __launch_bounds__(NTHR) k_bwd_prep(const BwdArgs a)
 }
 
 // dq, dk, dv of one chunk from the state before it, the adjoint state after
-// it and the chunk's own tokens.  Wave w owns tokens 16 w .. + 15: their dq
-// (as queries) and their dk, dv (as keys).
+// it and the chunk's own tokens, every product on fp32 MFMA.  Wave w owns
+// tokens 16 w .. + 15: their dq (as queries) and their dk, dv (as keys).
+// Launched for fp32 inputs (bf16 inputs run k_bwd_chunk_bf).
 template <bool F32, int D>
 __global__ void __launch_bounds__(NTHR) k_bwd_chunk(const BwdArgs a)
 {
